@@ -1,0 +1,307 @@
+"""Pins of the CPU oracle against things other than itself: hand-worked
+format examples, the page's printed sweep table, closed forms, invariants,
+special cases that reduce to library routines, and a pure-Python brute force.
+
+CPU only (no GPU marker)."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+
+import synth
+from oracle import brute
+from oracle import moe
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _tiny_experts(seed, E, H, I, shared=False):
+    shape = synth.LayerShape(E=E, H=H, I=I, top_k=1, shared=shared)
+    ex = [synth.expert(seed, shape, e) for e in range(E)]
+    sh = synth.expert(seed, shape, "shared") if shared else None
+    return ex, sh
+
+
+def _lists(w):
+    return {k: v.tolist() for k, v in w.items()}
+
+
+# ------------------------------------------------------------------ dequant
+
+
+def test_dequant_golden_nibbles():
+    d = json.load(open(os.path.join(GOLDEN, "int4_nibbles.json")))
+    for c in d["cases"]:
+        packed = np.array([[c["byte"]] + [0x88] * 15], dtype=np.uint8)  # 32 codes, one group
+        scales = np.array([[c["scale_fp16_bits"]]], dtype=np.uint16)
+        W = moe.dequant(packed, scales)
+        assert W.shape == (1, 32)
+        assert W[0, 0] == c["even"] and W[0, 1] == c["odd"], c
+        assert np.all(W[0, 2:] == 0.0)
+
+
+def test_dequant_group_boundary():
+    # two groups along K: inputs 0..31 use scale 0, 32..63 use scale 1
+    packed = np.full((1, 32), 0x99, dtype=np.uint8)  # every code 9 -> +1 * scale
+    scales = np.array([[0x3C00, 0x4000]], dtype=np.uint16)  # 1.0, 2.0
+    W = moe.dequant(packed, scales)
+    assert np.all(W[0, :32] == 1.0) and np.all(W[0, 32:] == 2.0)
+
+
+def test_dequant_exact_all_codes_scale_sweep():
+    rng = np.random.default_rng(1)
+    # every finite positive fp16 pattern in a sweep, including the ends of the
+    # synthetic range 0.002 and 0.02 and subnormals
+    bits = np.unique(np.concatenate([
+        rng.integers(1, 0x7C00, size=3000), np.array([1, 0x3FF, 0x400, 0x1818, 0x2D1F, 0x7BFF]),
+        np.array([np.float16(0.002).view(np.uint16), np.float16(0.02).view(np.uint16)]),
+    ]).astype(np.uint16))
+    codes = np.arange(16, dtype=np.uint8)
+    packed = np.zeros((bits.size, 16), dtype=np.uint8)
+    packed[:, :8] = (codes[0::2] | (codes[1::2] << 4))[None, :]
+    W = moe.dequant(packed, bits[:, None])
+    for r in range(0, bits.size, 97):
+        s = Fraction(float(bits[r:r + 1].view(np.float16)[0]))
+        for c in range(16):
+            assert Fraction(W[r, c]) == (c - 8) * s
+    # zero-point code gives exact zero for every scale
+    assert np.all(W[:, 8] == 0.0)
+
+
+def test_unpack_inverse_of_packing():
+    rng = np.random.default_rng(2)
+    codes = rng.integers(0, 16, size=(5, 64), dtype=np.uint8)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    assert np.array_equal(moe.unpack_codes(packed), codes)
+
+
+def test_bf16_decode_matches_torch():
+    import torch
+    rng = np.random.default_rng(3)
+    f = rng.standard_normal(1000).astype(np.float32) * 100
+    bits = synth.f32_to_bf16_bits(f)
+    ref = torch.from_numpy(f).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(moe.decode_bf16(bits), ref)
+
+
+# ------------------------------------------------------------------ routing
+
+
+def test_top1_is_argmax_with_low_index_ties():
+    rng = np.random.default_rng(4)
+    lg = rng.standard_normal((50, 16)).astype(np.float32)
+    lg[:10, 3] = lg[:10, 7] = lg[:10].max(axis=1) + 1.0  # ties at the top
+    ids = moe.select_topk(lg, 1)
+    assert np.array_equal(ids[:, 0], np.argmax(lg, axis=1))
+    assert np.all(ids[:10, 0] == 3)
+    w = moe.routing_weights(lg, ids)
+    assert np.all(w == 1.0)
+
+
+def test_injected_ties_pick_lower_index():
+    lg = np.zeros((1, 8), dtype=np.float32)
+    lg[0, [1, 4, 6]] = 2.0
+    lg[0, [0, 5]] = 1.0
+    ids = moe.select_topk(lg, 4)
+    assert ids.tolist() == [[1, 4, 6, 0]]
+    ids = moe.select_topk(np.zeros((1, 8), np.float32), 3)
+    assert ids.tolist() == [[0, 1, 2]]
+
+
+def test_route_invariants_and_full_softmax():
+    rng = np.random.default_rng(5)
+    for E, k, M in [(8, 2, 16), (384, 8, 33), (17, 17, 5), (64, 1, 9)]:
+        lg = rng.standard_normal((M, E)).astype(np.float32)
+        r = moe.route(lg, k)
+        ids, w = r["ids"], r["w"]
+        assert ids.shape == (M, k) and np.all((ids >= 0) & (ids < E))
+        assert all(len(set(row)) == k for row in ids.tolist())
+        assert np.allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-15 * k)
+        assert np.all(np.diff(w, axis=1) <= 0)  # descending in slot order
+        if k == E:
+            ref = scipy.special.softmax(lg.astype(np.float64), axis=1)
+            assert np.allclose(np.take_along_axis(ref, ids, axis=1), w, rtol=1e-13, atol=0)
+
+
+def test_counts_offsets_perm_against_loops():
+    rng = np.random.default_rng(6)
+    for E, k, M in [(8, 2, 16), (384, 8, 70), (5, 5, 3), (12, 3, 0)]:
+        lg = rng.standard_normal((M, E)).astype(np.float32)
+        r = moe.route(lg, k)
+        ids = r["ids"].tolist()
+        perm_ref, counts_ref = [], [0] * E
+        for e in range(E):  # counting sort written as loops, expert-major
+            for t in range(M):
+                for j in range(k):
+                    if ids[t][j] == e:
+                        perm_ref.append(t * k + j)
+                        counts_ref[e] += 1
+        assert r["counts"].tolist() == counts_ref
+        assert r["offsets"][0] == 0 and r["offsets"][-1] == M * k
+        assert r["offsets"][1:].tolist() == list(np.cumsum(counts_ref))
+        assert r["perm"].tolist() == perm_ref
+        assert sorted(r["perm"].tolist()) == list(range(M * k))
+        for f, pos in enumerate(r["inv_perm"].tolist()):
+            assert r["perm"][pos] == f
+
+
+def test_routing_statistics_match_page_sweep():
+    """The page reports ~8 of 384 experts active at M=1 and ~all at M=256 for
+    top-8 routing; uniform N(0,1) logits reproduce both, and the number of
+    touched experts follows E*(1-(1-k/E)^M)."""
+    table = json.load(open(os.path.join(GOLDEN, "marlin_moe_sweep.json")))
+    E, k = table["layer"]["E"], table["layer"]["top_k"]
+    rows = {r["M"]: r for r in table["rows"]}
+    assert "8/384" in rows[1]["note"] and "all" in rows[256]["note"]
+    touched = {}
+    for M in (1, 9, 90, 256):
+        n = []
+        for seed in range(6):
+            r = moe.route(synth.logits(seed, M, E), k)
+            n.append(int(np.count_nonzero(r["counts"])))
+        touched[M] = float(np.mean(n))
+    assert touched[1] == 8.0
+    for M in (9, 90, 256):
+        assert abs(touched[M] - synth.expected_touched(E, k, M)) < 0.04 * synth.expected_touched(E, k, M)
+    assert touched[256] >= 0.98 * E
+
+
+def test_page_table_units_consistent():
+    """us/token = 1000 * ms/call / M on every printed row (to the page's
+    rounding): the definition the benchmark uses."""
+    table = json.load(open(os.path.join(GOLDEN, "marlin_moe_sweep.json")))
+    for r in table["rows"]:
+        assert abs(1000.0 * r["ms_per_call"] / r["M"] - r["us_per_token"]) <= 0.006 * r["us_per_token"] + 0.05
+
+
+# -------------------------------------------------------------------- layer
+
+
+@pytest.mark.parametrize("E,H,I,k,M,shared", [
+    (4, 64, 32, 2, 3, False),
+    (3, 32, 64, 1, 2, False),
+    (1, 32, 32, 1, 2, False),
+    (5, 64, 32, 5, 2, False),
+    (4, 32, 32, 2, 2, True),
+    (6, 96, 32, 3, 2, False),
+])
+def test_oracle_matches_brute_force(E, H, I, k, M, shared):
+    seed = 11 + E + H + k
+    ex, sh = _tiny_experts(seed, E, H, I, shared)
+    x = synth.hidden(seed, M, H)
+    lg = synth.logits(seed, M, E)
+    r = moe.forward(x, lg, k, lambda e: ex[e], I, shared=sh)
+    out_b, ids_b, w_b = brute.layer(x.tolist(), lg.tolist(), k, [_lists(w) for w in ex], H, I,
+                                    shared=_lists(sh) if sh else None)
+    assert r["ids"].tolist() == ids_b
+    assert np.allclose(r["w"], np.array(w_b), rtol=1e-14, atol=0)
+    ob = np.array(out_b)
+    assert np.max(np.abs(r["out"] - ob)) <= 1e-12 * np.max(np.abs(ob))
+
+
+def _diag_expert(H, I, sg_bits, su_bits, sd_bits):
+    """Codes 9 on the diagonal (+1 * scale), 8 elsewhere (0)."""
+    codes13 = np.full((2 * I, H), 8, np.uint8)
+    for i in range(min(I, H)):
+        codes13[i, i] = 9
+        codes13[I + i, i] = 9
+    codes2 = np.full((H, I), 8, np.uint8)
+    for n in range(min(H, I)):
+        codes2[n, n] = 9
+    pack = lambda c: (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+    s13 = np.empty((2 * I, H // 32), np.uint16)
+    s13[:I] = sg_bits
+    s13[I:] = su_bits
+    s2 = np.full((H, I // 32), sd_bits, np.uint16)
+    return {"w13": pack(codes13), "s13": s13, "w2": pack(codes2), "s2": s2}
+
+
+def test_diagonal_weights_closed_form():
+    """Diagonal weights with power-of-two scales: out_n = sd*su*x_n*SiLU(sg*x_n)
+    for n < min(H, I), 0 otherwise (top-1, so the routing weight is 1)."""
+    H, I, M, E = 96, 64, 5, 3
+    sg, su, sd = 0x3800, 0x4000, 0x3400  # 0.5, 2.0, 0.25
+    ex = [_diag_expert(H, I, sg, su, sd) for _ in range(E)]
+    x = synth.hidden(21, M, H)
+    lg = synth.logits(21, M, E)
+    r = moe.forward(x, lg, 1, lambda e: ex[e], I)
+    xf = moe.decode_bf16(x)
+    for t in range(M):
+        for n in range(H):
+            if n < min(H, I):
+                v = float(xf[t, n])
+                g = 0.5 * v
+                expect = 0.25 * 2.0 * v * (g / (1.0 + math.exp(-g)))
+            else:
+                expect = 0.0
+            assert abs(r["out"][t, n] - expect) <= 1e-14 * max(1.0, abs(expect))
+
+
+def test_identical_experts_independent_of_logits():
+    H, I, E, k, M = 64, 32, 6, 3, 4
+    one = synth.expert(5, synth.LayerShape(E=1, H=H, I=I, top_k=1), 0)
+    x = synth.hidden(5, M, H)
+    outs = [moe.forward(x, synth.logits(s, M, E), k, lambda e: one, I)["out"] for s in range(3)]
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= 1e-12 * np.max(np.abs(outs[0]))
+
+
+def test_top1_equals_chosen_expert_mlp():
+    H, I, E, M = 64, 32, 5, 4
+    ex, _ = _tiny_experts(8, E, H, I)
+    x = synth.hidden(8, M, H)
+    lg = synth.logits(8, M, E)
+    r = moe.forward(x, lg, 1, lambda e: ex[e], I)
+    xf = moe.decode_bf16(x)
+    for t in range(M):
+        e = int(np.argmax(lg[t]))
+        y = brute._mlp(xf[t].tolist(), _lists(ex[e]), H, I)
+        assert np.allclose(r["out"][t], y, rtol=1e-12, atol=1e-12)
+
+
+def test_token_permutation_and_expert_relabeling():
+    H, I, E, k, M = 64, 32, 6, 2, 7
+    ex, _ = _tiny_experts(9, E, H, I)
+    x = synth.hidden(9, M, H)
+    lg = synth.logits(9, M, E)
+    base = moe.forward(x, lg, k, lambda e: ex[e], I)["out"]
+    tp = np.random.default_rng(0).permutation(M)
+    o = moe.forward(x[tp], lg[tp], k, lambda e: ex[e], I)["out"]
+    assert np.max(np.abs(o - base[tp])) <= 1e-12 * np.max(np.abs(base))
+    ep = np.random.default_rng(1).permutation(E)  # new expert j is old expert ep[j]
+    o = moe.forward(x, lg[:, ep], k, lambda j: ex[ep[j]], I)["out"]
+    assert np.max(np.abs(o - base)) <= 1e-12 * np.max(np.abs(base))
+
+
+def test_sampled_tokens_equal_full_rows():
+    H, I, E, k, M = 64, 32, 8, 2, 16
+    ex, sh = _tiny_experts(10, E, H, I, shared=True)
+    x = synth.hidden(10, M, H)
+    lg = synth.logits(10, M, E)
+    full = moe.forward(x, lg, k, lambda e: ex[e], I, shared=sh)["out"]
+    part = moe.forward(x, lg, k, lambda e: ex[e], I, shared=sh, tokens=[3, 0, 15])["out"]
+    # equal up to BLAS rounding order (the row count of each product differs)
+    assert np.max(np.abs(part - full[[3, 0, 15]])) <= 1e-13 * np.max(np.abs(full))
+
+
+def test_shared_expert_adds_with_weight_one():
+    H, I, E, k, M = 64, 32, 4, 2, 3
+    ex, sh = _tiny_experts(12, E, H, I, shared=True)
+    x = synth.hidden(12, M, H)
+    lg = synth.logits(12, M, E)
+    with_s = moe.forward(x, lg, k, lambda e: ex[e], I, shared=sh)["out"]
+    without = moe.forward(x, lg, k, lambda e: ex[e], I)["out"]
+    xf = moe.decode_bf16(x)
+    for t in range(M):
+        y = brute._mlp(xf[t].tolist(), _lists(sh), H, I)
+        assert np.allclose(with_s[t] - without[t], y, rtol=1e-10, atol=1e-12)
+
+
+def test_empty_call():
+    ex, _ = _tiny_experts(1, 4, 32, 32)
+    r = moe.forward(np.zeros((0, 32), np.uint16), np.zeros((0, 4), np.float32), 2, lambda e: ex[e], 32)
+    assert r["out"].shape == (0, 32) and r["perm"].size == 0 and r["counts"].sum() == 0
