@@ -1,0 +1,189 @@
+/*
+ * qmoe.h -- C ABI of a fused Mixture-of-Experts layer over 4-bit
+ * group-quantized expert weights, for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (definition: "The MoE Throughput Lever: Quantifying the INT4
+ * Marlin GEMM on Blackwell PRO 6000", sections "The Context: Why This
+ * Measurement Matters" and "The Benchmark: What Was Measured"; routing
+ * counts: "Detailed results", section "Nsight Compute on the stock kernel";
+ * sorted routing and the stacked gate+up GEMM: "perf(exl3): accelerate
+ * fat-expert prefill", description and section "Rollout"):
+ *
+ *   for each token t of M:
+ *     ids[t, 0..k-1] = the top_k experts by router logit (descending,
+ *                      ties to the lower expert index)
+ *     w[t, j]        = softmax(logits[t])[ids[t,j]], renormalised over j
+ *     out[t]         = sum_j w[t,j] * Down_e( SiLU(Gate_e x_t) * (Up_e x_t) ),
+ *                      e = ids[t,j], summed in j order
+ *                      (+ Down_s(SiLU(Gate_s x_t) * (Up_s x_t)) with weight 1
+ *                       when a shared expert is configured)
+ *
+ * Weight format (per expert, row-major, all device memory):
+ *   w13  uint8  [E, 2I, H/2]   gate rows 0..I-1, up rows I..2I-1; byte j of a
+ *                              row holds input 2j (low nibble) and 2j+1 (high
+ *                              nibble); code c in 0..15 means (c - 8) * scale
+ *   s13  fp16   [E, 2I, H/32]  one scale per 32 consecutive inputs of a row
+ *   w2   uint8  [E, H, I/2]    down projection, same packing along I
+ *   s2   fp16   [E, H, I/32]
+ * Activations x: bf16 [M, H]; router logits: fp32 [M, E]; out: bf16 [M, H].
+ * All row-major and contiguous.
+ *
+ * Arithmetic: weights are decoded to fp16 operands ((c-8)*scale rounded to
+ * nearest even in fp16) and x is converted exactly to fp16; products are
+ * accumulated in fp32 by MFMA; h = SiLU(gate)*up is held in fp16, the
+ * weighted per-slot results in fp32, and out is rounded to bf16 (nearest
+ * even).  Hence |x| and |h| must stay below 65504 (the fp16 range).
+ *
+ * Ownership: the caller owns every buffer.  The layer handle borrows the
+ * weight pointers for its lifetime and copies nothing.  The library never
+ * allocates device memory; per-call scratch lives in a caller-provided
+ * workspace whose size comes from qmoe_workspace_size().
+ *
+ * Streams: every enqueueing call takes a hipStream_t (as void*, NULL = the
+ * default stream), only enqueues work on it and never synchronises.  Faults
+ * inside kernels surface at the caller's next synchronisation.
+ *
+ * Errors: calls return QMOE_OK (0) or a negative status; the message of the
+ * last failure on the calling thread is returned by qmoe_last_error().  No
+ * call falls back to another implementation: an unsupported case is an
+ * error.  Argument checks run before any device query, so they work
+ * without a GPU.
+ *
+ * Thread safety: a handle may be used from several threads only if each
+ * thread uses its own workspace; the statistics counters are atomic.
+ */
+#ifndef QMOE_H
+#define QMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QMOE_VERSION 1
+
+enum qmoe_status {
+  QMOE_OK = 0,
+  QMOE_ERR_ARG = -1,          /* a null pointer, a bad size, a bad index */
+  QMOE_ERR_UNSUPPORTED = -2,  /* a shape or device this build does not run */
+  QMOE_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required */
+  QMOE_ERR_DEVICE = -4,       /* a HIP runtime query failed (e.g. no GPU) */
+  QMOE_ERR_LAUNCH = -5        /* a kernel launch or async copy failed */
+};
+
+/* Limits of this build. */
+#define QMOE_MAX_EXPERTS 1024
+#define QMOE_MAX_TOPK 32
+#define QMOE_GROUP 32
+
+typedef struct {
+  int32_t E;          /* routed experts, 1..QMOE_MAX_EXPERTS */
+  int32_t H;          /* hidden size, multiple of 32 */
+  int32_t I;          /* intermediate size, multiple of 32 */
+  int32_t top_k;      /* 1..min(E, QMOE_MAX_TOPK) */
+  int32_t group_size; /* must be 32 */
+  int32_t max_rows;   /* largest M a forward call may pass (>= 1) */
+  const uint8_t* w13;
+  const uint16_t* s13; /* fp16 bit patterns */
+  const uint8_t* w2;
+  const uint16_t* s2;
+  /* Optional shared expert, applied to every token with weight 1.0: either
+     all four NULL (none) or all four set; shapes as one routed expert. */
+  const uint8_t* shared_w13;
+  const uint16_t* shared_s13;
+  const uint8_t* shared_w2;
+  const uint16_t* shared_s2;
+} qmoe_layer_desc;
+
+typedef struct qmoe_layer qmoe_layer;
+
+/* Validate the description and create a handle (host memory only).  Fails
+   with QMOE_ERR_ARG on a bad field (the message names it), then with
+   QMOE_ERR_DEVICE if no HIP device can be queried and QMOE_ERR_UNSUPPORTED
+   if the current device is not gfx950. */
+int qmoe_layer_create(const qmoe_layer_desc* desc, qmoe_layer** out);
+void qmoe_layer_destroy(qmoe_layer* layer);
+
+/* Bytes of workspace a call with M tokens needs (0 <= M <= max_rows). */
+int qmoe_workspace_size(const qmoe_layer* layer, int64_t M, size_t* bytes);
+
+/* Enqueue the one-time initialisation of a workspace (clears its control
+   words).  Every call leaves the workspace initialised again, so this is
+   needed once per workspace; the library also does it by itself the first
+   time it sees a workspace pointer on a handle. */
+int qmoe_workspace_init(qmoe_layer* layer, void* workspace, size_t ws_bytes, void* stream);
+
+/* The whole layer: route, gate+up, down, combine (four kernel launches).
+   x: bf16 [M,H]; logits: fp32 [M,E]; out: bf16 [M,H] (device pointers).
+   M == 0 is a no-op.  Graph-capturable for a fixed M. */
+int qmoe_forward(qmoe_layer* layer, const void* x, const float* logits, int64_t M,
+                 void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/* The same four steps one at a time, on one workspace and in this order
+   (each reads what the previous one left in the workspace).  They let a
+   caller time or check each step alone.
+     qmoe_route     top-k routing, expert counts and their exclusive scan,
+                    the stable sort of routed slots by expert, the flat list
+                    of (expert, row-tile) work items, and x converted to the
+                    GEMM operand format;
+     qmoe_gate_up   per expert, the stacked gate+up product with
+                    h = SiLU(gate)*up;
+     qmoe_down      per expert, the down product times the routing weight,
+                    written per (token, slot);
+     qmoe_combine   out[t] = sum over slots j (in order) + shared expert. */
+int qmoe_route(qmoe_layer* layer, const void* x, const float* logits, int64_t M,
+               void* workspace, size_t ws_bytes, void* stream);
+int qmoe_gate_up(qmoe_layer* layer, int64_t M, void* workspace, size_t ws_bytes, void* stream);
+int qmoe_down(qmoe_layer* layer, int64_t M, void* workspace, size_t ws_bytes, void* stream);
+int qmoe_combine(qmoe_layer* layer, int64_t M, void* out, void* workspace, size_t ws_bytes,
+                 void* stream);
+
+/* Copy the routing results of the last qmoe_route/qmoe_forward on this
+   workspace into caller buffers (device pointers; any may be NULL):
+   ids int32 [M,k], w fp32 [M,k], counts int32 [E], offsets int32 [E+1],
+   perm int32 [M*k] (perm[pos] = t*k+j, experts in order, tokens ascending
+   within an expert). */
+int qmoe_read_routing(qmoe_layer* layer, int64_t M, const void* workspace, size_t ws_bytes,
+                      int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
+                      int32_t* perm, void* stream);
+
+/* Copy an intermediate of the last call into fp32 rows in slot order
+   (row t*k+j for routed slot j of token t; rows M*k+t for the shared expert):
+   which = 0: h = SiLU(gate)*up, [M*k (+M), I]  (after qmoe_gate_up)
+   which = 1: y = w * Down(h),   [M*k (+M), H]  (after qmoe_down) */
+int qmoe_read_intermediate(qmoe_layer* layer, int64_t M, const void* workspace, size_t ws_bytes,
+                           int32_t which, float* out_f32, void* stream);
+
+/* Decode one expert's weights with the same device function the GEMMs use
+   and write the fp16 operand values in natural order: which = 0: [2I, H]
+   from w13/s13, which = 1: [H, I] from w2/s2.  expert == E selects the
+   shared expert.  out: uint16 fp16 bit patterns, device memory. */
+int qmoe_dequant_debug(qmoe_layer* layer, int32_t expert, int32_t which, uint16_t* out_f16,
+                       void* stream);
+
+/* Host-side counters, bumped by the enqueueing calls (no device readback). */
+typedef struct {
+  uint64_t forward_calls;
+  uint64_t route_calls;       /* qmoe_route, also inside qmoe_forward */
+  uint64_t gemm_launches;     /* gate+up and down kernel launches */
+  uint64_t launches;          /* every kernel launch */
+  uint64_t workspace_inits;   /* explicit and automatic */
+  uint64_t workspace_bytes_last;
+  uint64_t workspace_bytes_peak;
+  uint64_t decode_tiles;      /* calls that used the 16-row tile shape */
+  uint64_t prefill_tiles;     /* calls that used the 128-row tile shape */
+} qmoe_stats;
+
+int qmoe_get_stats(const qmoe_layer* layer, qmoe_stats* out);
+int qmoe_reset_stats(qmoe_layer* layer);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* qmoe_last_error(void);
+int qmoe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMOE_H */

@@ -1,0 +1,98 @@
+"""ctypes binding of libqmoe.so (the C ABI in include/qmoe.h).
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every step of the layer runs in the library's kernels.
+If the library is missing this module raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libqmoe.so"
+
+QMOE_OK = 0
+QMOE_ERR_ARG = -1
+QMOE_ERR_UNSUPPORTED = -2
+QMOE_ERR_WORKSPACE = -3
+QMOE_ERR_DEVICE = -4
+QMOE_ERR_LAUNCH = -5
+
+
+class QmoeError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"qmoe error {code}: {message}")
+        self.code = code
+        self.message = message
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [
+        ("E", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
+        ("top_k", ctypes.c_int32), ("group_size", ctypes.c_int32), ("max_rows", ctypes.c_int32),
+        ("w13", ctypes.c_void_p), ("s13", ctypes.c_void_p),
+        ("w2", ctypes.c_void_p), ("s2", ctypes.c_void_p),
+        ("shared_w13", ctypes.c_void_p), ("shared_s13", ctypes.c_void_p),
+        ("shared_w2", ctypes.c_void_p), ("shared_s2", ctypes.c_void_p),
+    ]
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in (
+        "forward_calls", "route_calls", "gemm_launches", "launches", "workspace_inits",
+        "workspace_bytes_last", "workspace_bytes_peak", "decode_tiles", "prefill_tiles")]
+
+    def as_dict(self) -> dict:
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+_VP, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+
+# name -> (restype, argtypes); mirrors include/qmoe.h
+SIGNATURES = {
+    "qmoe_version": (ctypes.c_int, []),
+    "qmoe_last_error": (ctypes.c_char_p, []),
+    "qmoe_layer_create": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTER(_VP)]),
+    "qmoe_layer_destroy": (None, [_VP]),
+    "qmoe_workspace_size": (ctypes.c_int, [_VP, _I64, ctypes.POINTER(_SZ)]),
+    "qmoe_workspace_init": (ctypes.c_int, [_VP, _VP, _SZ, _VP]),
+    "qmoe_forward": (ctypes.c_int, [_VP, _VP, _VP, _I64, _VP, _VP, _SZ, _VP]),
+    "qmoe_route": (ctypes.c_int, [_VP, _VP, _VP, _I64, _VP, _SZ, _VP]),
+    "qmoe_gate_up": (ctypes.c_int, [_VP, _I64, _VP, _SZ, _VP]),
+    "qmoe_down": (ctypes.c_int, [_VP, _I64, _VP, _SZ, _VP]),
+    "qmoe_combine": (ctypes.c_int, [_VP, _I64, _VP, _VP, _SZ, _VP]),
+    "qmoe_read_routing": (ctypes.c_int, [_VP, _I64, _VP, _SZ, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "qmoe_read_intermediate": (ctypes.c_int, [_VP, _I64, _VP, _SZ, _I32, _VP, _VP]),
+    "qmoe_dequant_debug": (ctypes.c_int, [_VP, _I32, _I32, _VP, _VP]),
+    "qmoe_get_stats": (ctypes.c_int, [_VP, ctypes.POINTER(Stats)]),
+    "qmoe_reset_stats": (ctypes.c_int, [_VP]),
+}
+
+_lib = None
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, LIB_NAME)
+
+
+def load_library():
+    """Load the in-tree libqmoe.so; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def check(rc: int) -> None:
+    if rc != QMOE_OK:
+        raise QmoeError(rc, load_library().qmoe_last_error().decode())

@@ -1,0 +1,179 @@
+"""Python face of the fused int4 MoE layer: a thin wrapper over the C ABI.
+
+Tensors are torch device tensors (PyTorch supplies device memory and the
+stream); all computation happens in libqmoe.so's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from ._binding import LayerDesc, Stats, check, load_library
+
+GROUP = 32
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Layer:
+    """One MoE layer over packed int4 weights.
+
+    w13 uint8 [E,2I,H/2], s13 fp16-bits (int16/uint16/float16) [E,2I,H/32],
+    w2 uint8 [E,H,I/2], s2 [E,H,I/32]; `shared` an optional dict with the
+    same four keys for one always-selected shared expert.  The layer keeps
+    references to the tensors (the library borrows their memory)."""
+
+    def __init__(self, *, E, H, I, top_k, max_rows, w13, s13, w2, s2, shared=None):
+        self.lib = load_library()
+        self.E, self.H, self.I, self.top_k, self.max_rows = E, H, I, top_k, max_rows
+        self._keep = [w13, s13, w2, s2]
+        sh = shared or {}
+        if shared:
+            self._keep += [sh["w13"], sh["s13"], sh["w2"], sh["s2"]]
+        self.has_shared = bool(shared)
+        desc = LayerDesc(E, H, I, top_k, GROUP, max_rows, _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2),
+                         _ptr(sh.get("w13")), _ptr(sh.get("s13")), _ptr(sh.get("w2")), _ptr(sh.get("s2")))
+        handle = ctypes.c_void_p()
+        check(self.lib.qmoe_layer_create(ctypes.byref(desc), ctypes.byref(handle)))
+        self.handle = handle
+        self.device = w13.device
+        self._ws = None
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self.lib.qmoe_layer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ------------------------------------------------------------ workspace
+
+    def workspace_bytes(self, M: int) -> int:
+        n = ctypes.c_size_t()
+        check(self.lib.qmoe_workspace_size(self.handle, M, ctypes.byref(n)))
+        return n.value
+
+    def workspace(self, M: int, stream=None) -> torch.Tensor:
+        """A workspace large enough for M tokens, kept and grown as needed.
+        A new allocation is initialised explicitly (its memory may have held
+        other tensors)."""
+        need = self.workspace_bytes(M)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = None
+            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+            check(self.lib.qmoe_workspace_init(self.handle, _ptr(self._ws), self._ws.numel(), _stream(stream)))
+        return self._ws
+
+    def _args(self, M, stream):
+        ws = self.workspace(M, stream)
+        return _ptr(ws), ws.numel(), _stream(stream)
+
+    # -------------------------------------------------------------- calls
+
+    def _check_inputs(self, x, logits):
+        M = x.shape[0]
+        if x.dtype != torch.bfloat16 or tuple(x.shape) != (M, self.H):
+            raise ValueError(f"x must be bf16 [M, {self.H}]")
+        if logits.dtype != torch.float32 or tuple(logits.shape) != (M, self.E):
+            raise ValueError(f"logits must be float32 [M, {self.E}]")
+        return M
+
+    def forward(self, x, logits, out=None, stream=None):
+        M = self._check_inputs(x, logits)
+        if out is None:
+            out = torch.empty((M, self.H), dtype=torch.bfloat16, device=self.device)
+        ws, nb, st = self._args(M, stream)
+        check(self.lib.qmoe_forward(self.handle, _ptr(x), _ptr(logits), M, _ptr(out), ws, nb, st))
+        return out
+
+    __call__ = forward
+
+    def route(self, x, logits, stream=None):
+        M = self._check_inputs(x, logits)
+        ws, nb, st = self._args(M, stream)
+        check(self.lib.qmoe_route(self.handle, _ptr(x), _ptr(logits), M, ws, nb, st))
+
+    def gate_up(self, M, stream=None):
+        ws, nb, st = self._args(M, stream)
+        check(self.lib.qmoe_gate_up(self.handle, M, ws, nb, st))
+
+    def down(self, M, stream=None):
+        ws, nb, st = self._args(M, stream)
+        check(self.lib.qmoe_down(self.handle, M, ws, nb, st))
+
+    def combine(self, M, out=None, stream=None):
+        if out is None:
+            out = torch.empty((M, self.H), dtype=torch.bfloat16, device=self.device)
+        ws, nb, st = self._args(M, stream)
+        check(self.lib.qmoe_combine(self.handle, M, _ptr(out), ws, nb, st))
+        return out
+
+    def read_routing(self, M, stream=None) -> dict:
+        dev, k, E = self.device, self.top_k, self.E
+        r = {
+            "ids": torch.empty((M, k), dtype=torch.int32, device=dev),
+            "w": torch.empty((M, k), dtype=torch.float32, device=dev),
+            "counts": torch.empty((E,), dtype=torch.int32, device=dev),
+            "offsets": torch.empty((E + 1,), dtype=torch.int32, device=dev),
+            "perm": torch.empty((M * k,), dtype=torch.int32, device=dev),
+        }
+        ws, nb, st = self._args(M, stream)
+        check(self.lib.qmoe_read_routing(self.handle, M, ws, nb, _ptr(r["ids"]), _ptr(r["w"]),
+                                         _ptr(r["counts"]), _ptr(r["offsets"]), _ptr(r["perm"]), st))
+        return r
+
+    def read_intermediate(self, M, which, stream=None) -> torch.Tensor:
+        rows = M * self.top_k + (M if self.has_shared else 0)
+        cols = self.I if which == 0 else self.H
+        out = torch.empty((rows, cols), dtype=torch.float32, device=self.device)
+        ws, nb, st = self._args(M, stream)
+        check(self.lib.qmoe_read_intermediate(self.handle, M, ws, nb, which, _ptr(out), st))
+        return out
+
+    def dequant_debug(self, expert, which, stream=None) -> torch.Tensor:
+        shape = (2 * self.I, self.H) if which == 0 else (self.H, self.I)
+        out = torch.empty(shape, dtype=torch.int16, device=self.device)
+        check(self.lib.qmoe_dequant_debug(self.handle, expert, which, _ptr(out), _stream(stream)))
+        return out
+
+    def stats(self) -> dict:
+        s = Stats()
+        check(self.lib.qmoe_get_stats(self.handle, ctypes.byref(s)))
+        return s.as_dict()
+
+    def reset_stats(self):
+        check(self.lib.qmoe_reset_stats(self.handle))
+
+
+def layer_from_numpy(weights: dict, *, E, H, I, top_k, max_rows, device="cuda") -> Layer:
+    """Copy numpy weights (as produced by the seeded generators) to the GPU
+    and create a Layer over them."""
+    def dev(a):
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    shared = None
+    if "shared_w13" in weights:
+        shared = {k: dev(weights["shared_" + k]) for k in ("w13", "s13", "w2", "s2")}
+    return Layer(E=E, H=H, I=I, top_k=top_k, max_rows=max_rows,
+                 w13=dev(weights["w13"]), s13=dev(weights["s13"]),
+                 w2=dev(weights["w2"]), s2=dev(weights["s2"]), shared=shared)

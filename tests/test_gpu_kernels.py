@@ -1,0 +1,266 @@
+"""GPU parity of each step of the HIP path against the CPU oracle at sizes
+the oracle finishes in seconds: dequant (bit-exact), routing (bit-exact),
+gate+up (h), down (weighted y) and the whole layer, on shapes that cover
+both tile shapes, several K-steps, ragged tails, the shared expert and the
+degenerate cases."""
+import numpy as np
+import pytest
+
+import synth
+from helpers import (REL_TOL, check_routing, dev, dev_bf16, expert_getter, make_layer, rel_err, say,
+                     shared_of)
+from oracle import moe as oracle_moe
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+# ---------------------------------------------------------------- dequant
+
+
+def _crafted_expert(H, I, seed):
+    """Every code 0..15 in every position class, scales over a wide sweep
+    (the synthetic range's ends, random normal fp16 values, subnormals)."""
+    rng = np.random.default_rng(seed)
+    codes13 = (np.arange(2 * I * H) % 16).reshape(2 * I, H).astype(np.uint8)
+    rng.shuffle(codes13, axis=1)
+    codes2 = rng.integers(0, 16, size=(H, I), dtype=np.uint8)
+    pack = lambda c: (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+    def scales(shape):
+        s = rng.uniform(2.0 ** -10, 16.0, size=shape).astype(np.float16).view(np.uint16)
+        flat = s.reshape(-1)
+        specials = np.array([np.float16(0.002).view(np.uint16), np.float16(0.02).view(np.uint16),
+                             0x0001, 0x0200, 0x03FF, 0x0400, 0x3C00, 0x7BFF >> 2], dtype=np.uint16)
+        flat[:specials.size] = specials
+        return s
+    return {"w13": pack(codes13), "s13": scales((2 * I, H // 32)), "w2": pack(codes2), "s2": scales((H, I // 32))}
+
+
+def test_dequant_bit_exact_against_rne_of_exact_product():
+    H, I, E = 256, 128, 2
+    ex = [_crafted_expert(H, I, 100 + e) for e in range(E)]
+    w = {k: np.stack([x[k] for x in ex]) for k in ex[0]}
+    layer, _ = make_layer(synth.LayerShape(E=E, H=H, I=I, top_k=1), 0, 4, weights=w)
+    for e in range(E):
+        for which, (wk, sk) in enumerate((("w13", "s13"), ("w2", "s2"))):
+            say(f"dequant expert={e} which={which}")
+            got = layer.dequant_debug(e, which).cpu().numpy().view(np.uint16)
+            exact = oracle_moe.dequant(w[wk][e], w[sk][e])  # float64, exact
+            want = exact.astype(np.float16).view(np.uint16)  # one rounding to nearest even
+            assert np.array_equal(got, want), f"expert {e} which {which}"
+
+
+# ---------------------------------------------------------------- routing
+
+ROUTE_CASES = [
+    # E, k, M, logits kind
+    (8, 2, 16, "normal"),
+    (384, 8, 1, "normal"),
+    (384, 8, 9, "normal"),
+    (384, 8, 90, "normal"),
+    (384, 8, 256, "normal"),
+    (384, 8, 1024, "normal"),
+    (384, 8, 4096, "normal"),
+    (384, 8, 512, "zipf"),
+    (64, 4, 300, "ties"),
+    (1000, 32, 70, "normal"),
+    (64, 1, 65, "normal"),
+    (1, 1, 5, "normal"),
+    (16, 16, 130, "normal"),
+    (33, 3, 64, "zeros"),
+]
+
+
+def _logits(kind, seed, M, E):
+    if kind == "zipf":
+        return synth.logits(seed, M, E, skew=True)
+    lg = synth.logits(seed, M, E)
+    if kind == "ties":
+        lg = (np.round(lg * 2.0) / 2.0).astype(np.float32)  # few distinct values: many ties
+    if kind == "zeros":
+        lg = np.where(np.abs(lg) < 0.7, np.float32(0.0), lg).astype(np.float32)
+        lg[:, ::2] = np.where(lg[:, ::2] == 0, np.float32(-0.0), lg[:, ::2])  # +0 and -0 tie
+    return lg
+
+
+@pytest.mark.parametrize("E,k,M,kind", ROUTE_CASES)
+def test_routing_bit_exact(E, k, M, kind):
+    say(f"route E={E} k={k} M={M} {kind}")
+    shape = synth.LayerShape(E=E, H=32, I=32, top_k=k)
+    layer, _ = make_layer(shape, 1, M)
+    x = synth.hidden(2, M, 32)
+    lg = _logits(kind, 3, M, E)
+    layer.route(dev_bf16(x), dev(lg))
+    ref = oracle_moe.route(lg, k)
+    check_routing(layer, M, ref, E)
+
+
+def test_routing_repeatable_and_workspace_reuse():
+    E, k = 384, 8
+    shape = synth.LayerShape(E=E, H=32, I=32, top_k=k)
+    layer, _ = make_layer(shape, 1, 4096)
+    for M in (4096, 7, 1000, 7):  # shrinking and growing M on one workspace
+        say(f"route reuse M={M}")
+        lg = synth.logits(M, M, E)
+        layer.route(dev_bf16(synth.hidden(M, M, 32)), dev(lg))
+        check_routing(layer, M, oracle_moe.route(lg, k), E)
+
+
+# ------------------------------------------------------------ whole layer
+
+FWD_CASES = [
+    # E, H, I, k, M, shared   (decode tiles when M*k < 8E, else 128-row tiles)
+    (8, 256, 128, 2, 16, False),     # the tiny configuration
+    (8, 256, 128, 2, 1, False),
+    (16, 160, 96, 2, 37, False),     # ragged K (1.25 K-steps) and ragged N blocks, decode tiles
+    (64, 128, 64, 2, 9, True),       # decode tiles with a shared expert
+    (4, 160, 96, 2, 300, False),     # 128-row tiles, 2 row tiles per expert, ragged tails
+    (4, 256, 128, 1, 200, True),     # 128-row tiles with a shared expert
+    (4, 512, 256, 4, 20, False),     # top_k = E
+    (8, 1024, 512, 2, 64, False),    # several K-steps per wave in both GEMMs
+    (3, 96, 224, 2, 130, False),     # N not a multiple of the block width
+]
+
+
+def _run_case(E, H, I, k, M, shared, seed=5):
+    shape = synth.LayerShape(E=E, H=H, I=I, top_k=k, shared=shared)
+    layer, w = make_layer(shape, seed, max(M, 1))
+    x = synth.hidden(seed + 1, M, H)
+    lg = synth.logits(seed + 2, M, E)
+    ref = oracle_moe.forward(x, lg, k, expert_getter(w), I, shared=shared_of(w), return_h=True)
+    return layer, w, x, lg, ref
+
+
+@pytest.mark.parametrize("E,H,I,k,M,shared", FWD_CASES)
+def test_forward_parity(E, H, I, k, M, shared):
+    say(f"forward E={E} H={H} I={I} k={k} M={M} shared={shared}")
+    layer, w, x, lg, ref = _run_case(E, H, I, k, M, shared)
+    out = layer.forward(dev_bf16(x), dev(lg)).float().cpu().numpy()
+    check_routing(layer, M, ref, E)
+    err = rel_err(out, ref["out"])
+    say(f"  rel err out {err:.3e}")
+    assert err <= REL_TOL
+
+
+@pytest.mark.parametrize("E,H,I,k,M,shared", [FWD_CASES[2], FWD_CASES[4], FWD_CASES[5]])
+def test_steps_match_oracle_intermediates(E, H, I, k, M, shared):
+    """h = SiLU(gate)*up after the gate+up step and w*y after the down step,
+    per routed slot, against the oracle's float64 values."""
+    say(f"steps E={E} H={H} I={I} k={k} M={M} shared={shared}")
+    layer, w, x, lg, ref = _run_case(E, H, I, k, M, shared)
+    layer.route(dev_bf16(x), dev(lg))
+    layer.gate_up(M)
+    h = layer.read_intermediate(M, 0).cpu().numpy()
+    T = M * k
+    ref_h = np.stack([ref["h"][f] for f in range(T)])
+    assert rel_err(h[:T], ref_h) <= REL_TOL
+    layer.down(M)
+    y = layer.read_intermediate(M, 1).cpu().numpy()
+    xf = oracle_moe.decode_bf16(x)
+    get = expert_getter(w)
+    ref_y = np.zeros((T, H))
+    for t in range(M):
+        for j in range(k):
+            e = int(ref["ids"][t, j])
+            ref_y[t * k + j] = ref["w"][t, j] * oracle_moe.expert_mlp(xf[t:t + 1], get(e), I)[0]
+    assert rel_err(y[:T], ref_y) <= REL_TOL
+    if shared:
+        ref_s = oracle_moe.expert_mlp(xf, shared_of(w), I)
+        assert rel_err(y[T:], ref_s) <= REL_TOL
+    out = layer.combine(M).float().cpu().numpy()
+    assert rel_err(out, ref["out"]) <= REL_TOL
+
+
+def test_diagonal_weights_closed_form_on_gpu():
+    """Top-1 with diagonal weights and power-of-two scales: the output is
+    sd*su*x*SiLU(sg*x) on the first min(H, I) columns and 0 elsewhere."""
+    import math
+    H, I, E, M = 128, 64, 3, 11
+    codes13 = np.full((2 * I, H), 8, np.uint8)
+    for i in range(I):
+        codes13[i, i] = 9
+        codes13[I + i, i] = 9
+    codes2 = np.full((H, I), 8, np.uint8)
+    for n in range(I):
+        codes2[n, n] = 9
+    pack = lambda c: (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+    s13 = np.empty((2 * I, H // 32), np.uint16)
+    s13[:I], s13[I:] = 0x3800, 0x4000  # 0.5, 2.0
+    s2 = np.full((H, I // 32), 0x3400, np.uint16)  # 0.25
+    one = {"w13": pack(codes13), "s13": s13, "w2": pack(codes2), "s2": s2}
+    w = {k: np.stack([one[k]] * E) for k in one}
+    layer, _ = make_layer(synth.LayerShape(E=E, H=H, I=I, top_k=1), 0, M, weights=w)
+    x = synth.hidden(9, M, H)
+    out = layer.forward(dev_bf16(x), dev(synth.logits(9, M, E))).float().cpu().numpy()
+    xf = oracle_moe.decode_bf16(x)
+    expect = np.zeros((M, H))
+    for t in range(M):
+        for n in range(I):
+            v = xf[t, n]
+            g = 0.5 * v
+            expect[t, n] = 0.25 * (2.0 * v) * (g / (1.0 + math.exp(-g)))
+    assert np.all(out[:, I:] == 0.0)
+    assert rel_err(out, expect) <= REL_TOL
+
+
+def test_repeat_runs_bitwise_identical():
+    layer, w, x, lg, ref = _run_case(16, 160, 96, 2, 37, False)
+    xs, ls = dev_bf16(x), dev(lg)
+    import torch
+    a = layer.forward(xs, ls).clone()
+    b = layer.forward(xs, ls).clone()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_zero_tokens_is_a_noop():
+    import torch
+    shape = synth.TINY
+    layer, _ = make_layer(shape, 0, 4)
+    x = torch.empty((0, shape.H), dtype=torch.bfloat16, device="cuda")
+    lg = torch.empty((0, shape.E), dtype=torch.float32, device="cuda")
+    out = layer.forward(x, lg)
+    assert out.shape == (0, shape.H)
+
+
+def test_counters_and_workspace_accounting():
+    shape = synth.TINY
+    layer, _ = make_layer(shape, 0, 16)
+    x, lg = dev_bf16(synth.hidden(0, 16, shape.H)), dev(synth.logits(0, 16, shape.E))
+    layer.forward(x, lg)  # workspace allocated and initialised here
+    layer.reset_stats()
+    layer.forward(x, lg)
+    s = layer.stats()
+    assert s["forward_calls"] == 1 and s["route_calls"] == 1
+    assert s["gemm_launches"] == 2 and s["launches"] == 4
+    assert s["workspace_inits"] == 0
+    assert s["workspace_bytes_last"] == s["workspace_bytes_peak"] == layer.workspace_bytes(16) > 0
+    assert s["decode_tiles"] + s["prefill_tiles"] == 1
+
+
+def test_errors_from_the_library():
+    import torch
+    from quantized_mixture_experts_top_amd import QmoeError
+    from quantized_mixture_experts_top_amd._binding import QMOE_ERR_ARG, QMOE_ERR_WORKSPACE, check
+    import ctypes
+    shape = synth.TINY
+    layer, _ = make_layer(shape, 0, 8)
+    x, lg = dev_bf16(synth.hidden(0, 9, shape.H)), dev(synth.logits(0, 9, shape.E))
+    with pytest.raises(QmoeError) as ei:
+        layer.forward(x, lg)  # M = 9 > max_rows = 8
+    assert ei.value.code == QMOE_ERR_ARG and "max_rows" in ei.value.message
+    small = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    out = torch.empty((8, shape.H), dtype=torch.bfloat16, device="cuda")
+    rc = layer.lib.qmoe_forward(layer.handle, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(lg.data_ptr()), 8,
+                                ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(small.data_ptr()), 1024,
+                                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == QMOE_ERR_WORKSPACE
+    assert "needs" in layer.lib.qmoe_last_error().decode()
+    with pytest.raises(QmoeError):
+        check(layer.lib.qmoe_dequant_debug(layer.handle, shape.E, 0, None, None))
