@@ -80,8 +80,8 @@ enum qmoe_status {
 
 typedef struct {
   int32_t E;          /* routed experts, 1..QMOE_MAX_EXPERTS */
-  int32_t H;          /* hidden size, multiple of 32 */
-  int32_t I;          /* intermediate size, multiple of 32 */
+  int32_t H;          /* hidden size, multiple of 128 */
+  int32_t I;          /* intermediate size, multiple of 128 */
   int32_t top_k;      /* 1..min(E, QMOE_MAX_TOPK) */
   int32_t group_size; /* must be 32 */
   int32_t max_rows;   /* largest M a forward call may pass (>= 1) */

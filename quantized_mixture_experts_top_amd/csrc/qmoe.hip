@@ -36,7 +36,40 @@ namespace {
 constexpr int kThreads = 256;   // every kernel: 4 waves of 64
 constexpr int kChunk = 64;      // tokens per routing chunk = bits of one mask word
 constexpr int kCtrlWords = 64;  // [0] route ticket, [1] number of work items
+constexpr int kZeroWords = 64;  // 256 zero bytes after the control words
 constexpr int kKStep = 128;     // inputs per K-step of a wave (4 lane groups x 32)
+
+// Tile shapes (compile-time; one of the two shapes is picked per call from
+// M*top_k vs E).  NBW = 16-column output blocks per wave, WN x WK = waves of
+// a block along N and K, PF = K-steps of loads in flight beyond the current.
+#ifndef QMOE_DEC_GU_NBW
+#define QMOE_DEC_GU_NBW 1
+#endif
+#ifndef QMOE_DEC_GU_WN
+#define QMOE_DEC_GU_WN 2
+#endif
+#ifndef QMOE_DEC_GU_PF
+#define QMOE_DEC_GU_PF 3
+#endif
+#ifndef QMOE_DEC_DN_NBW
+#define QMOE_DEC_DN_NBW 1
+#endif
+#ifndef QMOE_DEC_DN_WN
+#define QMOE_DEC_DN_WN 4
+#endif
+#ifndef QMOE_DEC_DN_PF
+#define QMOE_DEC_DN_PF 3
+#endif
+#ifndef QMOE_PRE_MB
+#define QMOE_PRE_MB 8
+#endif
+#ifndef QMOE_PRE_GU_NBW
+#define QMOE_PRE_GU_NBW 1
+#endif
+#ifndef QMOE_PRE_DN_NBW
+#define QMOE_PRE_DN_NBW 2
+#endif
+constexpr int kPrefillRows = QMOE_PRE_MB * 16;
 constexpr int kAStride = kKStep + 8;  // LDS row stride of the A tile (halves), padded
 
 // ---------------------------------------------------------------- routing
@@ -58,11 +91,15 @@ struct RouteArgs {
   uint4* xa;  // fp16 A-format [M, H]
 };
 
-// Exclusive scan of in[0..n) into out[0..n] (out[n] = total) by the 256
-// threads of a block: each thread sums 5 consecutive entries, a wave-wide
-// Hillis-Steele scan over lanes combines them, then the 4 wave totals.
+constexpr int kRouteThreads = 1024;  // routing blocks: 16 waves
+constexpr int kRouteWaves = kRouteThreads / 64;
+
+// Exclusive scan of in[0..n) into out[0..n] (out[n] = total) by the 1024
+// threads of a routing block: each thread sums 2 consecutive entries, a
+// wave-wide Hillis-Steele scan over lanes combines them, then the 16 wave
+// totals.  This replaces a serial loop over the expert counts.
 __device__ void block_exclusive_scan(const int* in, int* out, int n, int* wsum) {
-  constexpr int kPer = 5;  // 256 * 5 >= QMOE_MAX_EXPERTS + 1
+  constexpr int kPer = 2;  // 1024 * 2 >= QMOE_MAX_EXPERTS + 1
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int v[kPer];
   int local = 0;
@@ -88,33 +125,32 @@ __device__ void block_exclusive_scan(const int* in, int* out, int n, int* wsum) 
     if (idx < n) out[idx] = run;
     run += v[i];
   }
-  if (tid == kThreads - 1) out[n] = run;
+  if (tid == kRouteThreads - 1) out[n] = run;
   __syncthreads();
 }
 
 // One block per chunk of 64 tokens; the last block to finish (atomic ticket,
-// no waiting) turns the per-chunk masks into counts, offsets, positions and
-// work items.  EPL = logits per lane (E <= 64 * EPL).
+// no waiting) turns the per-chunk token masks into counts, offsets,
+// positions and work items.  EPL = logits per lane (E <= 64 * EPL).
 template <int EPL>
-__global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   __shared__ uint32_t cm[QMOE_MAX_EXPERTS][2];
   __shared__ int s_cnt[QMOE_MAX_EXPERTS + 2];
   __shared__ int s_off[QMOE_MAX_EXPERTS + 2];
   __shared__ int s_ni[QMOE_MAX_EXPERTS + 2];
   __shared__ int s_ioff[QMOE_MAX_EXPERTS + 2];
-  __shared__ int s_wsum[4];
+  __shared__ int s_wsum[kRouteWaves];
   __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = blockIdx.x, E = a.E, k = a.k;
+  const int rows = min(kChunk, a.M - c * kChunk);
 
-  for (int e = tid; e < E; e += kThreads) cm[e][0] = cm[e][1] = 0u;
+  for (int e = tid; e < E; e += kRouteThreads) cm[e][0] = cm[e][1] = 0u;
   __syncthreads();
 
-  // ---- phase 1: each wave routes 16 tokens of the chunk
-  for (int i = 0; i < kChunk / 4; ++i) {
-    const int tl = wave * (kChunk / 4) + i;
+  // ---- phase 1a: top-k of each token, one wave per token
+  for (int tl = wave; tl < rows; tl += kRouteWaves) {
     const int t = c * kChunk + tl;
-    if (t >= a.M) break;
     const float* row = a.logits + (size_t)t * E;
     // key = (order-preserving logit bits, ~expert): the maximum key is the
     // largest logit, ties to the lowest expert index.  Absent experts = 0.
@@ -129,11 +165,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
       uint64_t best = 0;
 #pragma unroll
       for (int s = 0; s < EPL; ++s) best = key[s] > best ? key[s] : best;
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        const uint64_t o = shfl_xor_u64(best, m);
-        best = o > best ? o : best;
-      }
+      best = wave_max_u64(best);
       const int e_sel = (int)(~(uint32_t)best);
 #pragma unroll
       for (int s = 0; s < EPL; ++s)
@@ -153,44 +185,78 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
       a.wts[(size_t)t * k + lane] = ex / sum;
       atomicOr(&cm[my_e][tl >> 5], 1u << (tl & 31));
     }
-    // x row -> fp16 operand format
-    const uint4* xs = a.x + (size_t)t * (a.H / 8);
-    uint4* xd = a.xa + (size_t)t * (a.H / 8);
-    for (int ch = lane; ch < a.H / 8; ch += 64) xd[ch] = bf16x8_to_aformat(xs[ch]);
+  }
+
+  // ---- phase 1b: the chunk's x rows -> fp16 operand format (contiguous)
+  {
+    const long long n = (long long)rows * (a.H / 8);
+    const uint4* xs = a.x + (size_t)c * kChunk * (a.H / 8);
+    uint4* xd = a.xa + (size_t)c * kChunk * (a.H / 8);
+    for (long long q0 = tid; q0 < n; q0 += 4 * kRouteThreads) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const long long q = q0 + u * kRouteThreads;
+        v[u] = q < n ? xs[q] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const long long q = q0 + u * kRouteThreads;
+        if (q < n) xd[q] = bf16x8_to_aformat(v[u]);
+      }
+    }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += kThreads)
+  for (int e = tid; e < E; e += kRouteThreads)
     a.cmask[(size_t)c * E + e] = (unsigned long long)cm[e][0] | ((unsigned long long)cm[e][1] << 32);
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(a.ctrl, 1) == a.C - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+  if (a.C > 1) {
+    // several blocks: the last one to arrive (device-scope ticket) finishes
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = (atomicAdd(a.ctrl, 1) == a.C - 1);
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+  } else {
+    // one block (M <= 64): its own writes are visible to it after a barrier
+    __syncthreads();
+  }
 
   // ---- phase 2 (last block only)
-  const int T = a.M * k;
-  for (int e = tid; e < E; e += kThreads) {
-    int n = 0;
-    for (int cc = 0; cc < a.C; ++cc) n += __popcll(a.cmask[(size_t)cc * E + e]);
-    s_cnt[e] = n;
+  // per expert (one thread each), walk the chunks in order: the count, and
+  // each chunk's first rank within the expert; loads are batched by 8
+  {
+    const unsigned long long* __restrict__ cmask = a.cmask;
+    int* __restrict__ pbase = a.pbase;
+    for (int e = tid; e < E; e += kRouteThreads) {
+      int run = 0, cc = 0;
+      for (; cc + 8 <= a.C; cc += 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = __popcll(cmask[(size_t)(cc + u) * E + e]);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          pbase[(size_t)(cc + u) * E + e] = run;
+          run += v[u];
+        }
+      }
+      for (; cc < a.C; ++cc) {
+        const int v = __popcll(cmask[(size_t)cc * E + e]);
+        pbase[(size_t)cc * E + e] = run;
+        run += v;
+      }
+      s_cnt[e] = run;
+    }
   }
   if (tid == 0) s_cnt[E] = a.S;  // the shared expert takes every token
   __syncthreads();
-  for (int e = tid; e <= E; e += kThreads) s_ni[e] = (s_cnt[e] + a.bmc - 1) / a.bmc;
+  for (int e = tid; e <= E; e += kRouteThreads) s_ni[e] = (s_cnt[e] + a.bmc - 1) / a.bmc;
   __syncthreads();
   block_exclusive_scan(s_cnt, s_off, E + 1, s_wsum);
   block_exclusive_scan(s_ni, s_ioff, E + 1, s_wsum);
-  for (int e = tid; e <= E; e += kThreads) a.counts[e] = s_cnt[e];
-  for (int e = tid; e <= E + 1; e += kThreads) a.offsets[e] = s_off[e];
-  for (int e = tid; e < E; e += kThreads) {
-    int run = s_off[e];
-    for (int cc = 0; cc < a.C; ++cc) {
-      a.pbase[(size_t)cc * E + e] = run;
-      run += __popcll(a.cmask[(size_t)cc * E + e]);
-    }
-  }
-  for (int e = tid; e <= E; e += kThreads) {
+  for (int e = tid; e <= E; e += kRouteThreads) a.counts[e] = s_cnt[e];
+  for (int e = tid; e <= E + 1; e += kRouteThreads) a.offsets[e] = s_off[e];
+  for (int e = tid; e <= E; e += kRouteThreads) {
     const int base = s_ioff[e], n = s_cnt[e];
     for (int i = 0; i < s_ni[e]; ++i) {
       const int r0 = i * a.bmc;
@@ -198,20 +264,49 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
     }
   }
   if (tid == 0) a.ctrl[1] = min(s_ioff[E + 1], a.max_items);
-  __threadfence();
+  if (a.C > 1) __threadfence();
   __syncthreads();
-  for (int f = tid; f < T; f += kThreads) {
-    const int t = f / k, e = a.ids[f];
-    const int cc = t / kChunk, tl = t % kChunk;
-    const unsigned long long m = a.cmask[(size_t)cc * E + e];
-    const int rank = __popcll(m & ((1ull << tl) - 1ull));
-    const int pos = a.pbase[(size_t)cc * E + e] + rank;
-    a.perm[pos] = f;
-    a.inv_perm[f] = pos;
+  // sorted position of every routed slot: expert offset + rank of the
+  // token's chunk + rank inside the chunk (popcount of the lower mask bits)
+  {
+    const int* __restrict__ ids = a.ids;
+    const unsigned long long* __restrict__ cmask = a.cmask;
+    const int* __restrict__ pbase = a.pbase;
+    int* __restrict__ perm = a.perm;
+    int* __restrict__ inv_perm = a.inv_perm;
+    for (int t = tid; t < a.M; t += kRouteThreads) {
+      const int cc = t / kChunk, tl = t % kChunk;
+      const unsigned long long below = (1ull << tl) - 1ull;
+      for (int j0 = 0; j0 < k; j0 += 8) {
+        const int nj = min(8, k - j0);
+        int e[8], pb[8];
+        unsigned long long mk[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) e[u] = u < nj ? ids[t * k + j0 + u] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const size_t ce = (size_t)cc * E + e[u];
+          pb[u] = u < nj ? pbase[ce] : 0;
+          mk[u] = u < nj ? cmask[ce] : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (u < nj) {
+            const int f = t * k + j0 + u;
+            const int pos = s_off[e[u]] + pb[u] + __popcll(mk[u] & below);
+            perm[pos] = f;
+            inv_perm[f] = pos;
+          }
+        }
+      }
+    }
   }
-  for (int t = tid; t < a.S; t += kThreads) a.perm[T + t] = T + t;
-  __syncthreads();
-  if (tid == 0) atomicExch(a.ctrl, 0);
+  const int T = a.M * k;
+  for (int t = tid; t < a.S; t += kRouteThreads) a.perm[T + t] = T + t;
+  if (a.C > 1) {
+    __syncthreads();
+    if (tid == 0) atomicExch(a.ctrl, 0);
+  }
 }
 
 // ------------------------------------------------------------------ GEMMs
@@ -227,45 +322,78 @@ struct GemmArgs {
   const int* perm;
   const float* wts;
   const _Float16* a;  // A rows in A-format: x (gate+up) or h (down)
+  uint32_t a_bytes;      // bytes of the A buffer (loads past it read 0)
   _Float16* h_out;    // gate+up: h [R, N] in A-format
   float* y_out;       // down: y [R, N] in slot order
 };
 
-template <int NBB, int MB>
+template <int NBB>
 struct Frag {
-  uint4 b[NBB];       // 32 packed codes of this lane's weight row per block
-  uint32_t sc[NBB];   // the group's fp16 scale bits
+  u32x4_t b[NBB];  // 32 packed codes of this lane's weight row per block
 };
 
-__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+__device__ __forceinline__ uint32_t word(const u32x4_t& v, int i) { return v[i]; }
+
+// The fp16 scale of sub-step u from a lane's 4 scales (2 dwords), duplicated
+// into both halves of a dword: one byte permute.
+__device__ __forceinline__ uint32_t scale_pair(uint32_t lo, uint32_t hi, int u) {
+  const uint32_t sel = u == 0 ? 0x01000100u : u == 1 ? 0x03020302u : u == 2 ? 0x05040504u : 0x07060706u;
+  return __builtin_amdgcn_perm(hi, lo, sel);
 }
+
+// Raw buffer resource over [base, base + bytes): loads take a 32-bit per-lane
+// offset and a scalar per-step offset, and read 0 past the end.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kOob = 0x7FFFFF00u;  // a lane offset past any buffer: its loads read 0
+constexpr int kSuper = 4 * kKStep;     // inputs per super-step (16 groups)
 
 // One work item = (expert, up to MB*16 routed rows) x (an N range).  A block
 // has 4 waves: WN waves along N (each NBW blocks of 16 output columns) times
 // WK waves along K (partial sums reduced through LDS in a fixed order).
-// Per K-step a lane of group kq (= lane/16) decodes the 32 codes of inputs
-// [k0 + 32kq, +32) of one weight row: one 16-byte load and one scale.
-// MB == 1: A rows are read straight from global memory (decode, few rows);
-// MB > 1: the block stages the A tile for each K-step in LDS.
-template <int MB, int NBW, int WN, int WK, bool GATEUP>
+//
+// K is walked in super-steps of 512 inputs (16 groups of 32).  Lane group kq
+// (= lane/16) owns groups 4kq..4kq+3 of each super-step and decodes one per
+// sub-step u: the 16 code bytes at 64kq + 16u of the row's 256-byte chunk
+// (so four sub-steps read every byte of the chunk) and the group's scale,
+// all four scales coming from one 8-byte load per super-step.  The MFMA
+// k-slot order is free as long as the activations follow it, so the
+// activation fragment of sub-step u, MFMA i is inputs (4kq+u)*32 + 8i .. +8.
+// MB == 1: activations are read straight from global memory (decode, few
+// rows); MB > 1: the block stages each sub-step's activation tile in LDS.
+// Loads are buffer loads with a fixed per-lane offset and a scalar
+// per-step offset (no vector address arithmetic); inputs past K read zeros.
+template <int MB, int NBW, int WN, int WK, int PF, bool GATEUP>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   static_assert(WN * WK == 4, "4 waves per block");
+  static_assert(PF == 3, "the sub-step ring holds one super-step");
   constexpr int NBB = GATEUP ? 2 * NBW : NBW;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index as a wave-uniform (scalar) value, so loop bounds derived
+  // from it give scalar branches and exact load counters
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave % WN, wk = wave / WN;
   const int r = lane & 15, kq = lane >> 4;
 
+#ifndef QMOE_XCD_MAP
+#define QMOE_XCD_MAP 1
+#endif
+#if QMOE_XCD_MAP == 1
   // all blocks of one item land on one XCD (block ids go round-robin over 8)
   const int bid = blockIdx.x, xcd = bid & 7, jj = bid >> 3;
   const int item = (jj / g.nblk) * 8 + xcd, nb = jj % g.nblk;
+#else
+  // consecutive blocks take consecutive N-blocks of one item (spread over XCDs)
+  const int item = blockIdx.x / g.nblk, nb = blockIdx.x % g.nblk;
+#endif
   const int n_items = min(g.ctrl[1], g.max_items);
   if (item >= n_items) return;
   const int4 it = g.items[item];
   const int e = it.x, nr = it.z, pos0 = it.w;
   // work items come from the workspace: reject any that do not fit it
   if (e < 0 || e > g.E || nr <= 0 || nr > MB * 16 || pos0 < 0 || pos0 > g.R - nr) return;
-  const size_t K2 = (size_t)g.K / 2, KG = (size_t)g.K / 32;
+  const uint32_t K2 = (uint32_t)g.K / 2, KG = (uint32_t)g.K / 32;
   const uint8_t* wb;
   const uint16_t* sbase;
   if (e < g.E) {
@@ -276,28 +404,35 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     wb = g.w_sh;
     sbase = g.s_sh;
   }
+  const __amdgpu_buffer_rsrc_t rB = buffer_rsrc(wb, (uint32_t)g.Nw * K2);
+  const __amdgpu_buffer_rsrc_t rS = buffer_rsrc(sbase, (uint32_t)g.Nw * KG * 2);
+  const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(g.a, g.a_bytes);
 
-  // weight rows of this lane, per B block
-  const uint8_t* brow[NBB];
-  const uint16_t* srow[NBB];
+  // byte offsets of this lane's code chunk and scale quad, per B block
+  uint32_t boff[NBB], soff[NBB];
   int col0[NBW];
 #pragma unroll
   for (int c = 0; c < NBW; ++c) {
     col0[c] = ((nb * WN + wn) * NBW + c) * 16;
-    const int n = col0[c] < g.N ? col0[c] + r : 0;
+    const uint32_t n = col0[c] < g.N ? col0[c] + r : 0;
     if (GATEUP) {
-      brow[2 * c] = wb + (size_t)n * K2;
-      srow[2 * c] = sbase + (size_t)n * KG;
-      brow[2 * c + 1] = wb + (size_t)(g.N + n) * K2;
-      srow[2 * c + 1] = sbase + (size_t)(g.N + n) * KG;
+      boff[2 * c] = n * K2 + 64 * kq;
+      soff[2 * c] = n * KG * 2 + 8 * kq;
+      boff[2 * c + 1] = (g.N + n) * K2 + 64 * kq;
+      soff[2 * c + 1] = (g.N + n) * KG * 2 + 8 * kq;
     } else {
-      brow[c] = wb + (size_t)n * K2;
-      srow[c] = sbase + (size_t)n * KG;
+      boff[c] = n * K2 + 64 * kq;
+      soff[c] = n * KG * 2 + 8 * kq;
     }
   }
 
-  const int nsteps = (g.K + kKStep - 1) / kKStep;
-  const int s_begin = wk * nsteps / WK, s_end = (wk + 1) * nsteps / WK;
+  // super-steps: nss_full whole ones, then (if K % 512 != 0) one partial,
+  // taken by the last wave along K with its missing groups masked
+  const int nss_full = g.K / kSuper, nss = (g.K + kSuper - 1) / kSuper;
+  const int S_begin = wk * nss / WK, S_end = (wk + 1) * nss / WK;
+  const int S_end_full = min(S_end, nss_full);
+  const bool has_tail = S_end > nss_full;
+  const int ngroups = g.K / 32;
   const int nmb = (nr + 15) / 16;
 
   float4_t acc[MB][NBB];
@@ -306,114 +441,208 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int b = 0; b < NBB; ++b) acc[mb][b] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto load_b = [&](int s, Frag<NBB, MB>& f) {
-    const int kk = s * kKStep + 32 * kq;
-    const bool kv = kk < g.K;
+  // codes of sub-step u of super-step S (ok: this lane's group exists)
+  auto load_b = [&](int S, int u, Frag<NBB>& f, bool ok) __attribute__((always_inline)) {
+#pragma unroll
+    for (int b = 0; b < NBB; ++b)
+      f.b[b] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rB, ok ? boff[b] + 16 * u : kOob, S * (kSuper / 2), 0));
+  };
+  // the four scales of super-step S, as two dwords per B block
+  auto load_sc = [&](int S, uint32_t (&sc)[NBB][2], bool ok) __attribute__((always_inline)) {
 #pragma unroll
     for (int b = 0; b < NBB; ++b) {
-      f.b[b] = kv ? *reinterpret_cast<const uint4*>(brow[b] + kk / 2)
-                  : make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-      f.sc[b] = kv ? (uint32_t)srow[b][kk / 32] : 0u;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rS, ok ? soff[b] : kOob, S * 32, 0);
+      sc[b][0] = v[0];
+      sc[b][1] = v[1];
     }
   };
-
-  // A source row (element offset of the row start) of tile row m, -1 if absent
-  auto a_row_of = [&](int m) -> long long {
-    if (m >= nr) return -1;
+  // byte offset of the activation row of tile row m (m < nr)
+  auto a_off_of = [&](int m) __attribute__((always_inline)) -> uint32_t {
     const int pos = pos0 + m;
     if (GATEUP) {
       const int slot = g.perm[pos];
-      if (slot < 0 || slot >= g.R) return -1;
+      if (slot < 0 || slot >= g.R) return kOob;
       const int tok = slot < g.T ? slot / g.k : slot - g.T;
-      if (tok >= g.M) return -1;
-      return (long long)tok * g.K;
+      if (tok >= g.M) return kOob;
+      return (uint32_t)tok * (uint32_t)g.K * 2;
     }
-    return (long long)pos * g.K;
+    return (uint32_t)pos * (uint32_t)g.K * 2;
   };
 
   if constexpr (MB == 1) {
-    // ---------------- decode tiles: A straight from global memory
-    const long long arow = a_row_of(r);
-    uint4 aq[4], aqn[4];
-    Frag<NBB, MB> f, fn;
-    auto load_a = [&](int s, uint4 (&q)[4]) {
-      const int kk = s * kKStep + 32 * kq;
-      const bool ok = arow >= 0 && kk < g.K;
-      const uint4* p = reinterpret_cast<const uint4*>(g.a + (ok ? arow + kk : 0));
+    // ---------------- decode tiles: activations straight from global memory,
+    // a ring of 4 sub-steps (one super-step) of loads in flight per wave.
+    // Rows past nr read a real row (their MFMA rows are never stored).
+    const uint32_t arow = a_off_of(min(r, nr - 1));
+    const uint32_t aoff = arow == kOob ? kOob : arow + 256 * kq;
+    Frag<NBB> fb[4];   // weight ring: 3 sub-steps ahead (HBM latency)
+    u32x4_t fa[2][4];  // activation ring: 1 sub-step ahead (L2-resident rows)
+    uint32_t sc_cur[NBB][2], sc_nxt[NBB][2];
+    auto load_a = [&](int S, int u, u32x4_t (&q)[4], bool ok) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) q[i] = ok ? p[i] : make_uint4(0u, 0u, 0u, 0u);
+      for (int i = 0; i < 4; ++i)
+        q[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rA, ok ? aoff + 64 * u + 16 * i : kOob, S * (kSuper * 2), 0));
     };
-    if (s_begin < s_end) {
-      load_b(s_begin, f);
-      load_a(s_begin, aq);
-    }
-    for (int s = s_begin; s < s_end; ++s) {
-      if (s + 1 < s_end) {
-        load_b(s + 1, fn);
-        load_a(s + 1, aqn);
-      }
+    auto compute = [&](const Frag<NBB>& fbu, const u32x4_t (&fau)[4], const uint32_t (&sc)[NBB][2], int u)
+                       __attribute__((always_inline)) {
+      uint32_t s2[NBB];
+#pragma unroll
+      for (int b = 0; b < NBB; ++b) s2[b] = scale_pair(sc[b][0], sc[b][1], u);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const half8_t av = __builtin_bit_cast(half8_t, aq[i]);
+        const half8_t av = __builtin_bit_cast(half8_t, fau[i]);
 #pragma unroll
-        for (int b = 0; b < NBB; ++b) acc[0][b] = mfma16x16x32(av, dq8(word(f.b[b], i), f.sc[b]), acc[0][b]);
-      }
-      f = fn;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) aq[i] = aqn[i];
-    }
-  } else {
-    // ---------------- prefill tiles: A tile of the K-step staged in LDS
-    __shared__ __attribute__((aligned(16))) _Float16 lds_a[MB * 16 * kAStride];
-    __shared__ long long lds_row[MB * 16];
-    for (int m = tid; m < MB * 16; m += kThreads) lds_row[m] = a_row_of(m);
-    __syncthreads();
-    // thread -> 16-byte segment `seg` of rows (tid/16) + 16*i of the tile
-    const int seg = tid & 15, row_base = tid >> 4;
-    constexpr int kRowsPerThread = MB;  // MB*16 rows / 16 row groups
-    uint4 st[kRowsPerThread];
-    auto load_a_tile = [&](int s) {
-      const int kk = s * kKStep + seg * 8;
-#pragma unroll
-      for (int i = 0; i < kRowsPerThread; ++i) {
-        const long long ar = lds_row[row_base + 16 * i];
-        st[i] = (ar >= 0 && kk < g.K) ? *reinterpret_cast<const uint4*>(g.a + ar + kk)
-                                      : make_uint4(0u, 0u, 0u, 0u);
+        for (int b = 0; b < NBB; ++b) acc[0][b] = mfma16x16x32(av, dq8p(word(fbu.b[b], i), s2[b]), acc[0][b]);
       }
     };
-    Frag<NBB, MB> f, fn;
-    // every wave of the block runs the same K range here (WK == 1 for MB > 1)
-    if (s_begin < s_end) {
-      load_b(s_begin, f);
-      load_a_tile(s_begin);
-    }
-    for (int s = s_begin; s < s_end; ++s) {
-      __syncthreads();
+    // Steady state: super-step S computes sub-steps u = 0..3 from weight
+    // slot u while loading the weights of sub-step u+3 (the next super-step's
+    // u-1 for u >= 1), the activations of sub-step u+1, and the next
+    // super-step's scales.  No branches: prefetches past the wave's range are
+    // clamped to its last super-step (cache hits), so the compiler counts
+    // outstanding loads exactly.
+    const int n = S_end_full - S_begin;
+    if (n > 0) {
+      load_sc(S_begin, sc_cur, true);
 #pragma unroll
-      for (int i = 0; i < kRowsPerThread; ++i)
-        *reinterpret_cast<uint4*>(&lds_a[(row_base + 16 * i) * kAStride + seg * 8]) = st[i];
-      __syncthreads();
-      if (s + 1 < s_end) {
-        load_b(s + 1, fn);
-        load_a_tile(s + 1);
-      }
+      for (int u = 0; u < 3; ++u) load_b(S_begin, u, fb[u], true);
+      load_a(S_begin, 0, fa[0], true);
+      for (int S = S_begin; S < S_end_full; ++S) {
+        const int Sn = min(S + 1, S_end_full - 1);
+        load_sc(Sn, sc_nxt, true);
+        load_b(S, 3, fb[3], true);
+        load_a(S, 1, fa[1], true);
+        compute(fb[0], fa[0], sc_cur, 0);
+        load_b(Sn, 0, fb[0], true);
+        load_a(S, 2, fa[0], true);
+        compute(fb[1], fa[1], sc_cur, 1);
+        load_b(Sn, 1, fb[1], true);
+        load_a(S, 3, fa[1], true);
+        compute(fb[2], fa[0], sc_cur, 2);
+        load_b(Sn, 2, fb[2], true);
+        load_a(Sn, 0, fa[0], true);
+        compute(fb[3], fa[1], sc_cur, 3);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        half8_t bf[NBB];
-#pragma unroll
-        for (int b = 0; b < NBB; ++b) bf[b] = dq8(word(f.b[b], i), f.sc[b]);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          if (mb < nmb) {
-            const half8_t av =
-                *reinterpret_cast<const half8_t*>(&lds_a[(mb * 16 + r) * kAStride + 32 * kq + 8 * i]);
-#pragma unroll
-            for (int b = 0; b < NBB; ++b) acc[mb][b] = mfma16x16x32(av, bf[b], acc[mb][b]);
-          }
+        for (int b = 0; b < NBB; ++b) {
+          sc_cur[b][0] = sc_nxt[b][0];
+          sc_cur[b][1] = sc_nxt[b][1];
         }
       }
-      f = fn;
     }
+    if (has_tail) {  // the partial super-step: groups past K read zeros
+      load_sc(nss_full, sc_cur, true);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool ok = nss_full * 16 + 4 * kq + u < ngroups;
+        load_b(nss_full, u, fb[u], ok);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool ok = nss_full * 16 + 4 * kq + u < ngroups;
+        load_a(nss_full, u, fa[0], ok);
+        compute(fb[u], fa[0], sc_cur, u);
+      }
+    }
+  } else {
+    // ---------------- prefill tiles: the activation tile of each sub-step
+    // (MB*16 rows x 128 inputs, in MFMA k order) staged in LDS
+    static_assert(WK == 1, "128-row tiles split N across waves, not K");
+    __shared__ __attribute__((aligned(16))) _Float16 lds_a[MB * 16 * kAStride];
+    __shared__ uint32_t lds_row[MB * 16];
+    for (int m = tid; m < MB * 16; m += kThreads) lds_row[m] = m < nr ? a_off_of(m) : kOob;
+    __syncthreads();
+    // thread -> 16-byte segment seg of rows (tid/16) + 16*i of the tile;
+    // tile column 32*q + 8*v (q = seg/4, v = seg%4) holds inputs
+    // (4q+u)*32 + 8v .. +8 of the super-step
+    const int seg = tid & 15, row_base = tid >> 4;
+    const int sq = seg >> 2, sv = seg & 3;
+    constexpr int kRowsPerThread = MB;  // MB*16 rows / 16 row groups
+    uint32_t aoffs[kRowsPerThread];
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) {
+      const uint32_t o = lds_row[row_base + 16 * i];
+      aoffs[i] = o == kOob ? kOob : o + 256 * sq + 16 * sv;
+    }
+    u32x4_t st[kRowsPerThread];  // native vectors: an array of uint4 structs stays in scratch
+    uint32_t sc_cur[NBB][2], sc_nxt[NBB][2];
+    Frag<NBB> fb0, fb1;
+#define QMOE_LOAD_A_TILE(S, U, OK)                                                                 \
+  do {                                                                                             \
+    _Pragma("unroll") for (int i = 0; i < kRowsPerThread; ++i) st[i] = __builtin_bit_cast(         \
+        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rA, (OK) ? aoffs[i] + 64 * (U) : kOob,      \
+                                                       (S) * (kSuper * 2), 0));                    \
+  } while (0)
+#define QMOE_STORE_A_TILE()                                                                        \
+  do {                                                                                             \
+    _Pragma("unroll") for (int i = 0; i < kRowsPerThread; ++i)                                     \
+        *reinterpret_cast<u32x4_t*>(&lds_a[(row_base + 16 * i) * kAStride + seg * 8]) = st[i];    \
+  } while (0)
+#define QMOE_COMPUTE(F, SC, U)                                                                     \
+  do {                                                                                             \
+    uint32_t s2_[NBB];                                                                             \
+    _Pragma("unroll") for (int b = 0; b < NBB; ++b) s2_[b] = scale_pair((SC)[b][0], (SC)[b][1], (U)); \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                \
+      half8_t bf[NBB];                                                                             \
+      _Pragma("unroll") for (int b = 0; b < NBB; ++b) bf[b] = dq8p(word((F).b[b], i), s2_[b]);     \
+      _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                                          \
+        if (mb < nmb) {                                                                            \
+          const half8_t av =                                                                       \
+              *reinterpret_cast<const half8_t*>(&lds_a[(mb * 16 + r) * kAStride + 32 * kq + 8 * i]); \
+          _Pragma("unroll") for (int b = 0; b < NBB; ++b) acc[mb][b] = mfma16x16x32(av, bf[b], acc[mb][b]); \
+        }                                                                                          \
+      }                                                                                            \
+    }                                                                                              \
+  } while (0)
+    // one sub-step: publish the staged tile, prefetch the next sub-step
+    // (clamped, unconditional), then compute
+#define QMOE_SUBSTEP(S, U, FCUR, FNEXT, SN, UN)                                                    \
+  do {                                                                                             \
+    __syncthreads();                                                                               \
+    QMOE_STORE_A_TILE();                                                                           \
+    __syncthreads();                                                                               \
+    load_b((SN), (UN), FNEXT, true);                                                               \
+    QMOE_LOAD_A_TILE((SN), (UN), true);                                                            \
+    QMOE_COMPUTE(FCUR, sc_cur, (U));                                                               \
+  } while (0)
+    const int n = S_end_full - S_begin;
+    if (n > 0) {
+      load_sc(S_begin, sc_cur, true);
+      load_b(S_begin, 0, fb0, true);
+      QMOE_LOAD_A_TILE(S_begin, 0, true);
+      for (int S = S_begin; S < S_end_full; ++S) {
+        const int Sn = min(S + 1, S_end_full - 1);
+        load_sc(Sn, sc_nxt, true);
+        QMOE_SUBSTEP(S, 0, fb0, fb1, S, 1);
+        QMOE_SUBSTEP(S, 1, fb1, fb0, S, 2);
+        QMOE_SUBSTEP(S, 2, fb0, fb1, S, 3);
+        QMOE_SUBSTEP(S, 3, fb1, fb0, Sn, 0);
+#pragma unroll
+        for (int b = 0; b < NBB; ++b) {
+          sc_cur[b][0] = sc_nxt[b][0];
+          sc_cur[b][1] = sc_nxt[b][1];
+        }
+      }
+    }
+    if (has_tail) {  // the partial super-step: groups past K read zeros
+      load_sc(nss_full, sc_cur, true);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool okb = nss_full * 16 + 4 * kq + u < ngroups;
+        const bool oka = nss_full * 16 + 4 * sq + u < ngroups;
+        load_b(nss_full, u, fb0, okb);
+        QMOE_LOAD_A_TILE(nss_full, u, oka);
+        __syncthreads();
+        QMOE_STORE_A_TILE();
+        __syncthreads();
+        QMOE_COMPUTE(fb0, sc_cur, u);
+      }
+    }
+#undef QMOE_SUBSTEP
+#undef QMOE_COMPUTE
+#undef QMOE_STORE_A_TILE
+#undef QMOE_LOAD_A_TILE
   }
 
   // ---- reduce the WK partial sums (fixed order: wave wk=0 adds 1, 2, 3)
@@ -457,7 +686,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
         const int pos = pos0 + row;
         if (GATEUP) {
           const float gt = acc[mb][2 * c][i], up = acc[mb][2 * c + 1][i];
-          const float hv = gt / (1.0f + __expf(-gt)) * up;
+          // odd columns are stored divided by 16 (operand format)
+          const float hv = gt / (1.0f + __expf(-gt)) * up * ((col & 1) ? 0.0625f : 1.0f);
           g.h_out[(size_t)pos * g.N + ((col & ~7) | inv_perm8(col & 7))] = (_Float16)hv;
         } else {
           const int slot = g.perm[pos];
@@ -509,8 +739,12 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t* w, co
   const int per_row = K / 8;
   if (idx >= (long long)N * per_row) return;
   const int n = (int)(idx / per_row), d = (int)(idx % per_row);
+  half8_t v = dq8(w[idx], s[(size_t)n * (K / 32) + d / 4]);
+#pragma unroll
+  for (int p = 0; p < 8; ++p)
+    if (x16_pos(p)) v[p] = v[p] * (_Float16)0.0625f;  // exact: undo the operand's x16
   // bit-cast the whole vector (a bit-cast of one vector element reads element 0)
-  const u16x8_t h = __builtin_bit_cast(u16x8_t, dq8(w[idx], s[(size_t)n * (K / 32) + d / 4]));
+  const u16x8_t h = __builtin_bit_cast(u16x8_t, v);
 #pragma unroll
   for (int p = 0; p < 8; ++p) out[(size_t)n * K + d * 8 + perm8(p)] = h[p];
 }
@@ -523,11 +757,12 @@ __global__ __launch_bounds__(kThreads) void read_h_kernel(const _Float16* h, con
   const int col = (int)(q % I);
   long long pos = f < T ? inv_perm[f] : f;
   if (pos < 0 || pos >= R) pos = f;
-  out[q] = (float)h[pos * I + ((col & ~7) | inv_perm8(col & 7))];
+  const float v = (float)h[pos * I + ((col & ~7) | inv_perm8(col & 7))];
+  out[q] = (col & 1) ? v * 16.0f : v;  // odd columns are stored divided by 16
 }
 
 __global__ void init_ctrl_kernel(int* ctrl) {
-  if (threadIdx.x < kCtrlWords) ctrl[threadIdx.x] = 0;
+  if (threadIdx.x < kCtrlWords + kZeroWords) ctrl[threadIdx.x] = 0;
 }
 
 // ============================================================= host side
@@ -573,14 +808,14 @@ Layout make_layout(const qmoe_layer* L, int64_t M) {
   l.S = L->shared ? M : 0;
   l.R = l.T + l.S;
   l.C = ceil_div(M, kChunk);
-  l.max_items16 = max_items_for(l.T, M, l.S, E, 16);
+  l.max_items16 = max_items_for(l.T, M, l.S, E, 16);  // the smaller row tile bounds both
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
     off = align256(off + bytes);
     return o;
   };
-  l.ctrl = take(kCtrlWords * 4);
+  l.ctrl = take((kCtrlWords + kZeroWords) * 4);
   l.ids = take(l.T * 4);
   l.wts = take(l.T * 4);
   l.counts = take((E + 1) * 4);
@@ -638,7 +873,7 @@ int check_call(qmoe_layer* L, int64_t M, const void* ws, size_t ws_bytes, Layout
 }
 
 int init_workspace(qmoe_layer* L, void* ws, size_t ws_bytes, hipStream_t st) {
-  init_ctrl_kernel<<<1, 64, 0, st>>>(static_cast<int*>(ws));
+  init_ctrl_kernel<<<1, kCtrlWords + kZeroWords, 0, st>>>(static_cast<int*>(ws));
   L->inits++;
   const int rc = check_launch(L, "workspace init");
   if (rc != QMOE_OK) return rc;
@@ -663,7 +898,7 @@ int do_route(qmoe_layer* L, const void* x, const float* logits, int64_t M, void*
   if (!x || !logits) return fail(QMOE_ERR_ARG, x ? "logits is NULL" : "x is NULL");
   if (!aligned16(x)) return fail(QMOE_ERR_ARG, "x must be 16-byte aligned");
   const bool dec = use_decode_tiles(L, M);
-  const int bmc = dec ? 16 : 128;
+  const int bmc = dec ? 16 : kPrefillRows;
   RouteArgs a;
   a.logits = logits;
   a.x = static_cast<const uint4*>(x);
@@ -688,16 +923,16 @@ int do_route(qmoe_layer* L, const void* x, const float* logits, int64_t M, void*
   a.xa = at<uint4>(ws, lay.xa);
   const dim3 grid((unsigned)lay.C);
   const int epl = (L->d.E + 63) / 64;
-  if (epl <= 1) route_kernel<1><<<grid, kThreads, 0, st>>>(a);
-  else if (epl <= 2) route_kernel<2><<<grid, kThreads, 0, st>>>(a);
-  else if (epl <= 4) route_kernel<4><<<grid, kThreads, 0, st>>>(a);
-  else if (epl <= 8) route_kernel<8><<<grid, kThreads, 0, st>>>(a);
-  else route_kernel<16><<<grid, kThreads, 0, st>>>(a);
+  if (epl <= 1) route_kernel<1><<<grid, kRouteThreads, 0, st>>>(a);
+  else if (epl <= 2) route_kernel<2><<<grid, kRouteThreads, 0, st>>>(a);
+  else if (epl <= 4) route_kernel<4><<<grid, kRouteThreads, 0, st>>>(a);
+  else if (epl <= 8) route_kernel<8><<<grid, kRouteThreads, 0, st>>>(a);
+  else route_kernel<16><<<grid, kRouteThreads, 0, st>>>(a);
   L->route_calls++;
   return check_launch(L, "route_kernel");
 }
 
-template <int MB, int NBW, int WN, int WK, bool GATEUP>
+template <int MB, int NBW, int WN, int WK, int PF, bool GATEUP>
 int launch_gemm(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t st) {
   GemmArgs g;
   const int E = L->d.E, H = L->d.H, I = L->d.I;
@@ -719,6 +954,7 @@ int launch_gemm(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream
     g.N = I;
     g.Nw = 2 * I;
     g.a = at<_Float16>(ws, lay.xa);
+    g.a_bytes = (uint32_t)(M * H * 2);
     g.h_out = at<_Float16>(ws, lay.h);
     g.y_out = nullptr;
   } else {
@@ -730,6 +966,7 @@ int launch_gemm(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream
     g.N = H;
     g.Nw = H;
     g.a = at<_Float16>(ws, lay.h);
+    g.a_bytes = (uint32_t)(lay.R * I * 2);
     g.h_out = nullptr;
     g.y_out = at<float>(ws, lay.y);
   }
@@ -738,7 +975,7 @@ int launch_gemm(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream
   g.nblk = (int)ceil_div(g.N, WN * NBW * 16);
   const int64_t blocks = 8 * (int64_t)g.nblk * ceil_div(g.max_items, 8);
   if (blocks > 0x7FFFFFFF) return fail(QMOE_ERR_UNSUPPORTED, "grid too large");
-  gemm_kernel<MB, NBW, WN, WK, GATEUP><<<dim3((unsigned)blocks), kThreads, 0, st>>>(g);
+  gemm_kernel<MB, NBW, WN, WK, PF, GATEUP><<<dim3((unsigned)blocks), kThreads, 0, st>>>(g);
   L->gemm_launches++;
   return check_launch(L, GATEUP ? "gate_up gemm" : "down gemm");
 }
@@ -746,15 +983,18 @@ int launch_gemm(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream
 int do_gate_up(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t st) {
   if (use_decode_tiles(L, M)) {
     L->decode_tiles++;
-    return launch_gemm<1, 1, 1, 4, true>(L, M, ws, lay, st);
+    return launch_gemm<1, QMOE_DEC_GU_NBW, QMOE_DEC_GU_WN, 4 / QMOE_DEC_GU_WN, QMOE_DEC_GU_PF, true>(L, M, ws,
+                                                                                                  lay, st);
   }
   L->prefill_tiles++;
-  return launch_gemm<8, 2, 4, 1, true>(L, M, ws, lay, st);
+  return launch_gemm<QMOE_PRE_MB, QMOE_PRE_GU_NBW, 4, 1, 3, true>(L, M, ws, lay, st);
 }
 
 int do_down(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t st) {
-  if (use_decode_tiles(L, M)) return launch_gemm<1, 1, 4, 1, false>(L, M, ws, lay, st);
-  return launch_gemm<8, 4, 4, 1, false>(L, M, ws, lay, st);
+  if (use_decode_tiles(L, M))
+    return launch_gemm<1, QMOE_DEC_DN_NBW, QMOE_DEC_DN_WN, 4 / QMOE_DEC_DN_WN, QMOE_DEC_DN_PF, false>(L, M, ws,
+                                                                                                   lay, st);
+  return launch_gemm<QMOE_PRE_MB, QMOE_PRE_DN_NBW, 4, 1, 3, false>(L, M, ws, lay, st);
 }
 
 int do_combine(qmoe_layer* L, int64_t M, void* out, void* ws, const Layout& lay, hipStream_t st) {
@@ -781,14 +1021,18 @@ int qmoe_layer_create(const qmoe_layer_desc* d, qmoe_layer** out) {
   *out = nullptr;
   if (!d) return fail(QMOE_ERR_ARG, "desc is NULL");
   if (d->E < 1 || d->E > QMOE_MAX_EXPERTS) return fail(QMOE_ERR_ARG, "E must be in [1, 1024]");
-  if (d->H < 32 || d->H % 32) return fail(QMOE_ERR_ARG, "H must be a positive multiple of 32");
-  if (d->I < 32 || d->I % 32) return fail(QMOE_ERR_ARG, "I must be a positive multiple of 32");
+  // a multiple of 128 keeps every row's scale quads 8-byte aligned
+  if (d->H < 128 || d->H % 128) return fail(QMOE_ERR_ARG, "H must be a positive multiple of 128");
+  if (d->I < 128 || d->I % 128) return fail(QMOE_ERR_ARG, "I must be a positive multiple of 128");
   if (d->top_k < 1 || d->top_k > d->E || d->top_k > QMOE_MAX_TOPK)
     return fail(QMOE_ERR_ARG, "top_k must be in [1, min(E, 32)]");
   if (d->group_size != QMOE_GROUP) return fail(QMOE_ERR_ARG, "group_size must be 32");
   if (d->max_rows < 1) return fail(QMOE_ERR_ARG, "max_rows must be >= 1");
-  if ((int64_t)d->max_rows * d->top_k > (1LL << 30) || (int64_t)d->max_rows * d->H > (1LL << 40))
-    return fail(QMOE_ERR_ARG, "max_rows too large");
+  // activation buffers are addressed with 32-bit offsets
+  if ((int64_t)d->max_rows * d->H * 2 >= (1LL << 31) ||
+      (int64_t)d->max_rows * (d->top_k + 1) * d->I * 2 >= (1LL << 31))
+    return fail(QMOE_ERR_ARG, "max_rows too large for 32-bit activation offsets");
+  if ((int64_t)2 * d->I * d->H / 2 >= (1LL << 31)) return fail(QMOE_ERR_ARG, "expert too large");
   if (!d->w13) return fail(QMOE_ERR_ARG, "w13 is NULL");
   if (!d->s13) return fail(QMOE_ERR_ARG, "s13 is NULL");
   if (!d->w2) return fail(QMOE_ERR_ARG, "w2 is NULL");
@@ -824,7 +1068,7 @@ int qmoe_workspace_size(const qmoe_layer* L, int64_t M, size_t* bytes) {
 int qmoe_workspace_init(qmoe_layer* L, void* ws, size_t ws_bytes, void* stream) {
   if (!L) return fail(QMOE_ERR_ARG, "layer is NULL");
   if (!ws) return fail(QMOE_ERR_WORKSPACE, "workspace is NULL");
-  if (ws_bytes < kCtrlWords * 4) return fail(QMOE_ERR_WORKSPACE, "workspace too small");
+  if (ws_bytes < (kCtrlWords + kZeroWords) * 4) return fail(QMOE_ERR_WORKSPACE, "workspace too small");
   if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return fail(QMOE_ERR_WORKSPACE, "workspace not 256-byte aligned");
   return init_workspace(L, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }

@@ -2,10 +2,12 @@
 //
 // Operand format ("A-format"): activations that feed the MFMA contraction are
 // stored as fp16, and inside every run of 8 consecutive inputs the values are
-// kept in the order of input offsets {0,4,1,5,2,6,3,7}.  That is the order in
-// which dq8() below produces decoded weights from one 32-bit word of packed
-// codes, so an activation fragment and a weight fragment pair up element by
-// element without any shuffling in the inner loop.
+// kept in the order of input offsets {0,4,1,5,2,6,3,7}, with the values at
+// odd offsets divided by 16 (exact for normal fp16 values).  That matches
+// dq8() below, which produces decoded weights from one 32-bit word of packed
+// codes in that order and with the odd offsets multiplied by 16, so an
+// activation fragment and a weight fragment pair up element by element with
+// no shuffling and the products are unchanged.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -17,6 +19,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // Position p of an 8-run holds input offset perm8(p) (0,4,1,5,2,6,3,7);
 // input offset o sits at position inv_perm8(o) (0,2,4,6,1,3,5,7).
@@ -26,27 +29,47 @@ __host__ __device__ constexpr int inv_perm8(int o) { return ((o & 3) << 1) | (o 
 __device__ __forceinline__ half2_t as_half2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 __device__ __forceinline__ uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
 
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  // one VALU op; register operands (gfx9 VOP3 encodings take no literals)
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+  return r;
+}
+
 // Decode 8 packed int4 codes (nibble j of v = input offset j) with one fp16
 // group scale into 8 fp16 operands, in A-format order.
 //
-// Each nibble is OR-ed into the mantissa of the fp16 constant 1024.0 (whose
-// unit in the last place is 1), giving 1024+q exactly; subtracting 1032
-// leaves q-8 exactly; one packed multiply by the scale rounds (q-8)*s to
-// nearest even.  Two packed fp16 operations per pair of weights, plus the
-// mask/shift that extracts the nibbles.
-__device__ __forceinline__ half8_t dq8(uint32_t v, uint32_t scale_bits) {
-  const uint32_t kMask = 0x000F000Fu, kMagic = 0x64006400u;
-  const half2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  const half2_t s = as_half2(scale_bits | (scale_bits << 16));
-  half2_t p0 = (as_half2((v & kMask) | kMagic) + bias) * s;          // offsets 0, 4
-  half2_t p1 = (as_half2(((v >> 4) & kMask) | kMagic) + bias) * s;   // 1, 5
-  half2_t p2 = (as_half2(((v >> 8) & kMask) | kMagic) + bias) * s;   // 2, 6
-  half2_t p3 = (as_half2(((v >> 12) & kMask) | kMagic) + bias) * s;  // 3, 7
+// A nibble OR-ed into the mantissa of the fp16 constant 1024.0 gives 1024+q
+// exactly (bits 0-3) or 1024+16q exactly (bits 4-7, still inside the 10-bit
+// mantissa).  Subtracting 1032 (resp. 1152) leaves q-8 (resp. 16(q-8))
+// exactly, and one packed multiply by the scale rounds to nearest even.  The
+// odd input offsets thus carry 16*(q-8)*s, which the A-format compensates.
+// Per 8 codes: 1 shift, 4 and-or, 4 packed adds, 4 packed multiplies.
+// s2: the fp16 scale in both halves of a dword.
+__device__ __forceinline__ half8_t dq8p(uint32_t v, uint32_t s2) {
+  const uint32_t kLo = 0x000F000Fu, kHi = 0x00F000F0u, kMagic = 0x64006400u;
+  const half2_t b_lo = as_half2(0xE408E408u);  // (-1032, -1032)
+  const half2_t b_hi = as_half2(0xE480E480u);  // (-1152, -1152)
+  const half2_t s = as_half2(s2);
+  const uint32_t v8 = v >> 8;
+  const half2_t p0 = (as_half2(and_or(v, kLo, kMagic)) + b_lo) * s;   // offsets 0, 4
+  const half2_t p1 = (as_half2(and_or(v, kHi, kMagic)) + b_hi) * s;   // 1, 5 (x16)
+  const half2_t p2 = (as_half2(and_or(v8, kLo, kMagic)) + b_lo) * s;  // 2, 6
+  const half2_t p3 = (as_half2(and_or(v8, kHi, kMagic)) + b_hi) * s;  // 3, 7 (x16)
   half8_t r;
   r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
   return r;
 }
+
+// scale_bits: one fp16 scale in the low 16 bits.
+__device__ __forceinline__ half8_t dq8(uint32_t v, uint32_t scale_bits) {
+  return dq8p(v, (scale_bits & 0xFFFFu) | (scale_bits << 16));
+}
+
+// Position p of an 8-run carries a value scaled by 16 when its input offset
+// perm8(p) is odd, i.e. for p in {2, 3, 6, 7}.
+__host__ __device__ constexpr bool x16_pos(int p) { return (p & 2) != 0; }
 
 // bf16 pair (one 32-bit word, element 0 in the low half) -> two floats.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -60,13 +83,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 }
 
 // 8 bf16 (natural order) -> 8 fp16 in A-format order.  bf16 -> fp32 is
-// exact and fp32 -> fp16 is exact for values inside the fp16 range.
+// exact, the odd offsets are divided by 16 (exact), and fp32 -> fp16 is exact
+// for values inside the fp16 normal range.
 __device__ __forceinline__ uint4 bf16x8_to_aformat(uint4 in) {
   float f[8];
-  f[0] = bf16_lo(in.x); f[1] = bf16_hi(in.x);
-  f[2] = bf16_lo(in.y); f[3] = bf16_hi(in.y);
-  f[4] = bf16_lo(in.z); f[5] = bf16_hi(in.z);
-  f[6] = bf16_lo(in.w); f[7] = bf16_hi(in.w);
+  f[0] = bf16_lo(in.x); f[1] = bf16_hi(in.x) * 0.0625f;
+  f[2] = bf16_lo(in.y); f[3] = bf16_hi(in.y) * 0.0625f;
+  f[4] = bf16_lo(in.z); f[5] = bf16_hi(in.z) * 0.0625f;
+  f[6] = bf16_lo(in.w); f[7] = bf16_hi(in.w) * 0.0625f;
   half2_t o0 = {(_Float16)f[0], (_Float16)f[4]};
   half2_t o1 = {(_Float16)f[1], (_Float16)f[5]};
   half2_t o2 = {(_Float16)f[2], (_Float16)f[6]};
@@ -85,6 +109,33 @@ __device__ __forceinline__ uint32_t ordered_key(float f) {
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
   uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Maximum of a 64-bit value over the 64 lanes of a wave, returned to every
+// lane.  DPP steps (quad permutes, row mirrors, row broadcasts) combine
+// lanes within and across rows of 16 without going through LDS; lane 63
+// ends with the maximum, which readlane broadcasts.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ void dpp_max_step(uint32_t& lo, uint32_t& hi) {
+  const uint32_t plo = __builtin_amdgcn_update_dpp(lo, lo, kCtrl, kRowMask, 0xF, false);
+  const uint32_t phi = __builtin_amdgcn_update_dpp(hi, hi, kCtrl, kRowMask, 0xF, false);
+  const uint64_t p = ((uint64_t)phi << 32) | plo, c = ((uint64_t)hi << 32) | lo;
+  const uint64_t m = p > c ? p : c;
+  lo = (uint32_t)m;
+  hi = (uint32_t)(m >> 32);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  dpp_max_step<0xB1, 0xF>(lo, hi);   // quad_perm [1,0,3,2]
+  dpp_max_step<0x4E, 0xF>(lo, hi);   // quad_perm [2,3,0,1]
+  dpp_max_step<0x141, 0xF>(lo, hi);  // row_half_mirror
+  dpp_max_step<0x140, 0xF>(lo, hi);  // row_mirror
+  dpp_max_step<0x142, 0xA>(lo, hi);  // row_bcast:15 into rows 1, 3
+  dpp_max_step<0x143, 0xC>(lo, hi);  // row_bcast:31 into rows 2, 3
+  lo = __builtin_amdgcn_readlane(lo, 63);
+  hi = __builtin_amdgcn_readlane(hi, 63);
   return ((uint64_t)hi << 32) | lo;
 }
 

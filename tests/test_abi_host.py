@@ -55,7 +55,7 @@ def _desc(**kw):
 
 @pytest.mark.parametrize("field,value,needle", [
     ("E", 0, "E must"), ("E", 1025, "E must"), ("H", 33, "H must"), ("H", 0, "H must"),
-    ("I", 48, "I must"), ("top_k", 0, "top_k"), ("top_k", 9, "top_k"), ("group_size", 64, "group_size"),
+    ("H", 160, "H must"), ("I", 48, "I must"), ("I", 96, "I must"), ("top_k", 0, "top_k"), ("top_k", 9, "top_k"), ("group_size", 64, "group_size"),
     ("max_rows", 0, "max_rows"), ("w13", None, "w13"), ("s13", None, "s13"), ("w2", None, "w2"),
     ("s2", None, "s2"), ("shared_w13", 0x5000, "shared expert"), ("w13", 0x1001, "aligned"),
 ])

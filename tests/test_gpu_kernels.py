@@ -93,9 +93,9 @@ def _logits(kind, seed, M, E):
 @pytest.mark.parametrize("E,k,M,kind", ROUTE_CASES)
 def test_routing_bit_exact(E, k, M, kind):
     say(f"route E={E} k={k} M={M} {kind}")
-    shape = synth.LayerShape(E=E, H=32, I=32, top_k=k)
+    shape = synth.LayerShape(E=E, H=128, I=128, top_k=k)
     layer, _ = make_layer(shape, 1, M)
-    x = synth.hidden(2, M, 32)
+    x = synth.hidden(2, M, 128)
     lg = _logits(kind, 3, M, E)
     layer.route(dev_bf16(x), dev(lg))
     ref = oracle_moe.route(lg, k)
@@ -104,12 +104,12 @@ def test_routing_bit_exact(E, k, M, kind):
 
 def test_routing_repeatable_and_workspace_reuse():
     E, k = 384, 8
-    shape = synth.LayerShape(E=E, H=32, I=32, top_k=k)
+    shape = synth.LayerShape(E=E, H=128, I=128, top_k=k)
     layer, _ = make_layer(shape, 1, 4096)
     for M in (4096, 7, 1000, 7):  # shrinking and growing M on one workspace
         say(f"route reuse M={M}")
         lg = synth.logits(M, M, E)
-        layer.route(dev_bf16(synth.hidden(M, M, 32)), dev(lg))
+        layer.route(dev_bf16(synth.hidden(M, M, 128)), dev(lg))
         check_routing(layer, M, oracle_moe.route(lg, k), E)
 
 
@@ -119,13 +119,13 @@ FWD_CASES = [
     # E, H, I, k, M, shared   (decode tiles when M*k < 8E, else 128-row tiles)
     (8, 256, 128, 2, 16, False),     # the tiny configuration
     (8, 256, 128, 2, 1, False),
-    (16, 160, 96, 2, 37, False),     # ragged K (1.25 K-steps) and ragged N blocks, decode tiles
-    (64, 128, 64, 2, 9, True),       # decode tiles with a shared expert
-    (4, 160, 96, 2, 300, False),     # 128-row tiles, 2 row tiles per expert, ragged tails
+    (16, 640, 384, 2, 37, False),    # K = 1 super-step + a partial one / a partial one; decode tiles
+    (64, 128, 128, 2, 9, True),      # decode tiles with a shared expert
+    (4, 640, 384, 2, 300, False),    # 128-row tiles, 2 row tiles per expert, partial super-steps
     (4, 256, 128, 1, 200, True),     # 128-row tiles with a shared expert
     (4, 512, 256, 4, 20, False),     # top_k = E
-    (8, 1024, 512, 2, 64, False),    # several K-steps per wave in both GEMMs
-    (3, 96, 224, 2, 130, False),     # N not a multiple of the block width
+    (8, 2048, 1536, 2, 64, False),   # several super-steps per wave in both GEMMs
+    (3, 384, 1152, 2, 130, False),   # N not a multiple of the block width
 ]
 
 
@@ -182,7 +182,7 @@ def test_diagonal_weights_closed_form_on_gpu():
     """Top-1 with diagonal weights and power-of-two scales: the output is
     sd*su*x*SiLU(sg*x) on the first min(H, I) columns and 0 elsewhere."""
     import math
-    H, I, E, M = 128, 64, 3, 11
+    H, I, E, M = 256, 128, 3, 11
     codes13 = np.full((2 * I, H), 8, np.uint8)
     for i in range(I):
         codes13[i, i] = 9
@@ -211,7 +211,7 @@ def test_diagonal_weights_closed_form_on_gpu():
 
 
 def test_repeat_runs_bitwise_identical():
-    layer, w, x, lg, ref = _run_case(16, 160, 96, 2, 37, False)
+    layer, w, x, lg, ref = _run_case(16, 640, 384, 2, 37, False)
     xs, ls = dev_bf16(x), dev(lg)
     import torch
     a = layer.forward(xs, ls).clone()
