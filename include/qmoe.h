@@ -28,11 +28,18 @@
  * Activations x: bf16 [M, H]; router logits: fp32 [M, E]; out: bf16 [M, H].
  * All row-major and contiguous.
  *
- * Arithmetic: weights are decoded to fp16 operands ((c-8)*scale rounded to
- * nearest even in fp16) and x is converted exactly to fp16; products are
- * accumulated in fp32 by MFMA; h = SiLU(gate)*up is held in fp16, the
- * weighted per-slot results in fp32, and out is rounded to bf16 (nearest
- * even).  Hence |x| and |h| must stay below 65504 (the fp16 range).
+ * Arithmetic: x is converted to fp16 (exact for normal-range values) and h
+ * = SiLU(gate)*up is held in fp16, so |x| and |h| must stay below 65504.
+ * Which kernel a call uses depends on the average number of routed rows per
+ * expert, M*top_k/E:
+ *   <= 1      dot-product GEMV: sum of x*(c-8) per 32-input group in fp32
+ *             (exact integer codes), times the group's scale in fp32;
+ *   (1, 8)    16-row MFMA tiles, and
+ *   >= 8      128-row MFMA tiles: codes decoded to fp16 operands
+ *             ((c-8)*scale rounded to nearest even), products accumulated
+ *             in fp32 by MFMA.
+ * The weighted per-slot results are fp32 and out is rounded to bf16
+ * (nearest even).  Results are deterministic for a given M.
  *
  * Ownership: the caller owns every buffer.  The layer handle borrows the
  * weight pointers for its lifetime and copies nothing.  The library never
@@ -172,8 +179,9 @@ typedef struct {
   uint64_t workspace_inits;   /* explicit and automatic */
   uint64_t workspace_bytes_last;
   uint64_t workspace_bytes_peak;
-  uint64_t decode_tiles;      /* calls that used the 16-row tile shape */
-  uint64_t prefill_tiles;     /* calls that used the 128-row tile shape */
+  uint64_t decode_tiles;      /* gate+up launches on 16-row MFMA tiles */
+  uint64_t prefill_tiles;     /* gate+up launches on 128-row MFMA tiles */
+  uint64_t gemv_tiles;        /* gate+up launches on <= 2-row dot-product items */
 } qmoe_stats;
 
 int qmoe_get_stats(const qmoe_layer* layer, qmoe_stats* out);

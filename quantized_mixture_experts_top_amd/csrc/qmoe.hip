@@ -23,6 +23,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <type_traits>
 #include <utility>
 #include <vector>
 
@@ -700,6 +701,263 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   }
 }
 
+// -------------------------------------------------------- GEMV (1-2 rows)
+
+// Work items of at most kGemvRows routed rows, used when a call averages at
+// most one routed row per expert (small M).  There each expert's product is
+// a weight-streaming matrix-vector product, so it runs on packed fp16 dot
+// products (v_dot2_f32_f16) rather than 16-row MFMA tiles: on MI355X, MFMAs
+// fed from a full-rate weight stream hold back the stream's load issue,
+// while the dot-product form keeps it close to the read bandwidth.
+//
+// Same super-step weight mapping as gemm_kernel (lane group kq owns groups
+// 4kq..4kq+3 of each 512-input super-step, one per sub-step; one 8-byte
+// scale load per super-step).  A nibble OR-ed into fp16 1024.0 minus 1032
+// (minus 1152 for the odd inputs, whose nibble sits 4 bits up) is exactly
+// q-8 (16(q-8)); dot products with the operand-format activations (odd
+// inputs divided by 16) give the group's sum of x*(q-8) in fp32, which the
+// group's scale then multiplies.  The item's activation rows are staged in
+// LDS once per block, padded by 16 bytes every 256 so that the four lane
+// groups' reads fall in different banks.
+constexpr int kGemvRows = 2;
+
+__host__ __device__ constexpr int gemv_row_runs(int K) { return K / 8 + K / 128; }  // padded 16-byte runs
+
+#ifndef QMOE_GEMV_WPE
+#define QMOE_GEMV_WPE 3
+#endif
+template <int WN, int WK, bool GATEUP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QMOE_GEMV_WPE))) void gemv_kernel(
+    GemmArgs g) {
+  static_assert(WN * WK == 4, "4 waves per block");
+  constexpr int NBB = 2;                 // weight blocks of 16 rows per wave
+  constexpr int NBW = GATEUP ? 1 : 2;    // output column blocks per wave
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave % WN, wk = wave / WN;
+  const int r = lane & 15, kq = lane >> 4;
+
+  // all blocks of one item land on one XCD (block ids go round-robin over 8)
+  const int bid = blockIdx.x, xcd = bid & 7, jj = bid >> 3;
+  const int item = (jj / g.nblk) * 8 + xcd, nb = jj % g.nblk;
+  const int n_items = min(g.ctrl[1], g.max_items);
+  if (item >= n_items) return;
+  const int4 it = g.items[item];
+  const int e = it.x, nr = it.z, pos0 = it.w;
+  if (e < 0 || e > g.E || nr <= 0 || nr > kGemvRows || pos0 < 0 || pos0 > g.R - nr) return;
+  const uint32_t K2 = (uint32_t)g.K / 2, KG = (uint32_t)g.K / 32;
+  const uint8_t* wb;
+  const uint16_t* sbase;
+  if (e < g.E) {
+    wb = g.w + (size_t)e * g.Nw * K2;
+    sbase = g.s + (size_t)e * g.Nw * KG;
+  } else {
+    if (g.w_sh == nullptr) return;
+    wb = g.w_sh;
+    sbase = g.s_sh;
+  }
+  const __amdgpu_buffer_rsrc_t rB = buffer_rsrc(wb, (uint32_t)g.Nw * K2);
+  const __amdgpu_buffer_rsrc_t rS = buffer_rsrc(sbase, (uint32_t)g.Nw * KG * 2);
+  const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(g.a, g.a_bytes);
+
+  uint32_t boff[NBB], soff[NBB];
+  int col0[NBW];
+#pragma unroll
+  for (int c = 0; c < NBW; ++c) {
+    col0[c] = ((nb * WN + wn) * NBW + c) * 16;
+    const uint32_t n = col0[c] < g.N ? col0[c] + r : 0;
+    if (GATEUP) {  // gate row n and up row N + n
+      boff[0] = n * K2 + 64 * kq;
+      soff[0] = n * KG * 2 + 8 * kq;
+      boff[1] = (g.N + n) * K2 + 64 * kq;
+      soff[1] = (g.N + n) * KG * 2 + 8 * kq;
+    } else {
+      boff[c] = n * K2 + 64 * kq;
+      soff[c] = n * KG * 2 + 8 * kq;
+    }
+  }
+
+  const int nss_full = g.K / kSuper, nss = (g.K + kSuper - 1) / kSuper;
+  const int S_begin = wk * nss / WK, S_end = (wk + 1) * nss / WK;
+  const int S_end_full = min(S_end, nss_full);
+  const bool has_tail = S_end > nss_full;
+  const int ngroups = g.K / 32;
+  const int prow = gemv_row_runs(g.K);
+
+  // one super-step of this lane's weights: 4 sub-steps of codes and the
+  // 4 scales (as 2 dwords) per weight block
+  struct Super {
+    u32x4_t b[NBB][4];
+    uint32_t sc[NBB][2];
+  };
+  auto load_super = [&](int S, Super& f, bool ok) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int b = 0; b < NBB; ++b)
+        f.b[b][u] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rB, ok ? boff[b] + 16 * u : kOob, S * (kSuper / 2), 0));
+#pragma unroll
+    for (int b = 0; b < NBB; ++b) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rS, ok ? soff[b] : kOob, S * 32, 0);
+      f.sc[b][0] = v[0];
+      f.sc[b][1] = v[1];
+    }
+  };
+
+  // the first super-step's loads go out before the rows are staged
+  Super fa, fb;
+  if (S_end_full > S_begin) load_super(S_begin, fa, true);
+
+  // ---- stage the item's activation rows (operand format) in LDS
+  extern __shared__ __attribute__((aligned(16))) uint32_t gemv_lds[];
+  u32x4_t* lds_x = reinterpret_cast<u32x4_t*>(gemv_lds);
+  {
+    const int runs = g.K / 8;
+    for (int t = 0; t < nr; ++t) {
+      uint32_t off;
+      if (GATEUP) {
+        const int slot = g.perm[pos0 + t];
+        const int tok = slot < g.T ? slot / g.k : slot - g.T;
+        off = (slot >= 0 && slot < g.R && tok < g.M) ? (uint32_t)tok * (uint32_t)g.K * 2 : kOob;
+      } else {
+        off = (uint32_t)(pos0 + t) * (uint32_t)g.K * 2;
+      }
+      for (int q = tid; q < runs; q += kThreads)
+        lds_x[t * prow + q + (q >> 4)] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rA, off == kOob ? kOob : off + 16 * q, 0, 0));
+    }
+  }
+  __syncthreads();
+
+  float acc[NBB][kGemvRows];
+#pragma unroll
+  for (int b = 0; b < NBB; ++b)
+#pragma unroll
+    for (int t = 0; t < kGemvRows; ++t) acc[b][t] = 0.f;
+
+  // Super-step S from registers.  Lane group kq's group of sub-step u is
+  // 16S + 4kq + u.  A group past K (partial last super-step) has scale 0 and
+  // reads the row's last group from LDS, so it adds exactly zero.
+  auto compute_super = [&](int S, const Super& f, auto rows_tag) __attribute__((always_inline)) {
+    constexpr int NR = decltype(rows_tag)::value;
+    const half2_t b_lo = as_half2(0xE408E408u), b_hi = as_half2(0xE480E480u);  // -1032, -1152
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int xq = min(S * (kSuper / 8) + (4 * kq + u) * 4, g.K / 8 - 4);  // first 16-byte run
+      u32x4_t xv[NR][4];
+#pragma unroll
+      for (int t = 0; t < NR; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xv[t][i] = lds_x[t * prow + xq + (xq >> 4) + i];
+#pragma unroll
+      for (int b = 0; b < NBB; ++b) {
+        float p[NR];
+#pragma unroll
+        for (int t = 0; t < NR; ++t) p[t] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t q = word(f.b[b][u], i), q8 = q >> 8;
+          const half2_t w0 = as_half2(and_or(q, 0x000F000Fu, 0x64006400u)) + b_lo;   // inputs 0, 4
+          const half2_t w1 = as_half2(and_or(q, 0x00F000F0u, 0x64006400u)) + b_hi;   // 1, 5 (x16)
+          const half2_t w2 = as_half2(and_or(q8, 0x000F000Fu, 0x64006400u)) + b_lo;  // 2, 6
+          const half2_t w3 = as_half2(and_or(q8, 0x00F000F0u, 0x64006400u)) + b_hi;  // 3, 7 (x16)
+#pragma unroll
+          for (int t = 0; t < NR; ++t) {
+            p[t] = __builtin_amdgcn_fdot2(w0, as_half2(xv[t][i][0]), p[t], false);
+            p[t] = __builtin_amdgcn_fdot2(w1, as_half2(xv[t][i][1]), p[t], false);
+            p[t] = __builtin_amdgcn_fdot2(w2, as_half2(xv[t][i][2]), p[t], false);
+            p[t] = __builtin_amdgcn_fdot2(w3, as_half2(xv[t][i][3]), p[t], false);
+          }
+        }
+        const float sf = (float)as_half2(f.sc[b][u >> 1])[u & 1];
+#pragma unroll
+        for (int t = 0; t < NR; ++t) acc[b][t] += sf * p[t];
+      }
+    }
+  };
+
+  // Ping-pong over whole super-steps: the next one's loads are issued
+  // before the current one is computed (a scheduling fence keeps them
+  // there), so a wave always has one super-step in flight.  Loads past the
+  // wave's range are clamped to its last super-step (cache hits), which
+  // keeps the loop branch-free and the load counters exact.
+  auto run = [&](auto rows_tag) __attribute__((always_inline)) {
+    const int last = S_end_full - 1;
+    for (int S = S_begin; S <= last; S += 2) {
+      load_super(min(S + 1, last), fb, true);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_super(S, fa, rows_tag);
+      if (S + 1 > last) break;
+      load_super(min(S + 2, last), fa, true);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_super(S + 1, fb, rows_tag);
+    }
+    if (has_tail) {  // the partial super-step (groups come in whole quads)
+      const bool quad_ok = nss_full * 16 + 4 * kq < ngroups;
+      load_super(nss_full, fa, quad_ok);  // codes and scales of missing groups read 0
+      compute_super(nss_full, fa, rows_tag);
+    }
+  };
+  if (nr == 1) run(std::integral_constant<int, 1>{});
+  else run(std::integral_constant<int, 2>{});
+
+  // ---- reduce over the 4 lane groups (they hold different groups of a row)
+#pragma unroll
+  for (int b = 0; b < NBB; ++b)
+#pragma unroll
+    for (int t = 0; t < kGemvRows; ++t) {
+      acc[b][t] += __shfl_xor(acc[b][t], 16, 64);
+      acc[b][t] += __shfl_xor(acc[b][t], 32, 64);
+    }
+  // ---- then over the WK waves along K (fixed order: wave wk=0 adds 1, 2, 3)
+  if constexpr (WK > 1) {
+    float* red = reinterpret_cast<float*>(gemv_lds);  // the staged rows are dead by now
+    constexpr int kVals = NBB * kGemvRows;
+    __syncthreads();
+    if (wk > 0 && kq == 0) {
+#pragma unroll
+      for (int b = 0; b < NBB; ++b)
+#pragma unroll
+        for (int t = 0; t < kGemvRows; ++t)
+          red[(((wk - 1) * WN + wn) * kVals + b * kGemvRows + t) * 16 + r] = acc[b][t];
+    }
+    __syncthreads();
+    if (wk > 0) return;
+#pragma unroll
+    for (int w = 1; w < WK; ++w)
+#pragma unroll
+      for (int b = 0; b < NBB; ++b)
+#pragma unroll
+        for (int t = 0; t < kGemvRows; ++t) acc[b][t] += red[(((w - 1) * WN + wn) * kVals + b * kGemvRows + t) * 16 + r];
+  }
+  if (kq != 0) return;
+
+  // ---- epilogue: lane r holds weight row r of each block for the item's rows
+#pragma unroll
+  for (int t = 0; t < kGemvRows; ++t) {
+    if (t >= nr) continue;
+    const int pos = pos0 + t;
+    if (GATEUP) {
+      if (col0[0] >= g.N) continue;
+      const int col = col0[0] + r;
+      const float gt = acc[0][t], up = acc[1][t];
+      // odd columns are stored divided by 16 (operand format)
+      const float hv = gt / (1.0f + __expf(-gt)) * up * ((col & 1) ? 0.0625f : 1.0f);
+      g.h_out[(size_t)pos * g.N + ((col & ~7) | inv_perm8(col & 7))] = (_Float16)hv;
+    } else {
+      const int slot = g.perm[pos];
+      if (slot < 0 || slot >= g.R) continue;
+      const float wv = slot < g.T ? g.wts[slot] : 1.0f;
+#pragma unroll
+      for (int c = 0; c < NBW; ++c) {
+        if (col0[c] >= g.N) continue;
+        g.y_out[(size_t)slot * g.N + col0[c] + r] = wv * acc[c][t];
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- combine
 
 // out[t, n] = sum_{j<k} y[t*k + j, n] (in j order) + y[T + t, n] if shared,
@@ -777,7 +1035,7 @@ int fail(int code, const std::string& msg) {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  int64_t T, S, R, C, max_items16;
+  int64_t T, S, R, C, max_items_all;
   size_t ctrl, ids, wts, counts, offsets, cmask, pbase, perm, inv_perm, items, xa, h, y, total;
 };
 
@@ -794,7 +1052,7 @@ struct qmoe_layer {
   int device = 0;
   bool shared = false;
   std::atomic<uint64_t> forward_calls{0}, route_calls{0}, gemm_launches{0}, launches{0}, inits{0},
-      ws_last{0}, ws_peak{0}, decode_tiles{0}, prefill_tiles{0};
+      ws_last{0}, ws_peak{0}, decode_tiles{0}, prefill_tiles{0}, gemv_tiles{0};
   std::mutex mu;
   std::vector<std::pair<const void*, size_t>> inited;
 };
@@ -808,7 +1066,7 @@ Layout make_layout(const qmoe_layer* L, int64_t M) {
   l.S = L->shared ? M : 0;
   l.R = l.T + l.S;
   l.C = ceil_div(M, kChunk);
-  l.max_items16 = max_items_for(l.T, M, l.S, E, 16);  // the smaller row tile bounds both
+  l.max_items_all = max_items_for(l.T, M, l.S, E, kGemvRows);  // the smallest row tile bounds all
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -824,7 +1082,7 @@ Layout make_layout(const qmoe_layer* L, int64_t M) {
   l.pbase = take(l.C * E * 4);
   l.perm = take(l.R * 4);
   l.inv_perm = take(l.T * 4);
-  l.items = take(l.max_items16 * 16);
+  l.items = take(l.max_items_all * 16);
   l.xa = take(M * H * 2);
   l.h = take(l.R * I * 2);
   l.y = take(l.R * H * 4);
@@ -832,9 +1090,20 @@ Layout make_layout(const qmoe_layer* L, int64_t M) {
   return l;
 }
 
-bool use_decode_tiles(const qmoe_layer* L, int64_t M) {
-  return M * (int64_t)L->d.top_k < 8 * (int64_t)L->d.E;
+// Tile regime of a call, from the average routed rows per expert:
+// GEMV (<= 1 row on average; items of <= 2 rows on packed dot products),
+// 16-row MFMA tiles (< 8 rows), or 128-row MFMA tiles.  The GEMV stages two
+// activation rows in LDS, so it is used while they fit in 64 KiB.
+enum Regime { kGemv, kDecode, kPrefill };
+constexpr int kGemvMaxK = 15360;
+static_assert(kGemvRows * gemv_row_runs(kGemvMaxK) * 16 <= 65536, "GEMV rows fit in 64 KiB of LDS");
+Regime regime_of(const qmoe_layer* L, int64_t M) {
+  const int64_t T = M * (int64_t)L->d.top_k, E = L->d.E;
+  if (T <= E && L->d.H <= kGemvMaxK && L->d.I <= kGemvMaxK) return kGemv;
+  if (T < 8 * E) return kDecode;
+  return kPrefill;
 }
+int rows_per_item(Regime rg) { return rg == kGemv ? kGemvRows : rg == kDecode ? 16 : kPrefillRows; }
 
 template <typename T>
 T* at(void* ws, size_t off) {
@@ -897,8 +1166,7 @@ int do_route(qmoe_layer* L, const void* x, const float* logits, int64_t M, void*
              hipStream_t st) {
   if (!x || !logits) return fail(QMOE_ERR_ARG, x ? "logits is NULL" : "x is NULL");
   if (!aligned16(x)) return fail(QMOE_ERR_ARG, "x must be 16-byte aligned");
-  const bool dec = use_decode_tiles(L, M);
-  const int bmc = dec ? 16 : kPrefillRows;
+  const int bmc = rows_per_item(regime_of(L, M));
   RouteArgs a;
   a.logits = logits;
   a.x = static_cast<const uint4*>(x);
@@ -932,9 +1200,8 @@ int do_route(qmoe_layer* L, const void* x, const float* logits, int64_t M, void*
   return check_launch(L, "route_kernel");
 }
 
-template <int MB, int NBW, int WN, int WK, int PF, bool GATEUP>
-int launch_gemm(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t st) {
-  GemmArgs g;
+template <bool GATEUP>
+void fill_gemm_args(const qmoe_layer* L, int64_t M, void* ws, const Layout& lay, GemmArgs& g) {
   const int E = L->d.E, H = L->d.H, I = L->d.I;
   g.E = E;
   g.T = (int)lay.T;
@@ -970,6 +1237,13 @@ int launch_gemm(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream
     g.h_out = nullptr;
     g.y_out = at<float>(ws, lay.y);
   }
+}
+
+template <int MB, int NBW, int WN, int WK, int PF, bool GATEUP>
+int launch_gemm(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t st) {
+  GemmArgs g;
+  fill_gemm_args<GATEUP>(L, M, ws, lay, g);
+  const int E = L->d.E;
   const int bmc = MB * 16;
   g.max_items = (int)max_items_for(lay.T, M, lay.S, E, bmc);
   g.nblk = (int)ceil_div(g.N, WN * NBW * 16);
@@ -980,8 +1254,37 @@ int launch_gemm(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream
   return check_launch(L, GATEUP ? "gate_up gemm" : "down gemm");
 }
 
+#ifndef QMOE_GEMV_GU_WN
+#define QMOE_GEMV_GU_WN 2
+#endif
+#ifndef QMOE_GEMV_DN_WN
+#define QMOE_GEMV_DN_WN 4
+#endif
+
+template <int WN, bool GATEUP>
+int launch_gemv(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t st) {
+  constexpr int WK = 4 / WN;
+  GemmArgs g;
+  fill_gemm_args<GATEUP>(L, M, ws, lay, g);
+  g.max_items = (int)max_items_for(lay.T, M, lay.S, L->d.E, kGemvRows);
+  const int cols = GATEUP ? 16 : 32;  // output columns per wave
+  g.nblk = (int)ceil_div(g.N, WN * cols);
+  const int64_t blocks = 8 * (int64_t)g.nblk * ceil_div(g.max_items, 8);
+  if (blocks > 0x7FFFFFFF) return fail(QMOE_ERR_UNSUPPORTED, "grid too large");
+  const size_t lds = std::max<size_t>((size_t)kGemvRows * gemv_row_runs(g.K) * 16,
+                                      (size_t)(WK - 1) * WN * 2 * kGemvRows * 16 * 4);
+  gemv_kernel<WN, WK, GATEUP><<<dim3((unsigned)blocks), kThreads, lds, st>>>(g);
+  L->gemm_launches++;
+  return check_launch(L, GATEUP ? "gate_up gemv" : "down gemv");
+}
+
 int do_gate_up(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t st) {
-  if (use_decode_tiles(L, M)) {
+  const Regime rg = regime_of(L, M);
+  if (rg == kGemv) {
+    L->gemv_tiles++;
+    return launch_gemv<QMOE_GEMV_GU_WN, true>(L, M, ws, lay, st);
+  }
+  if (rg == kDecode) {
     L->decode_tiles++;
     return launch_gemm<1, QMOE_DEC_GU_NBW, QMOE_DEC_GU_WN, 4 / QMOE_DEC_GU_WN, QMOE_DEC_GU_PF, true>(L, M, ws,
                                                                                                   lay, st);
@@ -991,7 +1294,9 @@ int do_gate_up(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_
 }
 
 int do_down(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t st) {
-  if (use_decode_tiles(L, M))
+  const Regime rg = regime_of(L, M);
+  if (rg == kGemv) return launch_gemv<QMOE_GEMV_DN_WN, false>(L, M, ws, lay, st);
+  if (rg == kDecode)
     return launch_gemm<1, QMOE_DEC_DN_NBW, QMOE_DEC_DN_WN, 4 / QMOE_DEC_DN_WN, QMOE_DEC_DN_PF, false>(L, M, ws,
                                                                                                    lay, st);
   return launch_gemm<QMOE_PRE_MB, QMOE_PRE_DN_NBW, 4, 1, 3, false>(L, M, ws, lay, st);
@@ -1201,6 +1506,7 @@ int qmoe_get_stats(const qmoe_layer* L, qmoe_stats* s) {
   s->workspace_bytes_peak = L->ws_peak.load();
   s->decode_tiles = L->decode_tiles.load();
   s->prefill_tiles = L->prefill_tiles.load();
+  s->gemv_tiles = L->gemv_tiles.load();
   return QMOE_OK;
 }
 
@@ -1215,6 +1521,7 @@ int qmoe_reset_stats(qmoe_layer* L) {
   L->ws_peak = 0;
   L->decode_tiles = 0;
   L->prefill_tiles = 0;
+  L->gemv_tiles = 0;
   return QMOE_OK;
 }
 

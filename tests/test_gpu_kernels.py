@@ -116,7 +116,8 @@ def test_routing_repeatable_and_workspace_reuse():
 # ------------------------------------------------------------ whole layer
 
 FWD_CASES = [
-    # E, H, I, k, M, shared   (decode tiles when M*k < 8E, else 128-row tiles)
+    # E, H, I, k, M, shared   (dot-product items of <= 2 rows when M*k <= E,
+    #                          16-row tiles when M*k < 8E, else 128-row tiles)
     (8, 256, 128, 2, 16, False),     # the tiny configuration
     (8, 256, 128, 2, 1, False),
     (16, 640, 384, 2, 37, False),    # K = 1 super-step + a partial one / a partial one; decode tiles
@@ -126,6 +127,9 @@ FWD_CASES = [
     (4, 512, 256, 4, 20, False),     # top_k = E
     (8, 2048, 1536, 2, 64, False),   # several super-steps per wave in both GEMMs
     (3, 384, 1152, 2, 130, False),   # N not a multiple of the block width
+    (64, 1152, 640, 2, 20, False),   # dot-product items: whole + partial super-steps in both GEMMs
+    (32, 2048, 1536, 4, 8, True),    # dot-product items, 2-row items, shared expert, split K
+    (16, 256, 128, 8, 2, False),     # dot-product items, top_k = 8, partial super-steps only
 ]
 
 
@@ -149,7 +153,8 @@ def test_forward_parity(E, H, I, k, M, shared):
     assert err <= REL_TOL
 
 
-@pytest.mark.parametrize("E,H,I,k,M,shared", [FWD_CASES[2], FWD_CASES[4], FWD_CASES[5]])
+@pytest.mark.parametrize("E,H,I,k,M,shared", [FWD_CASES[2], FWD_CASES[4], FWD_CASES[5], FWD_CASES[9],
+                                               FWD_CASES[10]])
 def test_steps_match_oracle_intermediates(E, H, I, k, M, shared):
     """h = SiLU(gate)*up after the gate+up step and w*y after the down step,
     per routed slot, against the oracle's float64 values."""
@@ -178,11 +183,12 @@ def test_steps_match_oracle_intermediates(E, H, I, k, M, shared):
     assert rel_err(out, ref["out"]) <= REL_TOL
 
 
-def test_diagonal_weights_closed_form_on_gpu():
+@pytest.mark.parametrize("M", [11, 2])  # 16-row tiles, dot-product items
+def test_diagonal_weights_closed_form_on_gpu(M):
     """Top-1 with diagonal weights and power-of-two scales: the output is
     sd*su*x*SiLU(sg*x) on the first min(H, I) columns and 0 elsewhere."""
     import math
-    H, I, E, M = 256, 128, 3, 11
+    H, I, E = 256, 128, 3
     codes13 = np.full((2 * I, H), 8, np.uint8)
     for i in range(I):
         codes13[i, i] = 9
@@ -210,8 +216,9 @@ def test_diagonal_weights_closed_form_on_gpu():
     assert rel_err(out, expect) <= REL_TOL
 
 
-def test_repeat_runs_bitwise_identical():
-    layer, w, x, lg, ref = _run_case(16, 640, 384, 2, 37, False)
+@pytest.mark.parametrize("case", [(16, 640, 384, 2, 37, False), (32, 2048, 1536, 4, 8, True)])
+def test_repeat_runs_bitwise_identical(case):
+    layer, w, x, lg, ref = _run_case(*case)
     xs, ls = dev_bf16(x), dev(lg)
     import torch
     a = layer.forward(xs, ls).clone()
@@ -241,7 +248,7 @@ def test_counters_and_workspace_accounting():
     assert s["gemm_launches"] == 2 and s["launches"] == 4
     assert s["workspace_inits"] == 0
     assert s["workspace_bytes_last"] == s["workspace_bytes_peak"] == layer.workspace_bytes(16) > 0
-    assert s["decode_tiles"] + s["prefill_tiles"] == 1
+    assert s["decode_tiles"] + s["prefill_tiles"] + s["gemv_tiles"] == 1
 
 
 def test_errors_from_the_library():
