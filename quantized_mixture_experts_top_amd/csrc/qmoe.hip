@@ -710,18 +710,41 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 // fed from a full-rate weight stream hold back the stream's load issue,
 // while the dot-product form keeps it close to the read bandwidth.
 //
-// Same super-step weight mapping as gemm_kernel (lane group kq owns groups
-// 4kq..4kq+3 of each 512-input super-step, one per sub-step; one 8-byte
-// scale load per super-step).  A nibble OR-ed into fp16 1024.0 minus 1032
-// (minus 1152 for the odd inputs, whose nibble sits 4 bits up) is exactly
-// q-8 (16(q-8)); dot products with the operand-format activations (odd
-// inputs divided by 16) give the group's sum of x*(q-8) in fp32, which the
-// group's scale then multiplies.  The item's activation rows are staged in
-// LDS once per block, padded by 16 bytes every 256 so that the four lane
-// groups' reads fall in different banks.
+// Lane (r, kq) of a wave owns weight row r of each 16-row block.  K is
+// walked in super-steps of 512 inputs (a 256-byte chunk of each row); in
+// sub-step u the four lanes of a row read its 64 contiguous bytes 64u..64u+63,
+// lane kq taking group 4u + kq.  Lane kq loads the row's scale quad kq (8
+// bytes, groups 4kq..4kq+3) and two cross-row lane swaps transpose the four
+// quads so that lane kq holds the scales of groups kq, 4+kq, 8+kq, 12+kq.
+//
+// Arithmetic: a nibble q OR-ed into fp16 1024.0 is 1024+q exactly; minus
+// 1032 it is q-8 (for the odd inputs, whose nibble sits 4 bits up: 1024+16q
+// minus 1152 = 16(q-8), and their activations are stored divided by 16).
+// Dot products with the activations give the group's sum of x*(q-8) in
+// fp32 (exact products); the group's scale multiplies it in fp32.  A zero
+// weight (code 8) contributes exactly zero.
+//
+// The item's activation rows are staged in LDS once per block.
 constexpr int kGemvRows = 2;
 
-__host__ __device__ constexpr int gemv_row_runs(int K) { return K / 8 + K / 128; }  // padded 16-byte runs
+// LDS bytes of a block: the activation rows
+__host__ __device__ constexpr size_t gemv_lds_bytes(int K) { return (size_t)kGemvRows * K * 2; }
+
+// lane swaps between the 16-lane rows of a wave: (rows of a, rows of b)
+// become (a0 b0 a2 b2, a1 b1 a3 b3) for 16 and (a0 a1 b0 b1, a2 a3 b2 b3)
+// for 32
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  const auto v = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                                                  false, false);
+  a = __builtin_bit_cast(float, (uint32_t)v[0]);
+  b = __builtin_bit_cast(float, (uint32_t)v[1]);
+}
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  const auto v = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                                                  false, false);
+  a = __builtin_bit_cast(float, (uint32_t)v[0]);
+  b = __builtin_bit_cast(float, (uint32_t)v[1]);
+}
 
 #ifndef QMOE_GEMV_WPE
 #define QMOE_GEMV_WPE 3
@@ -737,9 +760,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QMOE_G
   const int wn = wave % WN, wk = wave / WN;
   const int r = lane & 15, kq = lane >> 4;
 
-  // all blocks of one item land on one XCD (block ids go round-robin over 8)
-  const int bid = blockIdx.x, xcd = bid & 7, jj = bid >> 3;
-  const int item = (jj / g.nblk) * 8 + xcd, nb = jj % g.nblk;
+  // consecutive blocks take consecutive column blocks of one item, so each
+  // item's stream is spread over all XCDs
+  const int item = blockIdx.x / g.nblk, nb = blockIdx.x % g.nblk;
   const int n_items = min(g.ctrl[1], g.max_items);
   if (item >= n_items) return;
   const int4 it = g.items[item];
@@ -767,12 +790,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QMOE_G
     col0[c] = ((nb * WN + wn) * NBW + c) * 16;
     const uint32_t n = col0[c] < g.N ? col0[c] + r : 0;
     if (GATEUP) {  // gate row n and up row N + n
-      boff[0] = n * K2 + 64 * kq;
+      boff[0] = n * K2 + 16 * kq;
       soff[0] = n * KG * 2 + 8 * kq;
-      boff[1] = (g.N + n) * K2 + 64 * kq;
+      boff[1] = (g.N + n) * K2 + 16 * kq;
       soff[1] = (g.N + n) * KG * 2 + 8 * kq;
     } else {
-      boff[c] = n * K2 + 64 * kq;
+      boff[c] = n * K2 + 16 * kq;
       soff[c] = n * KG * 2 + 8 * kq;
     }
   }
@@ -782,24 +805,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QMOE_G
   const int S_end_full = min(S_end, nss_full);
   const bool has_tail = S_end > nss_full;
   const int ngroups = g.K / 32;
-  const int prow = gemv_row_runs(g.K);
 
   // one super-step of this lane's weights: 4 sub-steps of codes and the
-  // 4 scales (as 2 dwords) per weight block
+  // scale quad (2 dwords) per weight block
   struct Super {
     u32x4_t b[NBB][4];
     uint32_t sc[NBB][2];
   };
-  auto load_super = [&](int S, Super& f, bool ok) __attribute__((always_inline)) {
+  // sub_ok: sub-step u's groups exist (uniform); quad_ok: this lane's quad
+  auto load_super = [&](int S, Super& f, int n_sub, bool quad_ok) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int b = 0; b < NBB; ++b)
         f.b[b][u] = __builtin_bit_cast(
-            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rB, ok ? boff[b] + 16 * u : kOob, S * (kSuper / 2), 0));
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rB, u < n_sub ? boff[b] + 64 * u : kOob, S * (kSuper / 2), 0));
 #pragma unroll
     for (int b = 0; b < NBB; ++b) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rS, ok ? soff[b] : kOob, S * 32, 0);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rS, quad_ok ? soff[b] : kOob, S * 32, 0);
       f.sc[b][0] = v[0];
       f.sc[b][1] = v[1];
     }
@@ -807,26 +830,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QMOE_G
 
   // the first super-step's loads go out before the rows are staged
   Super fa, fb;
-  if (S_end_full > S_begin) load_super(S_begin, fa, true);
+  if (S_end_full > S_begin) load_super(S_begin, fa, 4, true);
 
   // ---- stage the item's activation rows (operand format) in LDS
   extern __shared__ __attribute__((aligned(16))) uint32_t gemv_lds[];
   u32x4_t* lds_x = reinterpret_cast<u32x4_t*>(gemv_lds);
-  {
-    const int runs = g.K / 8;
-    for (int t = 0; t < nr; ++t) {
-      uint32_t off;
-      if (GATEUP) {
-        const int slot = g.perm[pos0 + t];
-        const int tok = slot < g.T ? slot / g.k : slot - g.T;
-        off = (slot >= 0 && slot < g.R && tok < g.M) ? (uint32_t)tok * (uint32_t)g.K * 2 : kOob;
-      } else {
-        off = (uint32_t)(pos0 + t) * (uint32_t)g.K * 2;
-      }
-      for (int q = tid; q < runs; q += kThreads)
-        lds_x[t * prow + q + (q >> 4)] = __builtin_bit_cast(
-            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rA, off == kOob ? kOob : off + 16 * q, 0, 0));
+  const int runs = g.K / 8;
+  for (int t = 0; t < nr; ++t) {
+    uint32_t off;
+    if (GATEUP) {
+      const int slot = g.perm[pos0 + t];
+      const int tok = slot < g.T ? slot / g.k : slot - g.T;
+      off = (slot >= 0 && slot < g.R && tok < g.M) ? (uint32_t)tok * (uint32_t)g.K * 2 : kOob;
+    } else {
+      off = (uint32_t)(pos0 + t) * (uint32_t)g.K * 2;
     }
+    for (int q = tid; q < runs; q += kThreads)
+      lds_x[t * runs + q] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rA, off == kOob ? kOob : off + 16 * q, 0, 0));
   }
   __syncthreads();
 
@@ -836,20 +857,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QMOE_G
 #pragma unroll
     for (int t = 0; t < kGemvRows; ++t) acc[b][t] = 0.f;
 
-  // Super-step S from registers.  Lane group kq's group of sub-step u is
-  // 16S + 4kq + u.  A group past K (partial last super-step) has scale 0 and
-  // reads the row's last group from LDS, so it adds exactly zero.
+  // Super-step S from registers.  A group past K (partial last super-step)
+  // has scale 0 and reads the row's last group, so it adds exactly zero.
   auto compute_super = [&](int S, const Super& f, auto rows_tag) __attribute__((always_inline)) {
     constexpr int NR = decltype(rows_tag)::value;
     const half2_t b_lo = as_half2(0xE408E408u), b_hi = as_half2(0xE480E480u);  // -1032, -1152
+    // scales: lane kq holds quad kq; transpose so that sc[b][u] = group 4u+kq
+    float sc[NBB][4];
+#pragma unroll
+    for (int b = 0; b < NBB; ++b) {
+      const half2_t lo = as_half2(f.sc[b][0]), hi = as_half2(f.sc[b][1]);
+      float q0 = (float)lo[0], q1 = (float)lo[1], q2 = (float)hi[0], q3 = (float)hi[1];
+      swap16(q0, q1);
+      swap16(q2, q3);
+      swap32(q0, q2);
+      swap32(q1, q3);
+      sc[b][0] = q0;
+      sc[b][1] = q1;
+      sc[b][2] = q2;
+      sc[b][3] = q3;
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int xq = min(S * (kSuper / 8) + (4 * kq + u) * 4, g.K / 8 - 4);  // first 16-byte run
+      const int xq = min((S * 16 + 4 * u + kq) * 4, runs - 4);  // first 16-byte run of the group
       u32x4_t xv[NR][4];
 #pragma unroll
       for (int t = 0; t < NR; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xv[t][i] = lds_x[t * prow + xq + (xq >> 4) + i];
+        for (int i = 0; i < 4; ++i) xv[t][i] = lds_x[t * runs + xq + i];
 #pragma unroll
       for (int b = 0; b < NBB; ++b) {
         float p[NR];
@@ -870,32 +905,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QMOE_G
             p[t] = __builtin_amdgcn_fdot2(w3, as_half2(xv[t][i][3]), p[t], false);
           }
         }
-        const float sf = (float)as_half2(f.sc[b][u >> 1])[u & 1];
 #pragma unroll
-        for (int t = 0; t < NR; ++t) acc[b][t] += sf * p[t];
+        for (int t = 0; t < NR; ++t) acc[b][t] += sc[b][u] * p[t];
       }
     }
   };
 
   // Ping-pong over whole super-steps: the next one's loads are issued
   // before the current one is computed (a scheduling fence keeps them
-  // there), so a wave always has one super-step in flight.  Loads past the
-  // wave's range are clamped to its last super-step (cache hits), which
-  // keeps the loop branch-free and the load counters exact.
+  // there), so a wave always has one super-step in flight.  The loop runs
+  // while two remain and the last one or two are peeled, so every load is
+  // used and the load counters stay exact.
   auto run = [&](auto rows_tag) __attribute__((always_inline)) {
     const int last = S_end_full - 1;
-    for (int S = S_begin; S <= last; S += 2) {
-      load_super(min(S + 1, last), fb, true);
+    int S = S_begin;
+    for (; S + 2 <= last; S += 2) {
+      load_super(S + 1, fb, 4, true);
       __builtin_amdgcn_sched_barrier(0);
       compute_super(S, fa, rows_tag);
-      if (S + 1 > last) break;
-      load_super(min(S + 2, last), fa, true);
+      load_super(S + 2, fa, 4, true);
       __builtin_amdgcn_sched_barrier(0);
       compute_super(S + 1, fb, rows_tag);
     }
-    if (has_tail) {  // the partial super-step (groups come in whole quads)
-      const bool quad_ok = nss_full * 16 + 4 * kq < ngroups;
-      load_super(nss_full, fa, quad_ok);  // codes and scales of missing groups read 0
+    if (S + 1 == last) {
+      load_super(S + 1, fb, 4, true);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_super(S, fa, rows_tag);
+      compute_super(S + 1, fb, rows_tag);
+    } else if (S == last) {
+      compute_super(S, fa, rows_tag);
+    }
+    if (has_tail) {  // the partial super-step: whole quads of groups remain
+      const int n_sub = (ngroups - nss_full * 16) / 4;
+      load_super(nss_full, fa, n_sub, kq < n_sub);
       compute_super(nss_full, fa, rows_tag);
     }
   };
@@ -1096,7 +1138,7 @@ Layout make_layout(const qmoe_layer* L, int64_t M) {
 // activation rows in LDS, so it is used while they fit in 64 KiB.
 enum Regime { kGemv, kDecode, kPrefill };
 constexpr int kGemvMaxK = 15360;
-static_assert(kGemvRows * gemv_row_runs(kGemvMaxK) * 16 <= 65536, "GEMV rows fit in 64 KiB of LDS");
+static_assert(gemv_lds_bytes(kGemvMaxK) <= 65536, "GEMV rows fit in 64 KiB of LDS");
 Regime regime_of(const qmoe_layer* L, int64_t M) {
   const int64_t T = M * (int64_t)L->d.top_k, E = L->d.E;
   if (T <= E && L->d.H <= kGemvMaxK && L->d.I <= kGemvMaxK) return kGemv;
@@ -1255,7 +1297,7 @@ int launch_gemm(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream
 }
 
 #ifndef QMOE_GEMV_GU_WN
-#define QMOE_GEMV_GU_WN 2
+#define QMOE_GEMV_GU_WN 4
 #endif
 #ifndef QMOE_GEMV_DN_WN
 #define QMOE_GEMV_DN_WN 4
@@ -1269,10 +1311,9 @@ int launch_gemv(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream
   g.max_items = (int)max_items_for(lay.T, M, lay.S, L->d.E, kGemvRows);
   const int cols = GATEUP ? 16 : 32;  // output columns per wave
   g.nblk = (int)ceil_div(g.N, WN * cols);
-  const int64_t blocks = 8 * (int64_t)g.nblk * ceil_div(g.max_items, 8);
+  const int64_t blocks = (int64_t)g.nblk * g.max_items;
   if (blocks > 0x7FFFFFFF) return fail(QMOE_ERR_UNSUPPORTED, "grid too large");
-  const size_t lds = std::max<size_t>((size_t)kGemvRows * gemv_row_runs(g.K) * 16,
-                                      (size_t)(WK - 1) * WN * 2 * kGemvRows * 16 * 4);
+  const size_t lds = std::max<size_t>(gemv_lds_bytes(g.K), (size_t)(WK - 1) * WN * 2 * kGemvRows * 16 * 4);
   gemv_kernel<WN, WK, GATEUP><<<dim3((unsigned)blocks), kThreads, lds, st>>>(g);
   L->gemm_launches++;
   return check_launch(L, GATEUP ? "gate_up gemv" : "down gemv");
