@@ -130,6 +130,49 @@ __device__ void block_exclusive_scan(const int* in, int* out, int n, int* wsum) 
   __syncthreads();
 }
 
+// Counts, offsets, work items and positions from the per-expert token masks
+// of a chunk, all in LDS: used when the whole call is one chunk (M <= 64).
+// Shared by the multi-chunk path's tail: the items and the scan are built
+// the same way there from counts gathered over chunks.
+__device__ void route_items(const RouteArgs& a, int* s_cnt, int* s_off, int* s_ni, int* s_ioff, int* s_wsum) {
+  const int tid = threadIdx.x, E = a.E;
+  if (tid == 0) s_cnt[E] = a.S;  // the shared expert takes every token
+  __syncthreads();
+  for (int e = tid; e <= E; e += kRouteThreads) s_ni[e] = (s_cnt[e] + a.bmc - 1) / a.bmc;
+  __syncthreads();
+  block_exclusive_scan(s_cnt, s_off, E + 1, s_wsum);
+  block_exclusive_scan(s_ni, s_ioff, E + 1, s_wsum);
+  for (int e = tid; e <= E; e += kRouteThreads) a.counts[e] = s_cnt[e];
+  for (int e = tid; e <= E + 1; e += kRouteThreads) a.offsets[e] = s_off[e];
+  for (int e = tid; e <= E; e += kRouteThreads) {
+    const int base = s_ioff[e], n = s_cnt[e];
+    for (int i = 0; i < s_ni[e]; ++i) {
+      const int r0 = i * a.bmc;
+      if (base + i < a.max_items) a.items[base + i] = make_int4(e, r0, min(a.bmc, n - r0), s_off[e] + r0);
+    }
+  }
+  if (tid == 0) a.ctrl[1] = min(s_ioff[E + 1], a.max_items);
+}
+
+__device__ void route_finish_single(const RouteArgs& a, const uint32_t (*cm)[2], const int* s_ids, int* s_cnt,
+                                    int* s_off, int* s_ni, int* s_ioff, int* s_wsum) {
+  const int tid = threadIdx.x, E = a.E, k = a.k;
+  for (int e = tid; e < E; e += kRouteThreads) s_cnt[e] = __popc(cm[e][0]) + __popc(cm[e][1]);
+  route_items(a, s_cnt, s_off, s_ni, s_ioff, s_wsum);
+  __syncthreads();
+  // slot (t, j): its expert's offset plus the number of lower tokens routed
+  // to that expert (each token selects an expert at most once)
+  for (int f = tid; f < a.M * k; f += kRouteThreads) {
+    const int t = f / k, e = s_ids[f];
+    const unsigned long long m = (unsigned long long)cm[e][0] | ((unsigned long long)cm[e][1] << 32);
+    const int pos = s_off[e] + __popcll(m & ((1ull << t) - 1ull));
+    a.perm[pos] = f;
+    a.inv_perm[f] = pos;
+  }
+  const int T = a.M * k;
+  for (int t = tid; t < a.S; t += kRouteThreads) a.perm[T + t] = T + t;
+}
+
 // One block per chunk of 64 tokens; the last block to finish (atomic ticket,
 // no waiting) turns the per-chunk token masks into counts, offsets,
 // positions and work items.  EPL = logits per lane (E <= 64 * EPL).
@@ -142,11 +185,22 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   __shared__ int s_ioff[QMOE_MAX_EXPERTS + 2];
   __shared__ int s_wsum[kRouteWaves];
   __shared__ int s_last;
+  __shared__ int s_ids[kChunk * QMOE_MAX_TOPK];  // the chunk's selected experts
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = blockIdx.x, E = a.E, k = a.k;
   const int rows = min(kChunk, a.M - c * kChunk);
 
   for (int e = tid; e < E; e += kRouteThreads) cm[e][0] = cm[e][1] = 0u;
+
+  // x rows of the chunk, as 16-byte runs; the first kXPre runs of each
+  // thread are loaded before the top-k so their latency overlaps it
+  constexpr int kXPre = 8;
+  const long long xn = (long long)rows * (a.H / 8);
+  const uint4* xs = a.x + (size_t)c * kChunk * (a.H / 8);
+  uint4* xd = a.xa + (size_t)c * kChunk * (a.H / 8);
+  uint4 xpre[kXPre];
+#pragma unroll
+  for (int u = 0; u < kXPre; ++u) xpre[u] = xs[min(tid + (long long)u * kRouteThreads, xn - 1)];  // clamped
   __syncthreads();
 
   // ---- phase 1a: top-k of each token, one wave per token
@@ -155,13 +209,19 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     const float* row = a.logits + (size_t)t * E;
     // key = (order-preserving logit bits, ~expert): the maximum key is the
     // largest logit, ties to the lowest expert index.  Absent experts = 0.
+    // (loads clamped into the row rather than predicated, so they all
+    // issue before the first wait)
+    float lv[EPL];
+#pragma unroll
+    for (int s = 0; s < EPL; ++s) lv[s] = row[min(s * 64 + lane, E - 1)];
     uint64_t key[EPL];
 #pragma unroll
     for (int s = 0; s < EPL; ++s) {
       const int e = s * 64 + lane;
-      key[s] = (e < E) ? (((uint64_t)ordered_key(row[e]) << 32) | (uint32_t)(~e)) : 0ull;
+      key[s] = (e < E) ? (((uint64_t)ordered_key(lv[s]) << 32) | (uint32_t)(~e)) : 0ull;
     }
     int my_e = 0;
+    float my_l = 0.0f;
     for (int j = 0; j < k; ++j) {
       uint64_t best = 0;
 #pragma unroll
@@ -171,11 +231,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
 #pragma unroll
       for (int s = 0; s < EPL; ++s)
         if (s * 64 + lane == e_sel) key[s] = 0;
-      if (lane == j) my_e = e_sel;
+      if (lane == j) {
+        my_e = e_sel;
+        my_l = from_ordered_key((uint32_t)(best >> 32));
+      }
     }
     // renormalised softmax over the selected logits: the full-softmax
     // denominator cancels, so w_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0)
-    const float lj = (lane < k) ? row[my_e] : 0.0f;
+    const float lj = (lane < k) ? my_l : 0.0f;
     const float l0 = __shfl(lj, 0, 64);
     const float ex = (lane < k) ? expf(lj - l0) : 0.0f;
     float sum = ex;
@@ -183,6 +246,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
     if (lane < k) {
       a.ids[(size_t)t * k + lane] = my_e;
+      s_ids[tl * k + lane] = my_e;
       a.wts[(size_t)t * k + lane] = ex / sum;
       atomicOr(&cm[my_e][tl >> 5], 1u << (tl & 31));
     }
@@ -190,16 +254,16 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
 
   // ---- phase 1b: the chunk's x rows -> fp16 operand format (contiguous)
   {
-    const long long n = (long long)rows * (a.H / 8);
-    const uint4* xs = a.x + (size_t)c * kChunk * (a.H / 8);
-    uint4* xd = a.xa + (size_t)c * kChunk * (a.H / 8);
-    for (long long q0 = tid; q0 < n; q0 += 4 * kRouteThreads) {
+#pragma unroll
+    for (int u = 0; u < kXPre; ++u) {
+      const long long q = tid + (long long)u * kRouteThreads;
+      if (q < xn) xd[q] = bf16x8_to_aformat(xpre[u]);
+    }
+    const long long n = xn;
+    for (long long q0 = tid + (long long)kXPre * kRouteThreads; q0 < n; q0 += 4 * kRouteThreads) {
       uint4 v[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const long long q = q0 + u * kRouteThreads;
-        v[u] = q < n ? xs[q] : make_uint4(0u, 0u, 0u, 0u);
-      }
+      for (int u = 0; u < 4; ++u) v[u] = xs[min(q0 + u * kRouteThreads, n - 1)];  // clamped
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const long long q = q0 + u * kRouteThreads;
@@ -208,6 +272,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     }
   }
   __syncthreads();
+  if (a.C == 1) {
+    route_finish_single(a, cm, s_ids, s_cnt, s_off, s_ni, s_ioff, s_wsum);
+    return;
+  }
   for (int e = tid; e < E; e += kRouteThreads)
     a.cmask[(size_t)c * E + e] = (unsigned long long)cm[e][0] | ((unsigned long long)cm[e][1] << 32);
   if (a.C > 1) {
@@ -249,23 +317,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
       s_cnt[e] = run;
     }
   }
-  if (tid == 0) s_cnt[E] = a.S;  // the shared expert takes every token
-  __syncthreads();
-  for (int e = tid; e <= E; e += kRouteThreads) s_ni[e] = (s_cnt[e] + a.bmc - 1) / a.bmc;
-  __syncthreads();
-  block_exclusive_scan(s_cnt, s_off, E + 1, s_wsum);
-  block_exclusive_scan(s_ni, s_ioff, E + 1, s_wsum);
-  for (int e = tid; e <= E; e += kRouteThreads) a.counts[e] = s_cnt[e];
-  for (int e = tid; e <= E + 1; e += kRouteThreads) a.offsets[e] = s_off[e];
-  for (int e = tid; e <= E; e += kRouteThreads) {
-    const int base = s_ioff[e], n = s_cnt[e];
-    for (int i = 0; i < s_ni[e]; ++i) {
-      const int r0 = i * a.bmc;
-      if (base + i < a.max_items) a.items[base + i] = make_int4(e, r0, min(a.bmc, n - r0), s_off[e] + r0);
-    }
-  }
-  if (tid == 0) a.ctrl[1] = min(s_ioff[E + 1], a.max_items);
-  if (a.C > 1) __threadfence();
+  route_items(a, s_cnt, s_off, s_ni, s_ioff, s_wsum);
+  __threadfence();
   __syncthreads();
   // sorted position of every routed slot: expert offset + rank of the
   // token's chunk + rank inside the chunk (popcount of the lower mask bits)
@@ -1003,31 +1056,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QMOE_G
 // ---------------------------------------------------------------- combine
 
 // out[t, n] = sum_{j<k} y[t*k + j, n] (in j order) + y[T + t, n] if shared,
-// rounded to bf16.  One thread per 8 consecutive columns.
-__global__ __launch_bounds__(kThreads) void combine_kernel(const float* y, uint4* out, int M, int H,
+// rounded to bf16.  One thread per 4 consecutive columns; the k slots are
+// loaded in batches of 8 before they are summed, so a thread waits for one
+// round trip per batch rather than one per slot.
+__global__ __launch_bounds__(kThreads) void combine_kernel(const float* y, uint2* out, int M, int H,
                                                             int k, int T, int S) {
   const long long q = (long long)blockIdx.x * kThreads + threadIdx.x;
-  const int per_row = H / 8;
+  const int per_row = H / 4;
   if (q >= (long long)M * per_row) return;
-  const int t = (int)(q / per_row), c8 = (int)(q % per_row);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const float4* p = reinterpret_cast<const float4*>(y + ((size_t)t * k + j) * H + (size_t)c8 * 8);
-    const float4 u = p[0], v = p[1];
-    acc[0] += u.x; acc[1] += u.y; acc[2] += u.z; acc[3] += u.w;
-    acc[4] += v.x; acc[5] += v.y; acc[6] += v.z; acc[7] += v.w;
+  const int t = (int)(q / per_row), c4 = (int)(q % per_row);
+  const float4* base = reinterpret_cast<const float4*>(y) + (size_t)c4;
+  const size_t row4 = (size_t)H / 4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int n = k + (S ? 1 : 0);  // slot rows to add, the shared expert last
+  for (int j0 = 0; j0 < n; j0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u;
+      const size_t r = j < k ? (size_t)t * k + j : (size_t)T + t;
+      v[u] = j < n ? base[r * row4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (j0 + u < n) {
+        acc.x += v[u].x;
+        acc.y += v[u].y;
+        acc.z += v[u].z;
+        acc.w += v[u].w;
+      }
+    }
   }
-  if (S) {
-    const float4* p = reinterpret_cast<const float4*>(y + ((size_t)T + t) * H + (size_t)c8 * 8);
-    const float4 u = p[0], v = p[1];
-    acc[0] += u.x; acc[1] += u.y; acc[2] += u.z; acc[3] += u.w;
-    acc[4] += v.x; acc[5] += v.y; acc[6] += v.z; acc[7] += v.w;
-  }
-  uint4 o;
-  o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-  o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
-  o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
-  o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
+  uint2 o;
+  o.x = f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16);
+  o.y = f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16);
   out[q] = o;
 }
 
@@ -1346,9 +1408,9 @@ int do_down(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t s
 int do_combine(qmoe_layer* L, int64_t M, void* out, void* ws, const Layout& lay, hipStream_t st) {
   if (!out) return fail(QMOE_ERR_ARG, "out is NULL");
   if (!aligned16(out)) return fail(QMOE_ERR_ARG, "out must be 16-byte aligned");
-  const int64_t n = M * (L->d.H / 8);
+  const int64_t n = M * (L->d.H / 4);
   combine_kernel<<<dim3((unsigned)ceil_div(n, kThreads)), kThreads, 0, st>>>(
-      at<float>(ws, lay.y), static_cast<uint4*>(out), (int)M, L->d.H, L->d.top_k, (int)lay.T, (int)lay.S);
+      at<float>(ws, lay.y), static_cast<uint2*>(out), (int)M, L->d.H, L->d.top_k, (int)lay.T, (int)lay.S);
   return check_launch(L, "combine_kernel");
 }
 

@@ -106,6 +106,11 @@ __device__ __forceinline__ uint32_t ordered_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inverse of ordered_key (a -0 input comes back as +0).
+__device__ __forceinline__ float from_ordered_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
   uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
