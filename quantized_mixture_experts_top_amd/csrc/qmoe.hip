@@ -779,6 +779,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 //
 // The item's activation rows are staged in LDS once per block.
 constexpr int kGemvRows = 2;
+constexpr int kGemvMaxRowsPerExpert = 4;  // GEMV while M*top_k <= 4E
 
 // LDS bytes of a block: the activation rows
 __host__ __device__ constexpr size_t gemv_lds_bytes(int K) { return (size_t)kGemvRows * K * 2; }
@@ -1195,15 +1196,19 @@ Layout make_layout(const qmoe_layer* L, int64_t M) {
 }
 
 // Tile regime of a call, from the average routed rows per expert:
-// GEMV (<= 1 row on average; items of <= 2 rows on packed dot products),
-// 16-row MFMA tiles (< 8 rows), or 128-row MFMA tiles.  The GEMV stages two
-// activation rows in LDS, so it is used while they fit in 64 KiB.
+// GEMV (items of <= 2 rows on packed dot products) up to 4 rows on average,
+// 16-row MFMA tiles below 8, 128-row MFMA tiles above.  An expert with more
+// than 2 rows takes several GEMV items, each streaming its weights; measured
+// on MI355X (E=384, H=7168, I=2048, top-8) that still beats the 16-row
+// tiles up to about 4 rows per expert (M=192), and loses beyond (M=256).
+// The GEMV stages two activation rows in LDS, so it is used while they fit
+// in 64 KiB.
 enum Regime { kGemv, kDecode, kPrefill };
 constexpr int kGemvMaxK = 15360;
 static_assert(gemv_lds_bytes(kGemvMaxK) <= 65536, "GEMV rows fit in 64 KiB of LDS");
 Regime regime_of(const qmoe_layer* L, int64_t M) {
   const int64_t T = M * (int64_t)L->d.top_k, E = L->d.E;
-  if (T <= E && L->d.H <= kGemvMaxK && L->d.I <= kGemvMaxK) return kGemv;
+  if (T <= kGemvMaxRowsPerExpert * E && L->d.H <= kGemvMaxK && L->d.I <= kGemvMaxK) return kGemv;
   if (T < 8 * E) return kDecode;
   return kPrefill;
 }

@@ -116,7 +116,7 @@ def test_routing_repeatable_and_workspace_reuse():
 # ------------------------------------------------------------ whole layer
 
 FWD_CASES = [
-    # E, H, I, k, M, shared   (dot-product items of <= 2 rows when M*k <= E,
+    # E, H, I, k, M, shared   (dot-product items of <= 2 rows when M*k <= 4E,
     #                          16-row tiles when M*k < 8E, else 128-row tiles)
     (8, 256, 128, 2, 16, False),     # the tiny configuration
     (8, 256, 128, 2, 1, False),
@@ -130,6 +130,9 @@ FWD_CASES = [
     (64, 1152, 640, 2, 20, False),   # dot-product items: whole + partial super-steps in both GEMMs
     (32, 2048, 1536, 4, 8, True),    # dot-product items, 2-row items, shared expert, split K
     (16, 256, 128, 8, 2, False),     # dot-product items, top_k = 8, partial super-steps only
+    (8, 512, 256, 2, 12, True),      # dot-product items, experts with several items, shared expert
+    (8, 256, 128, 2, 24, False),     # 16-row tiles on the tiny shape
+    (16, 640, 384, 2, 40, True),     # 16-row tiles with a shared expert, partial super-steps
 ]
 
 
@@ -154,7 +157,7 @@ def test_forward_parity(E, H, I, k, M, shared):
 
 
 @pytest.mark.parametrize("E,H,I,k,M,shared", [FWD_CASES[2], FWD_CASES[4], FWD_CASES[5], FWD_CASES[9],
-                                               FWD_CASES[10]])
+                                               FWD_CASES[10], FWD_CASES[12], FWD_CASES[14]])
 def test_steps_match_oracle_intermediates(E, H, I, k, M, shared):
     """h = SiLU(gate)*up after the gate+up step and w*y after the down step,
     per routed slot, against the oracle's float64 values."""
@@ -183,7 +186,7 @@ def test_steps_match_oracle_intermediates(E, H, I, k, M, shared):
     assert rel_err(out, ref["out"]) <= REL_TOL
 
 
-@pytest.mark.parametrize("M", [11, 2])  # 16-row tiles, dot-product items
+@pytest.mark.parametrize("M", [20, 2])  # 16-row tiles, dot-product items
 def test_diagonal_weights_closed_form_on_gpu(M):
     """Top-1 with diagonal weights and power-of-two scales: the output is
     sd*su*x*SiLU(sg*x) on the first min(H, I) columns and 0 elsewhere."""
