@@ -603,7 +603,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     // ---------------- prefill tiles: the activation tile of each sub-step
     // (MB*16 rows x 128 inputs, in MFMA k order) staged in LDS
     static_assert(WK == 1, "128-row tiles split N across waves, not K");
-    __shared__ __attribute__((aligned(16))) _Float16 lds_a[MB * 16 * kAStride];
+    __shared__ __attribute__((aligned(16))) _Float16 lds_a[2][MB * 16 * kAStride];  // double-buffered
     __shared__ uint32_t lds_row[MB * 16];
     for (int m = tid; m < MB * 16; m += kThreads) lds_row[m] = m < nr ? a_off_of(m) : kOob;
     __syncthreads();
@@ -628,12 +628,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
         u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rA, (OK) ? aoffs[i] + 64 * (U) : kOob,      \
                                                        (S) * (kSuper * 2), 0));                    \
   } while (0)
-#define QMOE_STORE_A_TILE()                                                                        \
+#define QMOE_STORE_A_TILE(BUF)                                                                     \
   do {                                                                                             \
     _Pragma("unroll") for (int i = 0; i < kRowsPerThread; ++i)                                     \
-        *reinterpret_cast<u32x4_t*>(&lds_a[(row_base + 16 * i) * kAStride + seg * 8]) = st[i];    \
+        *reinterpret_cast<u32x4_t*>(&lds_a[(BUF)][(row_base + 16 * i) * kAStride + seg * 8]) = st[i]; \
   } while (0)
-#define QMOE_COMPUTE(F, SC, U)                                                                     \
+#define QMOE_COMPUTE(F, SC, U, BUF)                                                                \
   do {                                                                                             \
     uint32_t s2_[NBB];                                                                             \
     _Pragma("unroll") for (int b = 0; b < NBB; ++b) s2_[b] = scale_pair((SC)[b][0], (SC)[b][1], (U)); \
@@ -643,35 +643,39 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
       _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                                          \
         if (mb < nmb) {                                                                            \
           const half8_t av =                                                                       \
-              *reinterpret_cast<const half8_t*>(&lds_a[(mb * 16 + r) * kAStride + 32 * kq + 8 * i]); \
+              *reinterpret_cast<const half8_t*>(&lds_a[(BUF)][(mb * 16 + r) * kAStride + 32 * kq + 8 * i]); \
           _Pragma("unroll") for (int b = 0; b < NBB; ++b) acc[mb][b] = mfma16x16x32(av, bf[b], acc[mb][b]); \
         }                                                                                          \
       }                                                                                            \
     }                                                                                              \
   } while (0)
-    // one sub-step: publish the staged tile, prefetch the next sub-step
-    // (clamped, unconditional), then compute
-#define QMOE_SUBSTEP(S, U, FCUR, FNEXT, SN, UN)                                                    \
+    // One sub-step with one barrier: prefetch the next sub-step's weights
+    // and activation tile (clamped, unconditional), compute this sub-step
+    // from LDS buffer BUF, then write the next tile (loaded during the
+    // compute) to the other buffer and meet the barrier that publishes it
+    // and frees BUF for the tile after next.
+#define QMOE_SUBSTEP(S, U, FCUR, FNEXT, SN, UN, BUF)                                               \
   do {                                                                                             \
-    __syncthreads();                                                                               \
-    QMOE_STORE_A_TILE();                                                                           \
-    __syncthreads();                                                                               \
     load_b((SN), (UN), FNEXT, true);                                                               \
     QMOE_LOAD_A_TILE((SN), (UN), true);                                                            \
-    QMOE_COMPUTE(FCUR, sc_cur, (U));                                                               \
+    QMOE_COMPUTE(FCUR, sc_cur, (U), (BUF));                                                        \
+    QMOE_STORE_A_TILE((BUF) ^ 1);                                                                  \
+    __syncthreads();                                                                               \
   } while (0)
     const int n = S_end_full - S_begin;
     if (n > 0) {
       load_sc(S_begin, sc_cur, true);
       load_b(S_begin, 0, fb0, true);
       QMOE_LOAD_A_TILE(S_begin, 0, true);
+      QMOE_STORE_A_TILE(0);
+      __syncthreads();
       for (int S = S_begin; S < S_end_full; ++S) {
         const int Sn = min(S + 1, S_end_full - 1);
         load_sc(Sn, sc_nxt, true);
-        QMOE_SUBSTEP(S, 0, fb0, fb1, S, 1);
-        QMOE_SUBSTEP(S, 1, fb1, fb0, S, 2);
-        QMOE_SUBSTEP(S, 2, fb0, fb1, S, 3);
-        QMOE_SUBSTEP(S, 3, fb1, fb0, Sn, 0);
+        QMOE_SUBSTEP(S, 0, fb0, fb1, S, 1, 0);
+        QMOE_SUBSTEP(S, 1, fb1, fb0, S, 2, 1);
+        QMOE_SUBSTEP(S, 2, fb0, fb1, S, 3, 0);
+        QMOE_SUBSTEP(S, 3, fb1, fb0, Sn, 0, 1);
 #pragma unroll
         for (int b = 0; b < NBB; ++b) {
           sc_cur[b][0] = sc_nxt[b][0];
@@ -688,9 +692,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
         load_b(nss_full, u, fb0, okb);
         QMOE_LOAD_A_TILE(nss_full, u, oka);
         __syncthreads();
-        QMOE_STORE_A_TILE();
+        QMOE_STORE_A_TILE(0);
         __syncthreads();
-        QMOE_COMPUTE(fb0, sc_cur, u);
+        QMOE_COMPUTE(fb0, sc_cur, u, 0);
       }
     }
 #undef QMOE_SUBSTEP
