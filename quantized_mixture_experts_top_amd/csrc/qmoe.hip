@@ -641,7 +641,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
       half8_t bf[NBB];                                                                             \
       _Pragma("unroll") for (int b = 0; b < NBB; ++b) bf[b] = dq8p(word((F).b[b], i), s2_[b]);     \
       _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                                          \
-        if (mb < nmb) {                                                                            \
+        if (mb < NMBC) {                                                                           \
           const half8_t av =                                                                       \
               *reinterpret_cast<const half8_t*>(&lds_a[(BUF)][(mb * 16 + r) * kAStride + 32 * kq + 8 * i]); \
           _Pragma("unroll") for (int b = 0; b < NBB; ++b) acc[mb][b] = mfma16x16x32(av, bf[b], acc[mb][b]); \
@@ -662,41 +662,52 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     QMOE_STORE_A_TILE((BUF) ^ 1);                                                                  \
     __syncthreads();                                                                               \
   } while (0)
-    const int n = S_end_full - S_begin;
-    if (n > 0) {
-      load_sc(S_begin, sc_cur, true);
-      load_b(S_begin, 0, fb0, true);
-      QMOE_LOAD_A_TILE(S_begin, 0, true);
-      QMOE_STORE_A_TILE(0);
-      __syncthreads();
-      for (int S = S_begin; S < S_end_full; ++S) {
-        const int Sn = min(S + 1, S_end_full - 1);
-        load_sc(Sn, sc_nxt, true);
-        QMOE_SUBSTEP(S, 0, fb0, fb1, S, 1, 0);
-        QMOE_SUBSTEP(S, 1, fb1, fb0, S, 2, 1);
-        QMOE_SUBSTEP(S, 2, fb0, fb1, S, 3, 0);
-        QMOE_SUBSTEP(S, 3, fb1, fb0, Sn, 0, 1);
-#pragma unroll
-        for (int b = 0; b < NBB; ++b) {
-          sc_cur[b][0] = sc_nxt[b][0];
-          sc_cur[b][1] = sc_nxt[b][1];
-        }
-      }
-    }
-    if (has_tail) {  // the partial super-step: groups past K read zeros
-      load_sc(nss_full, sc_cur, true);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bool okb = nss_full * 16 + 4 * kq + u < ngroups;
-        const bool oka = nss_full * 16 + 4 * sq + u < ngroups;
-        load_b(nss_full, u, fb0, okb);
-        QMOE_LOAD_A_TILE(nss_full, u, oka);
-        __syncthreads();
+    // The row blocks that hold routed rows are computed without a branch per
+    // block: the loop is instantiated for 2, 4, 6 and 8 blocks and the
+    // item's count rounds up to the next of these (blocks past the item's
+    // rows multiply zero rows, which are never stored).
+    auto kloop = [&](auto nmbc_tag) __attribute__((always_inline)) {
+      constexpr int NMBC = decltype(nmbc_tag)::value;
+      const int n = S_end_full - S_begin;
+      if (n > 0) {
+        load_sc(S_begin, sc_cur, true);
+        load_b(S_begin, 0, fb0, true);
+        QMOE_LOAD_A_TILE(S_begin, 0, true);
         QMOE_STORE_A_TILE(0);
         __syncthreads();
-        QMOE_COMPUTE(fb0, sc_cur, u, 0);
+        for (int S = S_begin; S < S_end_full; ++S) {
+          const int Sn = min(S + 1, S_end_full - 1);
+          load_sc(Sn, sc_nxt, true);
+          QMOE_SUBSTEP(S, 0, fb0, fb1, S, 1, 0);
+          QMOE_SUBSTEP(S, 1, fb1, fb0, S, 2, 1);
+          QMOE_SUBSTEP(S, 2, fb0, fb1, S, 3, 0);
+          QMOE_SUBSTEP(S, 3, fb1, fb0, Sn, 0, 1);
+  #pragma unroll
+          for (int b = 0; b < NBB; ++b) {
+            sc_cur[b][0] = sc_nxt[b][0];
+            sc_cur[b][1] = sc_nxt[b][1];
+          }
+        }
       }
-    }
+      if (has_tail) {  // the partial super-step: groups past K read zeros
+        load_sc(nss_full, sc_cur, true);
+  #pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bool okb = nss_full * 16 + 4 * kq + u < ngroups;
+          const bool oka = nss_full * 16 + 4 * sq + u < ngroups;
+          load_b(nss_full, u, fb0, okb);
+          QMOE_LOAD_A_TILE(nss_full, u, oka);
+          __syncthreads();
+          QMOE_STORE_A_TILE(0);
+          __syncthreads();
+          QMOE_COMPUTE(fb0, sc_cur, u, 0);
+        }
+      }
+    };
+    if (nmb <= 2) kloop(std::integral_constant<int, (MB < 2 ? MB : 2)>{});
+    else if (nmb <= 4) kloop(std::integral_constant<int, (MB < 4 ? MB : 4)>{});
+    else if (nmb <= 6) kloop(std::integral_constant<int, (MB < 6 ? MB : 6)>{});
+    else kloop(std::integral_constant<int, MB>{});
 #undef QMOE_SUBSTEP
 #undef QMOE_COMPUTE
 #undef QMOE_STORE_A_TILE
