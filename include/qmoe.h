@@ -35,8 +35,7 @@
  *   <= 4      dot-product GEMV on items of <= 2 rows: sum of x*(c-8) per
  *             32-input group in fp32 (exact integer codes), times the
  *             group's scale in fp32;
- *   (4, 8)    16-row MFMA tiles, and
- *   >= 8      128-row MFMA tiles: codes decoded to fp16 operands
+ *   > 4       128-row MFMA tiles: codes decoded to fp16 operands
  *             ((c-8)*scale rounded to nearest even), products accumulated
  *             in fp32 by MFMA.
  * The weighted per-slot results are fp32 and out is rounded to bf16
@@ -110,7 +109,12 @@ typedef struct qmoe_layer qmoe_layer;
 /* Validate the description and create a handle (host memory only).  Fails
    with QMOE_ERR_ARG on a bad field (the message names it), then with
    QMOE_ERR_DEVICE if no HIP device can be queried and QMOE_ERR_UNSUPPORTED
-   if the current device is not gfx950. */
+   if the current device is not gfx950.
+   The environment variable QMOE_SPLIT_K (1, 2 or 4; default 1), read here,
+   splits K of the dot-product GEMV over that many of a block's 4 waves
+   (partial sums reduced through LDS in a fixed order); any other value is
+   QMOE_ERR_ARG.  It changes the speed and the fp32 summation order, not the
+   result's tolerance. */
 int qmoe_layer_create(const qmoe_layer_desc* desc, qmoe_layer** out);
 void qmoe_layer_destroy(qmoe_layer* layer);
 
@@ -180,7 +184,6 @@ typedef struct {
   uint64_t workspace_inits;   /* explicit and automatic */
   uint64_t workspace_bytes_last;
   uint64_t workspace_bytes_peak;
-  uint64_t decode_tiles;      /* gate+up launches on 16-row MFMA tiles */
   uint64_t prefill_tiles;     /* gate+up launches on 128-row MFMA tiles */
   uint64_t gemv_tiles;        /* gate+up launches on <= 2-row dot-product items */
 } qmoe_stats;

@@ -41,7 +41,7 @@ class LayerDesc(ctypes.Structure):
 class Stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "forward_calls", "route_calls", "gemm_launches", "launches", "workspace_inits",
-        "workspace_bytes_last", "workspace_bytes_peak", "decode_tiles", "prefill_tiles", "gemv_tiles")]
+        "workspace_bytes_last", "workspace_bytes_peak", "prefill_tiles", "gemv_tiles")]
 
     def as_dict(self) -> dict:
         return {n: int(getattr(self, n)) for n, _ in self._fields_}

@@ -20,6 +20,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -43,24 +44,6 @@ constexpr int kKStep = 128;     // inputs per K-step of a wave (4 lane groups x 
 // Tile shapes (compile-time; one of the two shapes is picked per call from
 // M*top_k vs E).  NBW = 16-column output blocks per wave, WN x WK = waves of
 // a block along N and K, PF = K-steps of loads in flight beyond the current.
-#ifndef QMOE_DEC_GU_NBW
-#define QMOE_DEC_GU_NBW 1
-#endif
-#ifndef QMOE_DEC_GU_WN
-#define QMOE_DEC_GU_WN 2
-#endif
-#ifndef QMOE_DEC_GU_PF
-#define QMOE_DEC_GU_PF 3
-#endif
-#ifndef QMOE_DEC_DN_NBW
-#define QMOE_DEC_DN_NBW 1
-#endif
-#ifndef QMOE_DEC_DN_WN
-#define QMOE_DEC_DN_WN 4
-#endif
-#ifndef QMOE_DEC_DN_PF
-#define QMOE_DEC_DN_PF 3
-#endif
 #ifndef QMOE_PRE_MB
 #define QMOE_PRE_MB 8
 #endif
@@ -403,9 +386,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 constexpr uint32_t kOob = 0x7FFFFF00u;  // a lane offset past any buffer: its loads read 0
 constexpr int kSuper = 4 * kKStep;     // inputs per super-step (16 groups)
 
-// One work item = (expert, up to MB*16 routed rows) x (an N range).  A block
-// has 4 waves: WN waves along N (each NBW blocks of 16 output columns) times
-// WK waves along K (partial sums reduced through LDS in a fixed order).
+// 128-row tiles.  One work item = (expert, up to MB*16 routed rows) x (an N
+// range).  A block has 4 waves along N, each NBW blocks of 16 output
+// columns (gate+up: each with its up block).
 //
 // K is walked in super-steps of 512 inputs (16 groups of 32).  Lane group kq
 // (= lane/16) owns groups 4kq..4kq+3 of each super-step and decodes one per
@@ -414,14 +397,13 @@ constexpr int kSuper = 4 * kKStep;     // inputs per super-step (16 groups)
 // all four scales coming from one 8-byte load per super-step.  The MFMA
 // k-slot order is free as long as the activations follow it, so the
 // activation fragment of sub-step u, MFMA i is inputs (4kq+u)*32 + 8i .. +8.
-// MB == 1: activations are read straight from global memory (decode, few
-// rows); MB > 1: the block stages each sub-step's activation tile in LDS.
+// The block stages each sub-step's activation tile in LDS.
 // Loads are buffer loads with a fixed per-lane offset and a scalar
 // per-step offset (no vector address arithmetic); inputs past K read zeros.
-template <int MB, int NBW, int WN, int WK, int PF, bool GATEUP>
+template <int MB, int NBW, bool GATEUP>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
-  static_assert(WN * WK == 4, "4 waves per block");
-  static_assert(PF == 3, "the sub-step ring holds one super-step");
+  constexpr int WN = 4, WK = 1;
+  static_assert(MB > 1, "row tiles of at least 32 rows");
   constexpr int NBB = GATEUP ? 2 * NBW : NBW;
   const int tid = threadIdx.x, lane = tid & 63;
   // wave index as a wave-uniform (scalar) value, so loop bounds derived
@@ -524,60 +506,88 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     return (uint32_t)pos * (uint32_t)g.K * 2;
   };
 
-  if constexpr (MB == 1) {
-    // ---------------- decode tiles: activations straight from global memory,
-    // a ring of 4 sub-steps (one super-step) of loads in flight per wave.
-    // Rows past nr read a real row (their MFMA rows are never stored).
-    const uint32_t arow = a_off_of(min(r, nr - 1));
-    const uint32_t aoff = arow == kOob ? kOob : arow + 256 * kq;
-    Frag<NBB> fb[4];   // weight ring: 3 sub-steps ahead (HBM latency)
-    u32x4_t fa[2][4];  // activation ring: 1 sub-step ahead (L2-resident rows)
-    uint32_t sc_cur[NBB][2], sc_nxt[NBB][2];
-    auto load_a = [&](int S, int u, u32x4_t (&q)[4], bool ok) __attribute__((always_inline)) {
+  // ---------------- prefill tiles: the activation tile of each sub-step
+  // (MB*16 rows x 128 inputs, in MFMA k order) staged in LDS
+  static_assert(WK == 1, "128-row tiles split N across waves, not K");
+  __shared__ __attribute__((aligned(16))) _Float16 lds_a[2][MB * 16 * kAStride];  // double-buffered
+  __shared__ uint32_t lds_row[MB * 16];
+  for (int m = tid; m < MB * 16; m += kThreads) lds_row[m] = m < nr ? a_off_of(m) : kOob;
+  __syncthreads();
+  // thread -> 16-byte segment seg of rows (tid/16) + 16*i of the tile;
+  // tile column 32*q + 8*v (q = seg/4, v = seg%4) holds inputs
+  // (4q+u)*32 + 8v .. +8 of the super-step
+  const int seg = tid & 15, row_base = tid >> 4;
+  const int sq = seg >> 2, sv = seg & 3;
+  constexpr int kRowsPerThread = MB;  // MB*16 rows / 16 row groups
+  uint32_t aoffs[kRowsPerThread];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        q[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                               rA, ok ? aoff + 64 * u + 16 * i : kOob, S * (kSuper * 2), 0));
-    };
-    auto compute = [&](const Frag<NBB>& fbu, const u32x4_t (&fau)[4], const uint32_t (&sc)[NBB][2], int u)
-                       __attribute__((always_inline)) {
-      uint32_t s2[NBB];
-#pragma unroll
-      for (int b = 0; b < NBB; ++b) s2[b] = scale_pair(sc[b][0], sc[b][1], u);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const half8_t av = __builtin_bit_cast(half8_t, fau[i]);
-#pragma unroll
-        for (int b = 0; b < NBB; ++b) acc[0][b] = mfma16x16x32(av, dq8p(word(fbu.b[b], i), s2[b]), acc[0][b]);
-      }
-    };
-    // Steady state: super-step S computes sub-steps u = 0..3 from weight
-    // slot u while loading the weights of sub-step u+3 (the next super-step's
-    // u-1 for u >= 1), the activations of sub-step u+1, and the next
-    // super-step's scales.  No branches: prefetches past the wave's range are
-    // clamped to its last super-step (cache hits), so the compiler counts
-    // outstanding loads exactly.
+  for (int i = 0; i < kRowsPerThread; ++i) {
+    const uint32_t o = lds_row[row_base + 16 * i];
+    aoffs[i] = o == kOob ? kOob : o + 256 * sq + 16 * sv;
+  }
+  u32x4_t st[kRowsPerThread];  // native vectors: an array of uint4 structs stays in scratch
+  uint32_t sc_cur[NBB][2], sc_nxt[NBB][2];
+  Frag<NBB> fb0, fb1;
+#define QMOE_LOAD_A_TILE(S, U, OK)                                                                 \
+do {                                                                                             \
+  _Pragma("unroll") for (int i = 0; i < kRowsPerThread; ++i) st[i] = __builtin_bit_cast(         \
+      u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rA, (OK) ? aoffs[i] + 64 * (U) : kOob,      \
+                                                     (S) * (kSuper * 2), 0));                    \
+} while (0)
+#define QMOE_STORE_A_TILE(BUF)                                                                     \
+do {                                                                                             \
+  _Pragma("unroll") for (int i = 0; i < kRowsPerThread; ++i)                                     \
+      *reinterpret_cast<u32x4_t*>(&lds_a[(BUF)][(row_base + 16 * i) * kAStride + seg * 8]) = st[i]; \
+} while (0)
+#define QMOE_COMPUTE(F, SC, U, BUF)                                                                \
+do {                                                                                             \
+  uint32_t s2_[NBB];                                                                             \
+  _Pragma("unroll") for (int b = 0; b < NBB; ++b) s2_[b] = scale_pair((SC)[b][0], (SC)[b][1], (U)); \
+  _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                \
+    half8_t bf[NBB];                                                                             \
+    _Pragma("unroll") for (int b = 0; b < NBB; ++b) bf[b] = dq8p(word((F).b[b], i), s2_[b]);     \
+    _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                                          \
+      if (mb < NMBC) {                                                                           \
+        const half8_t av =                                                                       \
+            *reinterpret_cast<const half8_t*>(&lds_a[(BUF)][(mb * 16 + r) * kAStride + 32 * kq + 8 * i]); \
+        _Pragma("unroll") for (int b = 0; b < NBB; ++b) acc[mb][b] = mfma16x16x32(av, bf[b], acc[mb][b]); \
+      }                                                                                          \
+    }                                                                                            \
+  }                                                                                              \
+} while (0)
+  // One sub-step with one barrier: prefetch the next sub-step's weights
+  // and activation tile (clamped, unconditional), compute this sub-step
+  // from LDS buffer BUF, then write the next tile (loaded during the
+  // compute) to the other buffer and meet the barrier that publishes it
+  // and frees BUF for the tile after next.
+#define QMOE_SUBSTEP(S, U, FCUR, FNEXT, SN, UN, BUF)                                               \
+do {                                                                                             \
+  load_b((SN), (UN), FNEXT, true);                                                               \
+  QMOE_LOAD_A_TILE((SN), (UN), true);                                                            \
+  QMOE_COMPUTE(FCUR, sc_cur, (U), (BUF));                                                        \
+  QMOE_STORE_A_TILE((BUF) ^ 1);                                                                  \
+  __syncthreads();                                                                               \
+} while (0)
+  // The row blocks that hold routed rows are computed without a branch per
+  // block: the loop is instantiated for 2, 4, 6 and 8 blocks and the
+  // item's count rounds up to the next of these (blocks past the item's
+  // rows multiply zero rows, which are never stored).
+  auto kloop = [&](auto nmbc_tag) __attribute__((always_inline)) {
+    constexpr int NMBC = decltype(nmbc_tag)::value;
     const int n = S_end_full - S_begin;
     if (n > 0) {
       load_sc(S_begin, sc_cur, true);
-#pragma unroll
-      for (int u = 0; u < 3; ++u) load_b(S_begin, u, fb[u], true);
-      load_a(S_begin, 0, fa[0], true);
+      load_b(S_begin, 0, fb0, true);
+      QMOE_LOAD_A_TILE(S_begin, 0, true);
+      QMOE_STORE_A_TILE(0);
+      __syncthreads();
       for (int S = S_begin; S < S_end_full; ++S) {
         const int Sn = min(S + 1, S_end_full - 1);
         load_sc(Sn, sc_nxt, true);
-        load_b(S, 3, fb[3], true);
-        load_a(S, 1, fa[1], true);
-        compute(fb[0], fa[0], sc_cur, 0);
-        load_b(Sn, 0, fb[0], true);
-        load_a(S, 2, fa[0], true);
-        compute(fb[1], fa[1], sc_cur, 1);
-        load_b(Sn, 1, fb[1], true);
-        load_a(S, 3, fa[1], true);
-        compute(fb[2], fa[0], sc_cur, 2);
-        load_b(Sn, 2, fb[2], true);
-        load_a(Sn, 0, fa[0], true);
-        compute(fb[3], fa[1], sc_cur, 3);
+        QMOE_SUBSTEP(S, 0, fb0, fb1, S, 1, 0);
+        QMOE_SUBSTEP(S, 1, fb1, fb0, S, 2, 1);
+        QMOE_SUBSTEP(S, 2, fb0, fb1, S, 3, 0);
+        QMOE_SUBSTEP(S, 3, fb1, fb0, Sn, 0, 1);
 #pragma unroll
         for (int b = 0; b < NBB; ++b) {
           sc_cur[b][0] = sc_nxt[b][0];
@@ -589,156 +599,25 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
       load_sc(nss_full, sc_cur, true);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const bool ok = nss_full * 16 + 4 * kq + u < ngroups;
-        load_b(nss_full, u, fb[u], ok);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bool ok = nss_full * 16 + 4 * kq + u < ngroups;
-        load_a(nss_full, u, fa[0], ok);
-        compute(fb[u], fa[0], sc_cur, u);
-      }
-    }
-  } else {
-    // ---------------- prefill tiles: the activation tile of each sub-step
-    // (MB*16 rows x 128 inputs, in MFMA k order) staged in LDS
-    static_assert(WK == 1, "128-row tiles split N across waves, not K");
-    __shared__ __attribute__((aligned(16))) _Float16 lds_a[2][MB * 16 * kAStride];  // double-buffered
-    __shared__ uint32_t lds_row[MB * 16];
-    for (int m = tid; m < MB * 16; m += kThreads) lds_row[m] = m < nr ? a_off_of(m) : kOob;
-    __syncthreads();
-    // thread -> 16-byte segment seg of rows (tid/16) + 16*i of the tile;
-    // tile column 32*q + 8*v (q = seg/4, v = seg%4) holds inputs
-    // (4q+u)*32 + 8v .. +8 of the super-step
-    const int seg = tid & 15, row_base = tid >> 4;
-    const int sq = seg >> 2, sv = seg & 3;
-    constexpr int kRowsPerThread = MB;  // MB*16 rows / 16 row groups
-    uint32_t aoffs[kRowsPerThread];
-#pragma unroll
-    for (int i = 0; i < kRowsPerThread; ++i) {
-      const uint32_t o = lds_row[row_base + 16 * i];
-      aoffs[i] = o == kOob ? kOob : o + 256 * sq + 16 * sv;
-    }
-    u32x4_t st[kRowsPerThread];  // native vectors: an array of uint4 structs stays in scratch
-    uint32_t sc_cur[NBB][2], sc_nxt[NBB][2];
-    Frag<NBB> fb0, fb1;
-#define QMOE_LOAD_A_TILE(S, U, OK)                                                                 \
-  do {                                                                                             \
-    _Pragma("unroll") for (int i = 0; i < kRowsPerThread; ++i) st[i] = __builtin_bit_cast(         \
-        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rA, (OK) ? aoffs[i] + 64 * (U) : kOob,      \
-                                                       (S) * (kSuper * 2), 0));                    \
-  } while (0)
-#define QMOE_STORE_A_TILE(BUF)                                                                     \
-  do {                                                                                             \
-    _Pragma("unroll") for (int i = 0; i < kRowsPerThread; ++i)                                     \
-        *reinterpret_cast<u32x4_t*>(&lds_a[(BUF)][(row_base + 16 * i) * kAStride + seg * 8]) = st[i]; \
-  } while (0)
-#define QMOE_COMPUTE(F, SC, U, BUF)                                                                \
-  do {                                                                                             \
-    uint32_t s2_[NBB];                                                                             \
-    _Pragma("unroll") for (int b = 0; b < NBB; ++b) s2_[b] = scale_pair((SC)[b][0], (SC)[b][1], (U)); \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                \
-      half8_t bf[NBB];                                                                             \
-      _Pragma("unroll") for (int b = 0; b < NBB; ++b) bf[b] = dq8p(word((F).b[b], i), s2_[b]);     \
-      _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                                          \
-        if (mb < NMBC) {                                                                           \
-          const half8_t av =                                                                       \
-              *reinterpret_cast<const half8_t*>(&lds_a[(BUF)][(mb * 16 + r) * kAStride + 32 * kq + 8 * i]); \
-          _Pragma("unroll") for (int b = 0; b < NBB; ++b) acc[mb][b] = mfma16x16x32(av, bf[b], acc[mb][b]); \
-        }                                                                                          \
-      }                                                                                            \
-    }                                                                                              \
-  } while (0)
-    // One sub-step with one barrier: prefetch the next sub-step's weights
-    // and activation tile (clamped, unconditional), compute this sub-step
-    // from LDS buffer BUF, then write the next tile (loaded during the
-    // compute) to the other buffer and meet the barrier that publishes it
-    // and frees BUF for the tile after next.
-#define QMOE_SUBSTEP(S, U, FCUR, FNEXT, SN, UN, BUF)                                               \
-  do {                                                                                             \
-    load_b((SN), (UN), FNEXT, true);                                                               \
-    QMOE_LOAD_A_TILE((SN), (UN), true);                                                            \
-    QMOE_COMPUTE(FCUR, sc_cur, (U), (BUF));                                                        \
-    QMOE_STORE_A_TILE((BUF) ^ 1);                                                                  \
-    __syncthreads();                                                                               \
-  } while (0)
-    // The row blocks that hold routed rows are computed without a branch per
-    // block: the loop is instantiated for 2, 4, 6 and 8 blocks and the
-    // item's count rounds up to the next of these (blocks past the item's
-    // rows multiply zero rows, which are never stored).
-    auto kloop = [&](auto nmbc_tag) __attribute__((always_inline)) {
-      constexpr int NMBC = decltype(nmbc_tag)::value;
-      const int n = S_end_full - S_begin;
-      if (n > 0) {
-        load_sc(S_begin, sc_cur, true);
-        load_b(S_begin, 0, fb0, true);
-        QMOE_LOAD_A_TILE(S_begin, 0, true);
+        const bool okb = nss_full * 16 + 4 * kq + u < ngroups;
+        const bool oka = nss_full * 16 + 4 * sq + u < ngroups;
+        load_b(nss_full, u, fb0, okb);
+        QMOE_LOAD_A_TILE(nss_full, u, oka);
+        __syncthreads();
         QMOE_STORE_A_TILE(0);
         __syncthreads();
-        for (int S = S_begin; S < S_end_full; ++S) {
-          const int Sn = min(S + 1, S_end_full - 1);
-          load_sc(Sn, sc_nxt, true);
-          QMOE_SUBSTEP(S, 0, fb0, fb1, S, 1, 0);
-          QMOE_SUBSTEP(S, 1, fb1, fb0, S, 2, 1);
-          QMOE_SUBSTEP(S, 2, fb0, fb1, S, 3, 0);
-          QMOE_SUBSTEP(S, 3, fb1, fb0, Sn, 0, 1);
-  #pragma unroll
-          for (int b = 0; b < NBB; ++b) {
-            sc_cur[b][0] = sc_nxt[b][0];
-            sc_cur[b][1] = sc_nxt[b][1];
-          }
-        }
+        QMOE_COMPUTE(fb0, sc_cur, u, 0);
       }
-      if (has_tail) {  // the partial super-step: groups past K read zeros
-        load_sc(nss_full, sc_cur, true);
-  #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const bool okb = nss_full * 16 + 4 * kq + u < ngroups;
-          const bool oka = nss_full * 16 + 4 * sq + u < ngroups;
-          load_b(nss_full, u, fb0, okb);
-          QMOE_LOAD_A_TILE(nss_full, u, oka);
-          __syncthreads();
-          QMOE_STORE_A_TILE(0);
-          __syncthreads();
-          QMOE_COMPUTE(fb0, sc_cur, u, 0);
-        }
-      }
-    };
-    if (nmb <= 2) kloop(std::integral_constant<int, (MB < 2 ? MB : 2)>{});
-    else if (nmb <= 4) kloop(std::integral_constant<int, (MB < 4 ? MB : 4)>{});
-    else if (nmb <= 6) kloop(std::integral_constant<int, (MB < 6 ? MB : 6)>{});
-    else kloop(std::integral_constant<int, MB>{});
+    }
+  };
+  if (nmb <= 2) kloop(std::integral_constant<int, (MB < 2 ? MB : 2)>{});
+  else if (nmb <= 4) kloop(std::integral_constant<int, (MB < 4 ? MB : 4)>{});
+  else if (nmb <= 6) kloop(std::integral_constant<int, (MB < 6 ? MB : 6)>{});
+  else kloop(std::integral_constant<int, MB>{});
 #undef QMOE_SUBSTEP
 #undef QMOE_COMPUTE
 #undef QMOE_STORE_A_TILE
 #undef QMOE_LOAD_A_TILE
-  }
-
-  // ---- reduce the WK partial sums (fixed order: wave wk=0 adds 1, 2, 3)
-  if constexpr (WK > 1) {
-    constexpr int kVals = MB * NBB * 4;
-    __shared__ float red[(WK - 1) * WN * kVals * 64];
-    if (wk > 0) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int b = 0; b < NBB; ++b)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            red[((((wk - 1) * WN + wn) * kVals) + (mb * NBB + b) * 4 + i) * 64 + lane] = acc[mb][b][i];
-    }
-    __syncthreads();
-    if (wk > 0) return;
-#pragma unroll
-    for (int w = 1; w < WK; ++w)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int b = 0; b < NBB; ++b)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[mb][b][i] += red[((((w - 1) * WN + wn) * kVals) + (mb * NBB + b) * 4 + i) * 64 + lane];
-  }
 
   // ---- epilogue: lane holds rows mb*16 + 4*kq + i of column r of each block
 #pragma unroll
@@ -795,6 +674,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 // The item's activation rows are staged in LDS once per block.
 constexpr int kGemvRows = 2;
 constexpr int kGemvMaxRowsPerExpert = 4;  // GEMV while M*top_k <= 4E
+constexpr int kGemvMaxK = 15360;  // largest K the GEMV stages (two rows in 64 KiB of LDS)
 
 // LDS bytes of a block: the activation rows
 __host__ __device__ constexpr size_t gemv_lds_bytes(int K) { return (size_t)kGemvRows * K * 2; }
@@ -1172,7 +1052,8 @@ struct qmoe_layer {
   int device = 0;
   bool shared = false;
   std::atomic<uint64_t> forward_calls{0}, route_calls{0}, gemm_launches{0}, launches{0}, inits{0},
-      ws_last{0}, ws_peak{0}, decode_tiles{0}, prefill_tiles{0}, gemv_tiles{0};
+      ws_last{0}, ws_peak{0}, prefill_tiles{0}, gemv_tiles{0};
+  int split_k = 1;  // GEMV K split (1, 2 or 4 waves along K)
   std::mutex mu;
   std::vector<std::pair<const void*, size_t>> inited;
 };
@@ -1210,24 +1091,21 @@ Layout make_layout(const qmoe_layer* L, int64_t M) {
   return l;
 }
 
-// Tile regime of a call, from the average routed rows per expert:
-// GEMV (items of <= 2 rows on packed dot products) up to 4 rows on average,
-// 16-row MFMA tiles below 8, 128-row MFMA tiles above.  An expert with more
-// than 2 rows takes several GEMV items, each streaming its weights; measured
-// on MI355X (E=384, H=7168, I=2048, top-8) that still beats the 16-row
-// tiles up to about 4 rows per expert (M=192), and loses beyond (M=256).
-// The GEMV stages two activation rows in LDS, so it is used while they fit
-// in 64 KiB.
-enum Regime { kGemv, kDecode, kPrefill };
-constexpr int kGemvMaxK = 15360;
+// Kernel regime of a call, from the average routed rows per expert: the
+// dot-product GEMV (items of <= 2 rows) up to 4 rows on average, 128-row
+// MFMA tiles above.  An expert with more than 2 rows takes several GEMV
+// items, each streaming its weights; measured on MI355X (E=384, H=7168,
+// I=2048, top-8) that still beats the MFMA tiles up to about 4 rows per
+// expert (M=192), and loses beyond (M=256).  The GEMV stages two activation
+// rows in LDS, so it is used while they fit in 64 KiB.
+enum Regime { kGemv, kPrefill };
 static_assert(gemv_lds_bytes(kGemvMaxK) <= 65536, "GEMV rows fit in 64 KiB of LDS");
 Regime regime_of(const qmoe_layer* L, int64_t M) {
   const int64_t T = M * (int64_t)L->d.top_k, E = L->d.E;
   if (T <= kGemvMaxRowsPerExpert * E && L->d.H <= kGemvMaxK && L->d.I <= kGemvMaxK) return kGemv;
-  if (T < 8 * E) return kDecode;
   return kPrefill;
 }
-int rows_per_item(Regime rg) { return rg == kGemv ? kGemvRows : rg == kDecode ? 16 : kPrefillRows; }
+int rows_per_item(Regime rg) { return rg == kGemv ? kGemvRows : kPrefillRows; }
 
 template <typename T>
 T* at(void* ws, size_t off) {
@@ -1363,27 +1241,20 @@ void fill_gemm_args(const qmoe_layer* L, int64_t M, void* ws, const Layout& lay,
   }
 }
 
-template <int MB, int NBW, int WN, int WK, int PF, bool GATEUP>
+template <int MB, int NBW, bool GATEUP>
 int launch_gemm(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t st) {
   GemmArgs g;
   fill_gemm_args<GATEUP>(L, M, ws, lay, g);
   const int E = L->d.E;
   const int bmc = MB * 16;
   g.max_items = (int)max_items_for(lay.T, M, lay.S, E, bmc);
-  g.nblk = (int)ceil_div(g.N, WN * NBW * 16);
+  g.nblk = (int)ceil_div(g.N, 4 * NBW * 16);
   const int64_t blocks = 8 * (int64_t)g.nblk * ceil_div(g.max_items, 8);
   if (blocks > 0x7FFFFFFF) return fail(QMOE_ERR_UNSUPPORTED, "grid too large");
-  gemm_kernel<MB, NBW, WN, WK, PF, GATEUP><<<dim3((unsigned)blocks), kThreads, 0, st>>>(g);
+  gemm_kernel<MB, NBW, GATEUP><<<dim3((unsigned)blocks), kThreads, 0, st>>>(g);
   L->gemm_launches++;
   return check_launch(L, GATEUP ? "gate_up gemm" : "down gemm");
 }
-
-#ifndef QMOE_GEMV_GU_WN
-#define QMOE_GEMV_GU_WN 4
-#endif
-#ifndef QMOE_GEMV_DN_WN
-#define QMOE_GEMV_DN_WN 4
-#endif
 
 template <int WN, bool GATEUP>
 int launch_gemv(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t st) {
@@ -1401,28 +1272,27 @@ int launch_gemv(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream
   return check_launch(L, GATEUP ? "gate_up gemv" : "down gemv");
 }
 
+// GEMV shape: 4 waves along N, or K split over 2 or 4 of them (the split
+// each layer was created with; see qmoe_layer_create)
+template <bool GATEUP>
+int launch_gemv_split(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t st) {
+  if (L->split_k == 4) return launch_gemv<1, GATEUP>(L, M, ws, lay, st);
+  if (L->split_k == 2) return launch_gemv<2, GATEUP>(L, M, ws, lay, st);
+  return launch_gemv<4, GATEUP>(L, M, ws, lay, st);
+}
+
 int do_gate_up(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t st) {
-  const Regime rg = regime_of(L, M);
-  if (rg == kGemv) {
+  if (regime_of(L, M) == kGemv) {
     L->gemv_tiles++;
-    return launch_gemv<QMOE_GEMV_GU_WN, true>(L, M, ws, lay, st);
-  }
-  if (rg == kDecode) {
-    L->decode_tiles++;
-    return launch_gemm<1, QMOE_DEC_GU_NBW, QMOE_DEC_GU_WN, 4 / QMOE_DEC_GU_WN, QMOE_DEC_GU_PF, true>(L, M, ws,
-                                                                                                  lay, st);
+    return launch_gemv_split<true>(L, M, ws, lay, st);
   }
   L->prefill_tiles++;
-  return launch_gemm<QMOE_PRE_MB, QMOE_PRE_GU_NBW, 4, 1, 3, true>(L, M, ws, lay, st);
+  return launch_gemm<QMOE_PRE_MB, QMOE_PRE_GU_NBW, true>(L, M, ws, lay, st);
 }
 
 int do_down(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t st) {
-  const Regime rg = regime_of(L, M);
-  if (rg == kGemv) return launch_gemv<QMOE_GEMV_DN_WN, false>(L, M, ws, lay, st);
-  if (rg == kDecode)
-    return launch_gemm<1, QMOE_DEC_DN_NBW, QMOE_DEC_DN_WN, 4 / QMOE_DEC_DN_WN, QMOE_DEC_DN_PF, false>(L, M, ws,
-                                                                                                   lay, st);
-  return launch_gemm<QMOE_PRE_MB, QMOE_PRE_DN_NBW, 4, 1, 3, false>(L, M, ws, lay, st);
+  if (regime_of(L, M) == kGemv) return launch_gemv_split<false>(L, M, ws, lay, st);
+  return launch_gemm<QMOE_PRE_MB, QMOE_PRE_DN_NBW, false>(L, M, ws, lay, st);
 }
 
 int do_combine(qmoe_layer* L, int64_t M, void* out, void* ws, const Layout& lay, hipStream_t st) {
@@ -1470,6 +1340,11 @@ int qmoe_layer_create(const qmoe_layer_desc* d, qmoe_layer** out) {
   if (nsh != 0 && nsh != 4) return fail(QMOE_ERR_ARG, "shared expert: set all four pointers or none");
   if (!aligned16(d->w13) || !aligned16(d->w2) || (nsh && (!aligned16(d->shared_w13) || !aligned16(d->shared_w2))))
     return fail(QMOE_ERR_ARG, "weight code arrays must be 16-byte aligned");
+  int split_k = 1;
+  if (const char* v = std::getenv("QMOE_SPLIT_K")) {
+    split_k = std::atoi(v);
+    if (split_k != 1 && split_k != 2 && split_k != 4) return fail(QMOE_ERR_ARG, "QMOE_SPLIT_K must be 1, 2 or 4");
+  }
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return fail(QMOE_ERR_DEVICE, "no HIP device (hipGetDevice failed)");
   hipDeviceProp_t prop;
@@ -1480,6 +1355,7 @@ int qmoe_layer_create(const qmoe_layer_desc* d, qmoe_layer** out) {
   L->d = *d;
   L->device = dev;
   L->shared = nsh == 4;
+  L->split_k = split_k;
   *out = L;
   return QMOE_OK;
 }
@@ -1627,7 +1503,6 @@ int qmoe_get_stats(const qmoe_layer* L, qmoe_stats* s) {
   s->workspace_inits = L->inits.load();
   s->workspace_bytes_last = L->ws_last.load();
   s->workspace_bytes_peak = L->ws_peak.load();
-  s->decode_tiles = L->decode_tiles.load();
   s->prefill_tiles = L->prefill_tiles.load();
   s->gemv_tiles = L->gemv_tiles.load();
   return QMOE_OK;
@@ -1642,7 +1517,6 @@ int qmoe_reset_stats(qmoe_layer* L) {
   L->inits = 0;
   L->ws_last = 0;
   L->ws_peak = 0;
-  L->decode_tiles = 0;
   L->prefill_tiles = 0;
   L->gemv_tiles = 0;
   return QMOE_OK;

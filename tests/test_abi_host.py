@@ -67,6 +67,14 @@ def test_create_rejects_bad_fields(lib, field, value, needle):
     assert not h.value
 
 
+def test_create_rejects_bad_split_k(lib, monkeypatch):
+    monkeypatch.setenv("QMOE_SPLIT_K", "3")
+    h = ctypes.c_void_p()
+    assert lib.qmoe_layer_create(ctypes.byref(_desc()), ctypes.byref(h)) == B.QMOE_ERR_ARG
+    assert "QMOE_SPLIT_K" in lib.qmoe_last_error().decode()
+    assert not h.value
+
+
 def test_create_null_arguments(lib):
     h = ctypes.c_void_p()
     assert lib.qmoe_layer_create(None, ctypes.byref(h)) == B.QMOE_ERR_ARG

@@ -116,23 +116,23 @@ def test_routing_repeatable_and_workspace_reuse():
 # ------------------------------------------------------------ whole layer
 
 FWD_CASES = [
-    # E, H, I, k, M, shared   (dot-product items of <= 2 rows when M*k <= 4E,
-    #                          16-row tiles when M*k < 8E, else 128-row tiles)
-    (8, 256, 128, 2, 16, False),     # the tiny configuration
-    (8, 256, 128, 2, 1, False),
-    (16, 640, 384, 2, 37, False),    # K = 1 super-step + a partial one / a partial one; decode tiles
-    (64, 128, 128, 2, 9, True),      # decode tiles with a shared expert
-    (4, 640, 384, 2, 300, False),    # 128-row tiles, 2 row tiles per expert, partial super-steps
-    (4, 256, 128, 1, 200, True),     # 128-row tiles with a shared expert
+    # E, H, I, k, M, shared   (dot-product GEMV items of <= 2 rows when
+    #                          M*k <= 4E, else 128-row MFMA tiles)
+    (8, 256, 128, 2, 16, False),     # the tiny configuration (GEMV, several items per expert)
+    (8, 256, 128, 2, 1, False),      # GEMV, one row
+    (16, 640, 384, 2, 37, False),    # tiles: K = 1 super-step + a partial one / a partial one
+    (64, 128, 128, 2, 9, True),      # GEMV with a shared expert
+    (4, 640, 384, 2, 300, False),    # tiles: 2 row tiles per expert, partial super-steps
+    (4, 256, 128, 1, 200, True),     # tiles with a shared expert
     (4, 512, 256, 4, 20, False),     # top_k = E
-    (8, 2048, 1536, 2, 64, False),   # several super-steps per wave in both GEMMs
-    (3, 384, 1152, 2, 130, False),   # N not a multiple of the block width
-    (64, 1152, 640, 2, 20, False),   # dot-product items: whole + partial super-steps in both GEMMs
-    (32, 2048, 1536, 4, 8, True),    # dot-product items, 2-row items, shared expert, split K
-    (16, 256, 128, 8, 2, False),     # dot-product items, top_k = 8, partial super-steps only
-    (8, 512, 256, 2, 12, True),      # dot-product items, experts with several items, shared expert
-    (8, 256, 128, 2, 24, False),     # 16-row tiles on the tiny shape
-    (16, 640, 384, 2, 40, True),     # 16-row tiles with a shared expert, partial super-steps
+    (8, 2048, 1536, 2, 64, False),   # tiles: several super-steps per wave in both GEMMs
+    (3, 384, 1152, 2, 130, False),   # tiles: N not a multiple of the block width
+    (64, 1152, 640, 2, 20, False),   # GEMV: whole + partial super-steps in both GEMMs
+    (32, 2048, 1536, 4, 8, True),    # GEMV: 2-row items, shared expert
+    (16, 256, 128, 8, 2, False),     # GEMV: top_k = 8, partial super-steps only
+    (8, 512, 256, 2, 12, True),      # GEMV: experts with several items, shared expert
+    (8, 256, 128, 2, 40, False),     # tiles on the tiny shape (2 row blocks)
+    (16, 640, 384, 2, 72, True),     # tiles with a shared expert, partial super-steps
 ]
 
 
@@ -186,7 +186,24 @@ def test_steps_match_oracle_intermediates(E, H, I, k, M, shared):
     assert rel_err(out, ref["out"]) <= REL_TOL
 
 
-@pytest.mark.parametrize("M", [20, 2])  # 16-row tiles, dot-product items
+@pytest.mark.parametrize("split", ["2", "4"])
+@pytest.mark.parametrize("case", [(64, 1152, 640, 2, 20, False), (32, 2048, 1536, 4, 8, True),
+                                  (8, 512, 256, 2, 12, True)])
+def test_gemv_split_k_parity(monkeypatch, split, case):
+    """The GEMV with K split over 2 or 4 waves of a block (fixed-order LDS
+    reduction) against the oracle, and against the unsplit layer."""
+    import torch
+    monkeypatch.setenv("QMOE_SPLIT_K", split)
+    say(f"split-K {split} case {case}")
+    layer, w, x, lg, ref = _run_case(*case)
+    out = layer.forward(dev_bf16(x), dev(lg)).float().cpu().numpy()
+    assert layer.stats()["gemv_tiles"] == 1
+    err = rel_err(out, ref["out"])
+    say(f"  rel err out {err:.3e}")
+    assert err <= REL_TOL
+
+
+@pytest.mark.parametrize("M", [20, 2])  # 128-row tiles, dot-product items
 def test_diagonal_weights_closed_form_on_gpu(M):
     """Top-1 with diagonal weights and power-of-two scales: the output is
     sd*su*x*SiLU(sg*x) on the first min(H, I) columns and 0 elsewhere."""
@@ -251,7 +268,7 @@ def test_counters_and_workspace_accounting():
     assert s["gemm_launches"] == 2 and s["launches"] == 4
     assert s["workspace_inits"] == 0
     assert s["workspace_bytes_last"] == s["workspace_bytes_peak"] == layer.workspace_bytes(16) > 0
-    assert s["decode_tiles"] + s["prefill_tiles"] + s["gemv_tiles"] == 1
+    assert s["prefill_tiles"] + s["gemv_tiles"] == 1
 
 
 def test_errors_from_the_library():
