@@ -227,6 +227,9 @@ def main():
         roof = {"bound": "hbm", "achieved": round(r["gate_up_GBps"], 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(r["gate_up_GBps"] / HBM_PEAK_GBS, 4)}
     roof["traffic"] = traffic
+    # both fractions, whichever binds (the plateau sits near the ridge)
+    roof["hbm_frac"] = round(r["gate_up_GBps"] / HBM_PEAK_GBS, 4)
+    roof["mfma_frac"] = round(r["gate_up_TFLOPs"] / MFMA_PEAK_TFLOPS, 4)
     roof["kernel"] = "gate_up (stacked gate+up grouped GEMM, SiLU*up epilogue)"
     roof["kernel_us"] = round(r["gate_up_us"], 2)
     roof["algorithmic_bytes_per_launch"] = round(r["gate_up_bytes_per_launch"])
