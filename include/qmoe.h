@@ -121,10 +121,9 @@ void qmoe_layer_destroy(qmoe_layer* layer);
 /* Bytes of workspace a call with M tokens needs (0 <= M <= max_rows). */
 int qmoe_workspace_size(const qmoe_layer* layer, int64_t M, size_t* bytes);
 
-/* Enqueue the one-time initialisation of a workspace (clears its control
-   words).  Every call leaves the workspace initialised again, so this is
-   needed once per workspace; the library also does it by itself the first
-   time it sees a workspace pointer on a handle. */
+/* Enqueue a clear of a workspace's control words.  Optional: the calls do
+   not depend on what a workspace held before (a call that routes more than
+   64 tokens clears the routing ticket itself, one extra tiny launch). */
 int qmoe_workspace_init(qmoe_layer* layer, void* workspace, size_t ws_bytes, void* stream);
 
 /* The whole layer: route, gate+up, down, combine (four kernel launches).
@@ -181,7 +180,7 @@ typedef struct {
   uint64_t route_calls;       /* qmoe_route, also inside qmoe_forward */
   uint64_t gemm_launches;     /* gate+up and down kernel launches */
   uint64_t launches;          /* every kernel launch */
-  uint64_t workspace_inits;   /* explicit and automatic */
+  uint64_t workspace_inits;   /* qmoe_workspace_init calls */
   uint64_t workspace_bytes_last;
   uint64_t workspace_bytes_peak;
   uint64_t prefill_tiles;     /* gate+up launches on 128-row MFMA tiles */

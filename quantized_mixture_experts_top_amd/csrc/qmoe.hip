@@ -22,7 +22,6 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <mutex>
 #include <string>
 #include <type_traits>
 #include <utility>
@@ -38,12 +37,10 @@ namespace {
 constexpr int kThreads = 256;   // every kernel: 4 waves of 64
 constexpr int kChunk = 64;      // tokens per routing chunk = bits of one mask word
 constexpr int kCtrlWords = 64;  // [0] route ticket, [1] number of work items
-constexpr int kZeroWords = 64;  // 256 zero bytes after the control words
 constexpr int kKStep = 128;     // inputs per K-step of a wave (4 lane groups x 32)
 
-// Tile shapes (compile-time; one of the two shapes is picked per call from
-// M*top_k vs E).  NBW = 16-column output blocks per wave, WN x WK = waves of
-// a block along N and K, PF = K-steps of loads in flight beyond the current.
+// Shape of the 128-row MFMA tiles: MB row blocks of 16 per work item, NBW
+// 16-column output blocks per wave (gate+up: each with its up block).
 #ifndef QMOE_PRE_MB
 #define QMOE_PRE_MB 8
 #endif
@@ -340,10 +337,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   }
   const int T = a.M * k;
   for (int t = tid; t < a.S; t += kRouteThreads) a.perm[T + t] = T + t;
-  if (a.C > 1) {
-    __syncthreads();
-    if (tid == 0) atomicExch(a.ctrl, 0);
-  }
 }
 
 // ------------------------------------------------------------------ GEMMs
@@ -412,17 +405,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   const int wn = wave % WN, wk = wave / WN;
   const int r = lane & 15, kq = lane >> 4;
 
-#ifndef QMOE_XCD_MAP
-#define QMOE_XCD_MAP 1
-#endif
-#if QMOE_XCD_MAP == 1
-  // all blocks of one item land on one XCD (block ids go round-robin over 8)
+  // all blocks of one item land on one XCD (block ids go round-robin over
+  // 8), so the item's activation rows are reused from that XCD's L2
   const int bid = blockIdx.x, xcd = bid & 7, jj = bid >> 3;
   const int item = (jj / g.nblk) * 8 + xcd, nb = jj % g.nblk;
-#else
-  // consecutive blocks take consecutive N-blocks of one item (spread over XCDs)
-  const int item = blockIdx.x / g.nblk, nb = blockIdx.x % g.nblk;
-#endif
   const int n_items = min(g.ctrl[1], g.max_items);
   if (item >= n_items) return;
   const int4 it = g.items[item];
@@ -1020,7 +1006,7 @@ __global__ __launch_bounds__(kThreads) void read_h_kernel(const _Float16* h, con
 }
 
 __global__ void init_ctrl_kernel(int* ctrl) {
-  if (threadIdx.x < kCtrlWords + kZeroWords) ctrl[threadIdx.x] = 0;
+  if (threadIdx.x < kCtrlWords) ctrl[threadIdx.x] = 0;
 }
 
 // ============================================================= host side
@@ -1054,8 +1040,6 @@ struct qmoe_layer {
   std::atomic<uint64_t> forward_calls{0}, route_calls{0}, gemm_launches{0}, launches{0}, inits{0},
       ws_last{0}, ws_peak{0}, prefill_tiles{0}, gemv_tiles{0};
   int split_k = 1;  // GEMV K split (1, 2 or 4 waves along K)
-  std::mutex mu;
-  std::vector<std::pair<const void*, size_t>> inited;
 };
 
 namespace {
@@ -1074,7 +1058,7 @@ Layout make_layout(const qmoe_layer* L, int64_t M) {
     off = align256(off + bytes);
     return o;
   };
-  l.ctrl = take((kCtrlWords + kZeroWords) * 4);
+  l.ctrl = take(kCtrlWords * 4);
   l.ids = take(l.T * 4);
   l.wts = take(l.T * 4);
   l.counts = take((E + 1) * 4);
@@ -1144,22 +1128,10 @@ int check_call(qmoe_layer* L, int64_t M, const void* ws, size_t ws_bytes, Layout
 }
 
 int init_workspace(qmoe_layer* L, void* ws, size_t ws_bytes, hipStream_t st) {
-  init_ctrl_kernel<<<1, kCtrlWords + kZeroWords, 0, st>>>(static_cast<int*>(ws));
+  (void)ws_bytes;
+  init_ctrl_kernel<<<1, kCtrlWords, 0, st>>>(static_cast<int*>(ws));
   L->inits++;
-  const int rc = check_launch(L, "workspace init");
-  if (rc != QMOE_OK) return rc;
-  std::lock_guard<std::mutex> g(L->mu);
-  L->inited.emplace_back(ws, ws_bytes);
-  return QMOE_OK;
-}
-
-int ensure_inited(qmoe_layer* L, void* ws, size_t ws_bytes, hipStream_t st) {
-  {
-    std::lock_guard<std::mutex> g(L->mu);
-    for (auto& p : L->inited)
-      if (p.first == ws) return QMOE_OK;
-  }
-  return init_workspace(L, ws, ws_bytes, st);
+  return check_launch(L, "workspace init");
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -1191,6 +1163,13 @@ int do_route(qmoe_layer* L, const void* x, const float* logits, int64_t M, void*
   a.inv_perm = at<int>(ws, lay.inv_perm);
   a.items = at<int4>(ws, lay.items);
   a.xa = at<uint4>(ws, lay.xa);
+  if (lay.C > 1) {
+    // several routing blocks meet at a ticket: clear it first (the call
+    // then does not depend on what the workspace held before)
+    init_ctrl_kernel<<<1, kCtrlWords, 0, st>>>(a.ctrl);
+    const int rc = check_launch(L, "ticket clear");
+    if (rc != QMOE_OK) return rc;
+  }
   const dim3 grid((unsigned)lay.C);
   const int epl = (L->d.E + 63) / 64;
   if (epl <= 1) route_kernel<1><<<grid, kRouteThreads, 0, st>>>(a);
@@ -1372,7 +1351,7 @@ int qmoe_workspace_size(const qmoe_layer* L, int64_t M, size_t* bytes) {
 int qmoe_workspace_init(qmoe_layer* L, void* ws, size_t ws_bytes, void* stream) {
   if (!L) return fail(QMOE_ERR_ARG, "layer is NULL");
   if (!ws) return fail(QMOE_ERR_WORKSPACE, "workspace is NULL");
-  if (ws_bytes < (kCtrlWords + kZeroWords) * 4) return fail(QMOE_ERR_WORKSPACE, "workspace too small");
+  if (ws_bytes < kCtrlWords * 4) return fail(QMOE_ERR_WORKSPACE, "workspace too small");
   if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return fail(QMOE_ERR_WORKSPACE, "workspace not 256-byte aligned");
   return init_workspace(L, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
@@ -1383,7 +1362,6 @@ int qmoe_route(qmoe_layer* L, const void* x, const float* logits, int64_t M, voi
   int rc = check_call(L, M, ws, ws_bytes, &lay);
   if (rc != QMOE_OK || M == 0) return rc;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if ((rc = ensure_inited(L, ws, ws_bytes, st)) != QMOE_OK) return rc;
   return do_route(L, x, logits, M, ws, lay, st);
 }
 
@@ -1415,7 +1393,6 @@ int qmoe_forward(qmoe_layer* L, const void* x, const float* logits, int64_t M, v
   if (rc != QMOE_OK || M == 0) return rc;
   if (!out) return fail(QMOE_ERR_ARG, "out is NULL");
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if ((rc = ensure_inited(L, ws, ws_bytes, st)) != QMOE_OK) return rc;
   if ((rc = do_route(L, x, logits, M, ws, lay, st)) != QMOE_OK) return rc;
   if ((rc = do_gate_up(L, M, ws, lay, st)) != QMOE_OK) return rc;
   if ((rc = do_down(L, M, ws, lay, st)) != QMOE_OK) return rc;

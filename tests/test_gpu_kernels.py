@@ -246,6 +246,27 @@ def test_repeat_runs_bitwise_identical(case):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("M", [9, 130])  # one routing block; three meeting at a ticket
+def test_uninitialised_workspace(M):
+    """A workspace full of stale bytes, never initialised, gives the same
+    output as the layer's own (initialised) workspace: calls depend on no
+    workspace state from before."""
+    import ctypes
+    import torch
+    shape = synth.LayerShape(E=64, H=256, I=128, top_k=4)
+    layer, _ = make_layer(shape, 3, M)
+    x, lg = dev_bf16(synth.hidden(4, M, shape.H)), dev(synth.logits(4, M, shape.E))
+    want = layer.forward(x, lg).clone()
+    ws = torch.full((layer.workspace_bytes(M),), 0xA5, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(want)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    rc = layer.lib.qmoe_forward(layer.handle, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(lg.data_ptr()), M,
+                                ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()), ws.numel(), st)
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), want.view(torch.int16))
+
+
 def test_zero_tokens_is_a_noop():
     import torch
     shape = synth.TINY
