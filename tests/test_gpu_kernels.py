@@ -133,6 +133,12 @@ FWD_CASES = [
     (8, 512, 256, 2, 12, True),      # GEMV: experts with several items, shared expert
     (8, 256, 128, 2, 40, False),     # tiles on the tiny shape (2 row blocks)
     (16, 640, 384, 2, 72, True),     # tiles with a shared expert, partial super-steps
+    (1, 256, 128, 1, 3, False),      # one expert, GEMV (a plain quantized SwiGLU MLP)
+    (1, 256, 128, 1, 5, False),      # one expert, tiles
+    (32, 256, 128, 32, 3, False),    # top_k = 32 = E (the largest top_k)
+    (1024, 128, 128, 8, 20, True),   # 1024 experts (the most), shared expert
+    (4, 15360, 128, 2, 3, False),    # the largest K the GEMV stages in LDS
+    (4, 15488, 128, 1, 2, False),    # K past the GEMV's LDS: small M on tiles
 ]
 
 
@@ -265,6 +271,19 @@ def test_uninitialised_workspace(M):
     assert rc == 0
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), want.view(torch.int16))
+
+
+def test_side_stream():
+    """The layer enqueues only on the stream it is given."""
+    import torch
+    layer, w, x, lg, ref = _run_case(32, 2048, 1536, 4, 8, True)
+    xs, ls = dev_bf16(x), dev(lg)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        out = layer.forward(xs, ls, stream=side)
+    side.synchronize()
+    assert rel_err(out.float().cpu().numpy(), ref["out"]) <= REL_TOL
 
 
 def test_zero_tokens_is_a_noop():
