@@ -51,7 +51,6 @@ constexpr int kKStep = 128;     // inputs per K-step of a wave (4 lane groups x 
 #define QMOE_PRE_DN_NBW 2
 #endif
 constexpr int kPrefillRows = QMOE_PRE_MB * 16;
-constexpr int kAStride = kKStep + 8;  // LDS row stride of the A tile (halves), padded
 
 // ---------------------------------------------------------------- routing
 
@@ -376,6 +375,13 @@ __device__ __forceinline__ uint32_t scale_pair(uint32_t lo, uint32_t hi, int u) 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// 16 bytes per lane from a raw buffer straight into LDS: lane l's bytes
+// land at lds + 16*l (lds is wave-uniform); out-of-range lanes write zeros.
+// Kept out of the kernel templates, whose host-side instantiation cannot
+// take this builtin.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, _Float16* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
 constexpr uint32_t kOob = 0x7FFFFF00u;  // a lane offset past any buffer: its loads read 0
 constexpr int kSuper = 4 * kKStep;     // inputs per super-step (16 groups)
 
@@ -394,7 +400,7 @@ constexpr int kSuper = 4 * kKStep;     // inputs per super-step (16 groups)
 // Loads are buffer loads with a fixed per-lane offset and a scalar
 // per-step offset (no vector address arithmetic); inputs past K read zeros.
 template <int MB, int NBW, bool GATEUP>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void gemm_kernel(GemmArgs g) {
   constexpr int WN = 4, WK = 1;
   static_assert(MB > 1, "row tiles of at least 32 rows");
   constexpr int NBB = GATEUP ? 2 * NBW : NBW;
@@ -493,67 +499,83 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   };
 
   // ---------------- prefill tiles: the activation tile of each sub-step
-  // (MB*16 rows x 128 inputs, in MFMA k order) staged in LDS
+  // (MB*16 rows x 128 inputs) staged in LDS by direct global->LDS loads.
+  // In sub-step u a row's inputs are four 64-byte segments (segment kq =
+  // bytes 256kq + 64u of the row's super-step, the inputs of group 4kq+u).
+  // One load instruction fills one LDS block of 1 KiB: rows q, q+4, q+8,
+  // q+12 of a row block (lane l = 16rr + 4x + j takes byte 16j of segment
+  // (x - rr) mod 4 of row q + 4rr), so every four lanes read 64 contiguous
+  // bytes.  Blocks are 1040 bytes apart and segments rotate by row, so the
+  // 16 lanes that read one MFMA operand column (rows 0..15, one segment,
+  // one 16-byte piece) hit 16 distinct 16-byte bank groups.  Wave w loads
+  // block q = w of every row block.
   static_assert(WK == 1, "128-row tiles split N across waves, not K");
-  __shared__ __attribute__((aligned(16))) _Float16 lds_a[2][MB * 16 * kAStride];  // double-buffered
+  constexpr int kBlkHalves = 520;  // 1040-byte LDS block
+  // two buffers as separate arrays, so that the compiler can tell loads
+  // into one from operand reads of the other
+  __shared__ __attribute__((aligned(16))) _Float16 lds_a0[MB * 4 * kBlkHalves];
+  __shared__ __attribute__((aligned(16))) _Float16 lds_a1[MB * 4 * kBlkHalves];
+#define QMOE_LDS_A(BUF) ((BUF) ? lds_a1 : lds_a0)
   __shared__ uint32_t lds_row[MB * 16];
   for (int m = tid; m < MB * 16; m += kThreads) lds_row[m] = m < nr ? a_off_of(m) : kOob;
   __syncthreads();
-  // thread -> 16-byte segment seg of rows (tid/16) + 16*i of the tile;
-  // tile column 32*q + 8*v (q = seg/4, v = seg%4) holds inputs
-  // (4q+u)*32 + 8v .. +8 of the super-step
-  const int seg = tid & 15, row_base = tid >> 4;
-  const int sq = seg >> 2, sv = seg & 3;
-  constexpr int kRowsPerThread = MB;  // MB*16 rows / 16 row groups
-  uint32_t aoffs[kRowsPerThread];
+  // loads: per row block, this lane's row (q = wave, rr = lane/16) offset
+  // plus its segment and piece; rows past the item read zeros
+  uint32_t aoffs[MB];
+  const int aseg = ((lane >> 2) - (lane >> 4)) & 3;  // the segment this lane loads
+  {
+    const uint32_t inrow = 256 * aseg + 16 * (lane & 3);
+    const int rr = lane >> 4;
 #pragma unroll
-  for (int i = 0; i < kRowsPerThread; ++i) {
-    const uint32_t o = lds_row[row_base + 16 * i];
-    aoffs[i] = o == kOob ? kOob : o + 256 * sq + 16 * sv;
+    for (int mb = 0; mb < MB; ++mb) {
+      const uint32_t o = lds_row[mb * 16 + wave + 4 * rr];
+      aoffs[mb] = o == kOob ? kOob : o + inrow;
+    }
   }
-  u32x4_t st[kRowsPerThread];  // native vectors: an array of uint4 structs stays in scratch
+  // operand reads: lane (r, kq) reads row r = q + 4rr, segment kq, piece i
+  const int rd_half = (r & 3) * kBlkHalves + 128 * (r >> 2) + 32 * ((kq + (r >> 2)) & 3);
   uint32_t sc_cur[NBB][2], sc_nxt[NBB][2];
   Frag<NBB> fb0, fb1;
-#define QMOE_LOAD_A_TILE(S, U, OK)                                                                 \
-do {                                                                                             \
-  _Pragma("unroll") for (int i = 0; i < kRowsPerThread; ++i) st[i] = __builtin_bit_cast(         \
-      u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rA, (OK) ? aoffs[i] + 64 * (U) : kOob,      \
-                                                     (S) * (kSuper * 2), 0));                    \
-} while (0)
-#define QMOE_STORE_A_TILE(BUF)                                                                     \
-do {                                                                                             \
-  _Pragma("unroll") for (int i = 0; i < kRowsPerThread; ++i)                                     \
-      *reinterpret_cast<u32x4_t*>(&lds_a[(BUF)][(row_base + 16 * i) * kAStride + seg * 8]) = st[i]; \
-} while (0)
-#define QMOE_COMPUTE(F, SC, U, BUF)                                                                \
-do {                                                                                             \
-  uint32_t s2_[NBB];                                                                             \
-  _Pragma("unroll") for (int b = 0; b < NBB; ++b) s2_[b] = scale_pair((SC)[b][0], (SC)[b][1], (U)); \
-  _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                \
-    half8_t bf[NBB];                                                                             \
-    _Pragma("unroll") for (int b = 0; b < NBB; ++b) bf[b] = dq8p(word((F).b[b], i), s2_[b]);     \
+  // fragments (mb, wave) of sub-step U of super-step S into buffer BUF;
+  // lanes whose group is past K (OK false) read zeros
+#define QMOE_LOAD_A_TILE(S, U, OK, BUF)                                                          \
+  do {                                                                                           \
     _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                                          \
-      if (mb < NMBC) {                                                                           \
-        const half8_t av =                                                                       \
-            *reinterpret_cast<const half8_t*>(&lds_a[(BUF)][(mb * 16 + r) * kAStride + 32 * kq + 8 * i]); \
-        _Pragma("unroll") for (int b = 0; b < NBB; ++b) acc[mb][b] = mfma16x16x32(av, bf[b], acc[mb][b]); \
+      if (mb < NMBC)                                                                             \
+        load_lds16(rA, &QMOE_LDS_A(BUF)[(mb * 4 + wave) * kBlkHalves], (OK) ? aoffs[mb] : kOob,   \
+                   (S) * (kSuper * 2) + 64 * (U));                                               \
+    }                                                                                            \
+  } while (0)
+#define QMOE_COMPUTE(F, SC, U, BUF)                                                              \
+  do {                                                                                           \
+    uint32_t s2_[NBB];                                                                           \
+    _Pragma("unroll") for (int b = 0; b < NBB; ++b) s2_[b] = scale_pair((SC)[b][0], (SC)[b][1], (U)); \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                              \
+      half8_t bf[NBB];                                                                           \
+      _Pragma("unroll") for (int b = 0; b < NBB; ++b) bf[b] = dq8p(word((F).b[b], i), s2_[b]);   \
+      _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                                        \
+        if (mb < NMBC) {                                                                         \
+          const half8_t av =                                                                     \
+              *reinterpret_cast<const half8_t*>(&QMOE_LDS_A(BUF)[mb * 4 * kBlkHalves + rd_half + 8 * i]); \
+          _Pragma("unroll") for (int b = 0; b < NBB; ++b) acc[mb][b] = mfma16x16x32(av, bf[b], acc[mb][b]); \
+        }                                                                                        \
       }                                                                                          \
     }                                                                                            \
-  }                                                                                              \
-} while (0)
-  // One sub-step with one barrier: prefetch the next sub-step's weights
-  // and activation tile (clamped, unconditional), compute this sub-step
-  // from LDS buffer BUF, then write the next tile (loaded during the
-  // compute) to the other buffer and meet the barrier that publishes it
-  // and frees BUF for the tile after next.
-#define QMOE_SUBSTEP(S, U, FCUR, FNEXT, SN, UN, BUF)                                               \
-do {                                                                                             \
-  load_b((SN), (UN), FNEXT, true);                                                               \
-  QMOE_LOAD_A_TILE((SN), (UN), true);                                                            \
-  QMOE_COMPUTE(FCUR, sc_cur, (U), (BUF));                                                        \
-  QMOE_STORE_A_TILE((BUF) ^ 1);                                                                  \
-  __syncthreads();                                                                               \
-} while (0)
+  } while (0)
+  // One sub-step with one barrier: start the next sub-step's weight loads
+  // and its activation tile (into the other buffer), compute this sub-step
+  // from buffer BUF, then meet the barrier, which waits for the loads
+  // (the direct LDS writes count as outstanding loads) and so publishes
+  // the next tile and frees BUF for the tile after next.
+#define QMOE_SUBSTEP(S, U, FCUR, FNEXT, SN, UN, BUF)                                             \
+  do {                                                                                           \
+    load_b((SN), (UN), FNEXT, true);                                                             \
+    QMOE_LOAD_A_TILE((SN), (UN), true, (BUF) ^ 1);                                               \
+    __builtin_amdgcn_sched_barrier(0); /* keep the loads ahead of the compute */                 \
+    QMOE_COMPUTE(FCUR, sc_cur, (U), (BUF));                                                      \
+    __builtin_amdgcn_s_waitcnt(0);                                                               \
+    __syncthreads();                                                                             \
+  } while (0)
   // The row blocks that hold routed rows are computed without a branch per
   // block: the loop is instantiated for 2, 4, 6 and 8 blocks and the
   // item's count rounds up to the next of these (blocks past the item's
@@ -564,8 +586,8 @@ do {                                                                            
     if (n > 0) {
       load_sc(S_begin, sc_cur, true);
       load_b(S_begin, 0, fb0, true);
-      QMOE_LOAD_A_TILE(S_begin, 0, true);
-      QMOE_STORE_A_TILE(0);
+      QMOE_LOAD_A_TILE(S_begin, 0, true, 0);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       for (int S = S_begin; S < S_end_full; ++S) {
         const int Sn = min(S + 1, S_end_full - 1);
@@ -586,11 +608,11 @@ do {                                                                            
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const bool okb = nss_full * 16 + 4 * kq + u < ngroups;
-        const bool oka = nss_full * 16 + 4 * sq + u < ngroups;
+        const bool oka = nss_full * 16 + 4 * aseg + u < ngroups;
+        __syncthreads();  // every wave is done reading buffer 0
         load_b(nss_full, u, fb0, okb);
-        QMOE_LOAD_A_TILE(nss_full, u, oka);
-        __syncthreads();
-        QMOE_STORE_A_TILE(0);
+        QMOE_LOAD_A_TILE(nss_full, u, oka, 0);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         QMOE_COMPUTE(fb0, sc_cur, u, 0);
       }
@@ -602,8 +624,8 @@ do {                                                                            
   else kloop(std::integral_constant<int, MB>{});
 #undef QMOE_SUBSTEP
 #undef QMOE_COMPUTE
-#undef QMOE_STORE_A_TILE
 #undef QMOE_LOAD_A_TILE
+#undef QMOE_LDS_A
 
   // ---- epilogue: lane holds rows mb*16 + 4*kq + i of column r of each block
 #pragma unroll
