@@ -41,16 +41,15 @@ constexpr int kKStep = 128;     // inputs per K-step of a wave (4 lane groups x 
 
 // Shape of the 128-row MFMA tiles: MB row blocks of 16 per work item, NBW
 // 16-column output blocks per wave (gate+up: each with its up block).
-#ifndef QMOE_PRE_MB
-#define QMOE_PRE_MB 8
-#endif
-#ifndef QMOE_PRE_GU_NBW
-#define QMOE_PRE_GU_NBW 1
-#endif
-#ifndef QMOE_PRE_DN_NBW
-#define QMOE_PRE_DN_NBW 2
-#endif
-constexpr int kPrefillRows = QMOE_PRE_MB * 16;
+// 128-row tile shapes, measured on MI355X over 256..4096 tokens of the
+// 384-expert 7168/2048 layer.  Gate+up: blocks of 4 waves, each one 16-column
+// block of gate and its up block.  Down: blocks of 8 waves, each one
+// 16-column block; at under 128 registers four waves share a SIMD, which
+// hides the activation-tile latency better than wider waves do.
+constexpr int kTileMB = 8;  // row blocks of 16 per tile
+constexpr int kGuWN = 4, kGuNBW = 1, kGuWPE = 2;
+constexpr int kDnWN = 8, kDnNBW = 1, kDnWPE = 4;
+constexpr int kPrefillRows = kTileMB * 16;
 
 // ---------------------------------------------------------------- routing
 
@@ -382,11 +381,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, _Float16* lds, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
+// Wait until at most N vector-memory loads of this wave are outstanding
+// (expcnt and lgkmcnt left free; the gfx9 s_waitcnt field layout).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 constexpr uint32_t kOob = 0x7FFFFF00u;  // a lane offset past any buffer: its loads read 0
 constexpr int kSuper = 4 * kKStep;     // inputs per super-step (16 groups)
 
 // 128-row tiles.  One work item = (expert, up to MB*16 routed rows) x (an N
-// range).  A block has 4 waves along N, each NBW blocks of 16 output
+// range).  A block has WN (4 or 8) waves along N, each NBW blocks of 16 output
 // columns (gate+up: each with its up block).
 //
 // K is walked in super-steps of 512 inputs (16 groups of 32).  Lane group kq
@@ -399,9 +405,10 @@ constexpr int kSuper = 4 * kKStep;     // inputs per super-step (16 groups)
 // The block stages each sub-step's activation tile in LDS.
 // Loads are buffer loads with a fixed per-lane offset and a scalar
 // per-step offset (no vector address arithmetic); inputs past K read zeros.
-template <int MB, int NBW, bool GATEUP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void gemm_kernel(GemmArgs g) {
-  constexpr int WN = 4, WK = 1;
+template <int MB, int WN, int NBW, bool GATEUP>
+__global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP ? kGuWPE : kDnWPE))) void gemm_kernel(GemmArgs g) {
+  constexpr int WK = 1;
+  static_assert(WN == 4 || WN == 8, "4 or 8 waves along N");
   static_assert(MB > 1, "row tiles of at least 32 rows");
   constexpr int NBB = GATEUP ? 2 * NBW : NBW;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -436,21 +443,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const __amdgpu_buffer_rsrc_t rS = buffer_rsrc(sbase, (uint32_t)g.Nw * KG * 2);
   const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(g.a, g.a_bytes);
 
-  // byte offsets of this lane's code chunk and scale quad, per B block
-  uint32_t boff[NBB], soff[NBB];
+  // offsets of this lane's code chunk and scale quad within a 16-row B
+  // block (vector), and each B block's first weight row (wave-uniform, so
+  // it rides in the scalar offset; the lane part alone is bounds-checked
+  // and every in-range lane stays inside the weights)
+  const uint32_t bl = (uint32_t)r * K2 + 64 * kq, sl = (uint32_t)r * KG * 2 + 8 * kq;
+  uint32_t brow[NBB];
   int col0[NBW];
 #pragma unroll
   for (int c = 0; c < NBW; ++c) {
     col0[c] = ((nb * WN + wn) * NBW + c) * 16;
-    const uint32_t n = col0[c] < g.N ? col0[c] + r : 0;
+    const uint32_t n0 = col0[c] < g.N ? col0[c] : 0;
     if (GATEUP) {
-      boff[2 * c] = n * K2 + 64 * kq;
-      soff[2 * c] = n * KG * 2 + 8 * kq;
-      boff[2 * c + 1] = (g.N + n) * K2 + 64 * kq;
-      soff[2 * c + 1] = (g.N + n) * KG * 2 + 8 * kq;
+      brow[2 * c] = n0;
+      brow[2 * c + 1] = g.N + n0;
     } else {
-      boff[c] = n * K2 + 64 * kq;
-      soff[c] = n * KG * 2 + 8 * kq;
+      brow[c] = n0;
     }
   }
 
@@ -474,13 +482,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int b = 0; b < NBB; ++b)
       f.b[b] = __builtin_bit_cast(
-          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rB, ok ? boff[b] + 16 * u : kOob, S * (kSuper / 2), 0));
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rB, ok ? bl + 16 * u : kOob, S * (kSuper / 2) + brow[b] * K2, 0));
   };
   // the four scales of super-step S, as two dwords per B block
   auto load_sc = [&](int S, uint32_t (&sc)[NBB][2], bool ok) __attribute__((always_inline)) {
 #pragma unroll
     for (int b = 0; b < NBB; ++b) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rS, ok ? soff[b] : kOob, S * 32, 0);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rS, ok ? sl : kOob, S * 32 + brow[b] * KG * 2, 0);
       sc[b][0] = v[0];
       sc[b][1] = v[1];
     }
@@ -508,7 +516,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // bytes.  Blocks are 1040 bytes apart and segments rotate by row, so the
   // 16 lanes that read one MFMA operand column (rows 0..15, one segment,
   // one 16-byte piece) hit 16 distinct 16-byte bank groups.  Wave w loads
-  // block q = w of every row block.
+  // block q = w mod 4 of every (WN/4)-th row block, starting at w / 4.
   static_assert(WK == 1, "128-row tiles split N across waves, not K");
   constexpr int kBlkHalves = 520;  // 1040-byte LDS block
   // two buffers as separate arrays, so that the compiler can tell loads
@@ -517,33 +525,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   __shared__ __attribute__((aligned(16))) _Float16 lds_a1[MB * 4 * kBlkHalves];
 #define QMOE_LDS_A(BUF) ((BUF) ? lds_a1 : lds_a0)
   __shared__ uint32_t lds_row[MB * 16];
-  for (int m = tid; m < MB * 16; m += kThreads) lds_row[m] = m < nr ? a_off_of(m) : kOob;
+  for (int m = tid; m < MB * 16; m += 64 * WN) lds_row[m] = m < nr ? a_off_of(m) : kOob;
   __syncthreads();
-  // loads: per row block, this lane's row (q = wave, rr = lane/16) offset
-  // plus its segment and piece; rows past the item read zeros
-  uint32_t aoffs[MB];
+  // loads: per row block this wave loads, this lane's row (q = wave mod 4,
+  // rr = lane/16) offset plus its segment and piece; rows past the item
+  // read zeros
+  constexpr int MBS = WN / 4, NA = MB / MBS;
+  static_assert(MB % MBS == 0, "row blocks split evenly over the waves");
+  const int aq = wave & 3, amb0 = wave >> 2;
+  uint32_t aoffs[NA];
   const int aseg = ((lane >> 2) - (lane >> 4)) & 3;  // the segment this lane loads
   {
     const uint32_t inrow = 256 * aseg + 16 * (lane & 3);
     const int rr = lane >> 4;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const uint32_t o = lds_row[mb * 16 + wave + 4 * rr];
-      aoffs[mb] = o == kOob ? kOob : o + inrow;
+    for (int t = 0; t < NA; ++t) {
+      const uint32_t o = lds_row[(amb0 + MBS * t) * 16 + aq + 4 * rr];
+      aoffs[t] = o == kOob ? kOob : o + inrow;
     }
   }
   // operand reads: lane (r, kq) reads row r = q + 4rr, segment kq, piece i
   const int rd_half = (r & 3) * kBlkHalves + 128 * (r >> 2) + 32 * ((kq + (r >> 2)) & 3);
   uint32_t sc_cur[NBB][2], sc_nxt[NBB][2];
-  Frag<NBB> fb0, fb1;
-  // fragments (mb, wave) of sub-step U of super-step S into buffer BUF;
-  // lanes whose group is past K (OK false) read zeros
+  Frag<NBB> fb0, fb1, fb2, fb3;  // the weights of sub-steps 0..3
+  // this wave's blocks of sub-step U of super-step S into buffer BUF, for
+  // the NMBC row blocks in use (NMBC is a multiple of WN/4); lanes whose
+  // group is past K (OK false) read zeros
 #define QMOE_LOAD_A_TILE(S, U, OK, BUF)                                                          \
   do {                                                                                           \
-    _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                                          \
-      if (mb < NMBC)                                                                             \
-        load_lds16(rA, &QMOE_LDS_A(BUF)[(mb * 4 + wave) * kBlkHalves], (OK) ? aoffs[mb] : kOob,   \
-                   (S) * (kSuper * 2) + 64 * (U));                                               \
+    _Pragma("unroll") for (int t = 0; t < NA; ++t) {                                             \
+      if (t < NMBC / MBS)                                                                        \
+        load_lds16(rA, &QMOE_LDS_A(BUF)[((amb0 + MBS * t) * 4 + aq) * kBlkHalves],                \
+                   (OK) ? aoffs[t] : kOob, (S) * (kSuper * 2) + 64 * (U));                       \
     }                                                                                            \
   } while (0)
 #define QMOE_COMPUTE(F, SC, U, BUF)                                                              \
@@ -562,18 +575,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }                                                                                          \
     }                                                                                            \
   } while (0)
-  // One sub-step with one barrier: start the next sub-step's weight loads
-  // and its activation tile (into the other buffer), compute this sub-step
-  // from buffer BUF, then meet the barrier, which waits for the loads
-  // (the direct LDS writes count as outstanding loads) and so publishes
-  // the next tile and frees BUF for the tile after next.
-#define QMOE_SUBSTEP(S, U, FCUR, FNEXT, SN, UN, BUF)                                             \
+  // One sub-step with one barrier: start the next sub-step's activation
+  // tile (into the other buffer) and then the weights of the sub-step after
+  // next (into FNN), compute this sub-step from fragment set FCUR and
+  // buffer BUF, then wait until at most the NBB weight loads just issued
+  // are outstanding (loads complete in order, so the tile, written straight
+  // into LDS, and the next sub-step's weights are in) and meet the barrier
+  // that publishes the tile and frees BUF.  Weights get two sub-steps to
+  // arrive, the activation tile one.
+#define QMOE_SUBSTEP(U, FCUR, SA, UA, SB, UB, FNN, BUF)                                         \
   do {                                                                                           \
-    load_b((SN), (UN), FNEXT, true);                                                             \
-    QMOE_LOAD_A_TILE((SN), (UN), true, (BUF) ^ 1);                                               \
+    QMOE_LOAD_A_TILE((SA), (UA), true, (BUF) ^ 1);                                               \
+    load_b((SB), (UB), FNN, true);                                                               \
     __builtin_amdgcn_sched_barrier(0); /* keep the loads ahead of the compute */                 \
     QMOE_COMPUTE(FCUR, sc_cur, (U), (BUF));                                                      \
-    __builtin_amdgcn_s_waitcnt(0);                                                               \
+    wait_vmcnt<NBB>();                                                                           \
     __syncthreads();                                                                             \
   } while (0)
   // The row blocks that hold routed rows are computed without a branch per
@@ -587,15 +603,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       load_sc(S_begin, sc_cur, true);
       load_b(S_begin, 0, fb0, true);
       QMOE_LOAD_A_TILE(S_begin, 0, true, 0);
-      __builtin_amdgcn_s_waitcnt(0);
+      load_b(S_begin, 1, fb1, true);
+      wait_vmcnt<NBB>();
       __syncthreads();
       for (int S = S_begin; S < S_end_full; ++S) {
+        // the next super-step, clamped: the last one reloads itself
         const int Sn = min(S + 1, S_end_full - 1);
         load_sc(Sn, sc_nxt, true);
-        QMOE_SUBSTEP(S, 0, fb0, fb1, S, 1, 0);
-        QMOE_SUBSTEP(S, 1, fb1, fb0, S, 2, 1);
-        QMOE_SUBSTEP(S, 2, fb0, fb1, S, 3, 0);
-        QMOE_SUBSTEP(S, 3, fb1, fb0, Sn, 0, 1);
+        QMOE_SUBSTEP(0, fb0, S, 1, S, 2, fb2, 0);
+        QMOE_SUBSTEP(1, fb1, S, 2, S, 3, fb3, 1);
+        QMOE_SUBSTEP(2, fb2, S, 3, Sn, 0, fb0, 0);
+        QMOE_SUBSTEP(3, fb3, Sn, 0, Sn, 1, fb1, 1);
 #pragma unroll
         for (int b = 0; b < NBB; ++b) {
           sc_cur[b][0] = sc_nxt[b][0];
@@ -1242,17 +1260,17 @@ void fill_gemm_args(const qmoe_layer* L, int64_t M, void* ws, const Layout& lay,
   }
 }
 
-template <int MB, int NBW, bool GATEUP>
+template <int MB, int WN, int NBW, bool GATEUP>
 int launch_gemm(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t st) {
   GemmArgs g;
   fill_gemm_args<GATEUP>(L, M, ws, lay, g);
   const int E = L->d.E;
   const int bmc = MB * 16;
   g.max_items = (int)max_items_for(lay.T, M, lay.S, E, bmc);
-  g.nblk = (int)ceil_div(g.N, 4 * NBW * 16);
+  g.nblk = (int)ceil_div(g.N, WN * NBW * 16);
   const int64_t blocks = 8 * (int64_t)g.nblk * ceil_div(g.max_items, 8);
   if (blocks > 0x7FFFFFFF) return fail(QMOE_ERR_UNSUPPORTED, "grid too large");
-  gemm_kernel<MB, NBW, GATEUP><<<dim3((unsigned)blocks), kThreads, 0, st>>>(g);
+  gemm_kernel<MB, WN, NBW, GATEUP><<<dim3((unsigned)blocks), 64 * WN, 0, st>>>(g);
   L->gemm_launches++;
   return check_launch(L, GATEUP ? "gate_up gemm" : "down gemm");
 }
@@ -1288,12 +1306,12 @@ int do_gate_up(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_
     return launch_gemv_split<true>(L, M, ws, lay, st);
   }
   L->prefill_tiles++;
-  return launch_gemm<QMOE_PRE_MB, QMOE_PRE_GU_NBW, true>(L, M, ws, lay, st);
+  return launch_gemm<kTileMB, kGuWN, kGuNBW, true>(L, M, ws, lay, st);
 }
 
 int do_down(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t st) {
   if (regime_of(L, M) == kGemv) return launch_gemv_split<false>(L, M, ws, lay, st);
-  return launch_gemm<QMOE_PRE_MB, QMOE_PRE_DN_NBW, false>(L, M, ws, lay, st);
+  return launch_gemm<kTileMB, kDnWN, kDnNBW, false>(L, M, ws, lay, st);
 }
 
 int do_combine(qmoe_layer* L, int64_t M, void* out, void* ws, const Layout& lay, hipStream_t st) {
