@@ -362,11 +362,31 @@ struct Frag {
 
 __device__ __forceinline__ uint32_t word(const u32x4_t& v, int i) { return v[i]; }
 
-// The fp16 scale of sub-step u from a lane's 4 scales (2 dwords), duplicated
-// into both halves of a dword: one byte permute.
-__device__ __forceinline__ uint32_t scale_pair(uint32_t lo, uint32_t hi, int u) {
-  const uint32_t sel = u == 0 ? 0x01000100u : u == 1 ? 0x03020302u : u == 2 ? 0x05040504u : 0x07060706u;
-  return __builtin_amdgcn_perm(hi, lo, sel);
+// Lane swaps between the 16-lane rows of a wave: (rows of a, rows of b)
+// become (a0 b0 a2 b2, a1 b1 a3 b3) for 16 and (a0 a1 b0 b1, a2 a3 b2 b3)
+// for 32.
+__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
+  const auto v = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  a = v[0];
+  b = v[1];
+}
+__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
+  const auto v = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  a = v[0];
+  b = v[1];
+}
+// Lane (r, kq) holds the fp16 scales of groups 4kq..4kq+3 of its weight row
+// (2 dwords); afterwards d[u] holds the scale of group 4u + kq, duplicated
+// into both halves of the dword (a 4x4 transpose over the row's 4 lanes).
+__device__ __forceinline__ void transpose_scales(uint32_t lo, uint32_t hi, uint32_t (&d)[4]) {
+  d[0] = __builtin_amdgcn_perm(hi, lo, 0x01000100u);
+  d[1] = __builtin_amdgcn_perm(hi, lo, 0x03020302u);
+  d[2] = __builtin_amdgcn_perm(hi, lo, 0x05040504u);
+  d[3] = __builtin_amdgcn_perm(hi, lo, 0x07060706u);
+  swap16(d[0], d[1]);
+  swap16(d[2], d[3]);
+  swap32(d[0], d[2]);
+  swap32(d[1], d[3]);
 }
 
 // Raw buffer resource over [base, base + bytes): loads take a 32-bit per-lane
@@ -395,13 +415,15 @@ constexpr int kSuper = 4 * kKStep;     // inputs per super-step (16 groups)
 // range).  A block has WN (4 or 8) waves along N, each NBW blocks of 16 output
 // columns (gate+up: each with its up block).
 //
-// K is walked in super-steps of 512 inputs (16 groups of 32).  Lane group kq
-// (= lane/16) owns groups 4kq..4kq+3 of each super-step and decodes one per
-// sub-step u: the 16 code bytes at 64kq + 16u of the row's 256-byte chunk
-// (so four sub-steps read every byte of the chunk) and the group's scale,
-// all four scales coming from one 8-byte load per super-step.  The MFMA
-// k-slot order is free as long as the activations follow it, so the
-// activation fragment of sub-step u, MFMA i is inputs (4kq+u)*32 + 8i .. +8.
+// K is walked in super-steps of 512 inputs (16 groups of 32).  In sub-step
+// u lane group kq (= lane/16) decodes group 4u + kq: the 16 code bytes at
+// 64u + 16kq of the row's 256-byte chunk, so the four lanes of a row read
+// 64 contiguous bytes.  The scales come from one 8-byte load per row and
+// super-step (lane kq: groups 4kq..4kq+3) and a transpose across the row's
+// four lanes.  The MFMA k-slot order is free as long as the activations
+// follow it, so the activation fragment of sub-step u, MFMA i is inputs
+// (4u+kq)*32 + 8i .. +8: in sub-step u the tile covers 256 contiguous
+// bytes of each activation row.
 // The block stages each sub-step's activation tile in LDS.
 // Loads are buffer loads with a fixed per-lane offset and a scalar
 // per-step offset (no vector address arithmetic); inputs past K read zeros.
@@ -447,7 +469,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   // block (vector), and each B block's first weight row (wave-uniform, so
   // it rides in the scalar offset; the lane part alone is bounds-checked
   // and every in-range lane stays inside the weights)
-  const uint32_t bl = (uint32_t)r * K2 + 64 * kq, sl = (uint32_t)r * KG * 2 + 8 * kq;
+  const uint32_t bl = (uint32_t)r * K2 + 16 * kq, sl = (uint32_t)r * KG * 2 + 8 * kq;
   uint32_t brow[NBB];
   int col0[NBW];
 #pragma unroll
@@ -482,7 +504,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
 #pragma unroll
     for (int b = 0; b < NBB; ++b)
       f.b[b] = __builtin_bit_cast(
-          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rB, ok ? bl + 16 * u : kOob, S * (kSuper / 2) + brow[b] * K2, 0));
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rB, ok ? bl + 64 * u : kOob, S * (kSuper / 2) + brow[b] * K2, 0));
   };
   // the four scales of super-step S, as two dwords per B block
   auto load_sc = [&](int S, uint32_t (&sc)[NBB][2], bool ok) __attribute__((always_inline)) {
@@ -509,7 +531,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   // ---------------- prefill tiles: the activation tile of each sub-step
   // (MB*16 rows x 128 inputs) staged in LDS by direct global->LDS loads.
   // In sub-step u a row's inputs are four 64-byte segments (segment kq =
-  // bytes 256kq + 64u of the row's super-step, the inputs of group 4kq+u).
+  // bytes 256u + 64kq of the row's super-step, the inputs of group 4u+kq).
   // One load instruction fills one LDS block of 1 KiB: rows q, q+4, q+8,
   // q+12 of a row block (lane l = 16rr + 4x + j takes byte 16j of segment
   // (x - rr) mod 4 of row q + 4rr), so every four lanes read 64 contiguous
@@ -536,7 +558,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   uint32_t aoffs[NA];
   const int aseg = ((lane >> 2) - (lane >> 4)) & 3;  // the segment this lane loads
   {
-    const uint32_t inrow = 256 * aseg + 16 * (lane & 3);
+    const uint32_t inrow = 64 * aseg + 16 * (lane & 3);
     const int rr = lane >> 4;
 #pragma unroll
     for (int t = 0; t < NA; ++t) {
@@ -546,8 +568,12 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   }
   // operand reads: lane (r, kq) reads row r = q + 4rr, segment kq, piece i
   const int rd_half = (r & 3) * kBlkHalves + 128 * (r >> 2) + 32 * ((kq + (r >> 2)) & 3);
-  uint32_t sc_cur[NBB][2], sc_nxt[NBB][2];
+  uint32_t sc_cur[NBB][4], sc_nxt[NBB][2];  // this super-step's scales by sub-step; the next one's, raw
   Frag<NBB> fb0, fb1, fb2, fb3;  // the weights of sub-steps 0..3
+  auto promote_scales = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int b = 0; b < NBB; ++b) transpose_scales(sc_nxt[b][0], sc_nxt[b][1], sc_cur[b]);
+  };
   // this wave's blocks of sub-step U of super-step S into buffer BUF, for
   // the NMBC row blocks in use (NMBC is a multiple of WN/4); lanes whose
   // group is past K (OK false) read zeros
@@ -556,13 +582,13 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
     _Pragma("unroll") for (int t = 0; t < NA; ++t) {                                             \
       if (t < NMBC / MBS)                                                                        \
         load_lds16(rA, &QMOE_LDS_A(BUF)[((amb0 + MBS * t) * 4 + aq) * kBlkHalves],                \
-                   (OK) ? aoffs[t] : kOob, (S) * (kSuper * 2) + 64 * (U));                       \
+                   (OK) ? aoffs[t] : kOob, (S) * (kSuper * 2) + 256 * (U));                      \
     }                                                                                            \
   } while (0)
 #define QMOE_COMPUTE(F, SC, U, BUF)                                                              \
   do {                                                                                           \
     uint32_t s2_[NBB];                                                                           \
-    _Pragma("unroll") for (int b = 0; b < NBB; ++b) s2_[b] = scale_pair((SC)[b][0], (SC)[b][1], (U)); \
+    _Pragma("unroll") for (int b = 0; b < NBB; ++b) s2_[b] = (SC)[b][(U)];                   \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                              \
       half8_t bf[NBB];                                                                           \
       _Pragma("unroll") for (int b = 0; b < NBB; ++b) bf[b] = dq8p(word((F).b[b], i), s2_[b]);   \
@@ -600,12 +626,13 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
     constexpr int NMBC = decltype(nmbc_tag)::value;
     const int n = S_end_full - S_begin;
     if (n > 0) {
-      load_sc(S_begin, sc_cur, true);
+      load_sc(S_begin, sc_nxt, true);
       load_b(S_begin, 0, fb0, true);
       QMOE_LOAD_A_TILE(S_begin, 0, true, 0);
       load_b(S_begin, 1, fb1, true);
       wait_vmcnt<NBB>();
       __syncthreads();
+      promote_scales();
       for (int S = S_begin; S < S_end_full; ++S) {
         // the next super-step, clamped: the last one reloads itself
         const int Sn = min(S + 1, S_end_full - 1);
@@ -614,19 +641,16 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
         QMOE_SUBSTEP(1, fb1, S, 2, S, 3, fb3, 1);
         QMOE_SUBSTEP(2, fb2, S, 3, Sn, 0, fb0, 0);
         QMOE_SUBSTEP(3, fb3, Sn, 0, Sn, 1, fb1, 1);
-#pragma unroll
-        for (int b = 0; b < NBB; ++b) {
-          sc_cur[b][0] = sc_nxt[b][0];
-          sc_cur[b][1] = sc_nxt[b][1];
-        }
+        promote_scales();
       }
     }
     if (has_tail) {  // the partial super-step: groups past K read zeros
-      load_sc(nss_full, sc_cur, true);
+      load_sc(nss_full, sc_nxt, true);
+      promote_scales();
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const bool okb = nss_full * 16 + 4 * kq + u < ngroups;
-        const bool oka = nss_full * 16 + 4 * aseg + u < ngroups;
+        const bool okb = nss_full * 16 + 4 * u + kq < ngroups;
+        const bool oka = nss_full * 16 + 4 * u + aseg < ngroups;
         __syncthreads();  // every wave is done reading buffer 0
         load_b(nss_full, u, fb0, okb);
         QMOE_LOAD_A_TILE(nss_full, u, oka, 0);
@@ -705,20 +729,18 @@ constexpr int kGemvMaxK = 15360;  // largest K the GEMV stages (two rows in 64 K
 // LDS bytes of a block: the activation rows
 __host__ __device__ constexpr size_t gemv_lds_bytes(int K) { return (size_t)kGemvRows * K * 2; }
 
-// lane swaps between the 16-lane rows of a wave: (rows of a, rows of b)
-// become (a0 b0 a2 b2, a1 b1 a3 b3) for 16 and (a0 a1 b0 b1, a2 a3 b2 b3)
-// for 32
+// the row swaps above on fp32 values
 __device__ __forceinline__ void swap16(float& a, float& b) {
-  const auto v = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
-                                                  false, false);
-  a = __builtin_bit_cast(float, (uint32_t)v[0]);
-  b = __builtin_bit_cast(float, (uint32_t)v[1]);
+  uint32_t x = __builtin_bit_cast(uint32_t, a), y = __builtin_bit_cast(uint32_t, b);
+  swap16(x, y);
+  a = __builtin_bit_cast(float, x);
+  b = __builtin_bit_cast(float, y);
 }
 __device__ __forceinline__ void swap32(float& a, float& b) {
-  const auto v = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
-                                                  false, false);
-  a = __builtin_bit_cast(float, (uint32_t)v[0]);
-  b = __builtin_bit_cast(float, (uint32_t)v[1]);
+  uint32_t x = __builtin_bit_cast(uint32_t, a), y = __builtin_bit_cast(uint32_t, b);
+  swap32(x, y);
+  a = __builtin_bit_cast(float, x);
+  b = __builtin_bit_cast(float, y);
 }
 
 #ifndef QMOE_GEMV_WPE
