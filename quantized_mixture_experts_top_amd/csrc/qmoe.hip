@@ -42,12 +42,13 @@ constexpr int kKStep = 128;     // inputs per K-step of a wave (4 lane groups x 
 // Shape of the 128-row MFMA tiles: MB row blocks of 16 per work item, NBW
 // 16-column output blocks per wave (gate+up: each with its up block).
 // 128-row tile shapes, measured on MI355X over 256..4096 tokens of the
-// 384-expert 7168/2048 layer.  Gate+up: blocks of 4 waves, each one 16-column
-// block of gate and its up block.  Down: blocks of 8 waves, each one
-// 16-column block; at under 128 registers four waves share a SIMD, which
-// hides the activation-tile latency better than wider waves do.
+// 384-expert 7168/2048 layer.  Gate+up: blocks of 4 waves, each two 16-column
+// blocks of gate and their up blocks (64 weight rows per wave, so each
+// activation fragment read from LDS feeds 4 MFMAs).  Down: blocks of 8
+// waves, each one 16-column block; at under 128 registers four waves share
+// a SIMD, which hides the activation-tile latency better than wider waves.
 constexpr int kTileMB = 8;  // row blocks of 16 per tile
-constexpr int kGuWN = 4, kGuNBW = 1, kGuWPE = 2;
+constexpr int kGuWN = 4, kGuNBW = 2, kGuWPE = 2;
 constexpr int kDnWN = 8, kDnNBW = 1, kDnWPE = 4;
 constexpr int kPrefillRows = kTileMB * 16;
 
@@ -599,6 +600,9 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
           _Pragma("unroll") for (int b = 0; b < NBB; ++b) acc[mb][b] = mfma16x16x32(av, bf[b], acc[mb][b]); \
         }                                                                                        \
       }                                                                                          \
+      /* gate+up: one k-slice at a time, which keeps its 4 weight blocks */                      \
+      /* and 128 accumulators within 256 registers */                                            \
+      if (GATEUP) __builtin_amdgcn_sched_barrier(0);                                             \
     }                                                                                            \
   } while (0)
   // One sub-step with one barrier: start the next sub-step's activation
