@@ -727,7 +727,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
 //
 // The item's activation rows are staged in LDS once per block.
 constexpr int kGemvRows = 2;
-constexpr int kGemvMaxRowsPerExpert = 4;  // GEMV while M*top_k <= 4E
+constexpr int kGemvMaxRowsPer4Experts = 7;  // GEMV while 4*M*top_k <= 7E
 constexpr int kGemvMaxK = 15360;  // largest K the GEMV stages (two rows in 64 KiB of LDS)
 
 // LDS bytes of a block: the activation rows
@@ -1142,17 +1142,17 @@ Layout make_layout(const qmoe_layer* L, int64_t M) {
 }
 
 // Kernel regime of a call, from the average routed rows per expert: the
-// dot-product GEMV (items of <= 2 rows) up to 4 rows on average, 128-row
+// dot-product GEMV (items of <= 2 rows) up to 1.75 rows on average, 128-row
 // MFMA tiles above.  An expert with more than 2 rows takes several GEMV
-// items, each streaming its weights; measured on MI355X (E=384, H=7168,
-// I=2048, top-8) that still beats the MFMA tiles up to about 4 rows per
-// expert (M=192), and loses beyond (M=256).  The GEMV stages two activation
-// rows in LDS, so it is used while they fit in 64 KiB.
+// items, each streaming its weights.  Measured on MI355X (E=384, H=7168,
+// I=2048, top-8): the GEMV is ahead at 1.33 rows per expert (M=64, 7%),
+// the tiles at 2 (M=96, 3%) and 4 (M=192, 30%).  The GEMV stages two
+// activation rows in LDS, so it is used while they fit in 64 KiB.
 enum Regime { kGemv, kPrefill };
 static_assert(gemv_lds_bytes(kGemvMaxK) <= 65536, "GEMV rows fit in 64 KiB of LDS");
 Regime regime_of(const qmoe_layer* L, int64_t M) {
   const int64_t T = M * (int64_t)L->d.top_k, E = L->d.E;
-  if (T <= kGemvMaxRowsPerExpert * E && L->d.H <= kGemvMaxK && L->d.I <= kGemvMaxK) return kGemv;
+  if (4 * T <= kGemvMaxRowsPer4Experts * E && L->d.H <= kGemvMaxK && L->d.I <= kGemvMaxK) return kGemv;
   return kPrefill;
 }
 int rows_per_item(Regime rg) { return rg == kGemv ? kGemvRows : kPrefillRows; }

@@ -117,8 +117,9 @@ def test_routing_repeatable_and_workspace_reuse():
 
 FWD_CASES = [
     # E, H, I, k, M, shared   (dot-product GEMV items of <= 2 rows when
-    #                          M*k <= 4E, else 128-row MFMA tiles)
-    (8, 256, 128, 2, 16, False),     # the tiny configuration (GEMV, several items per expert)
+    #                          4*M*k <= 7E, else 128-row MFMA tiles)
+    (8, 256, 128, 2, 16, False),     # the tiny configuration (tiles)
+    (8, 256, 128, 2, 7, False),      # GEMV, several items per expert
     (8, 256, 128, 2, 1, False),      # GEMV, one row
     (16, 640, 384, 2, 37, False),    # tiles: K = 1 super-step + a partial one / a partial one
     (64, 128, 128, 2, 9, True),      # GEMV with a shared expert
@@ -130,10 +131,10 @@ FWD_CASES = [
     (64, 1152, 640, 2, 20, False),   # GEMV: whole + partial super-steps in both GEMMs
     (32, 2048, 1536, 4, 8, True),    # GEMV: 2-row items, shared expert
     (16, 256, 128, 8, 2, False),     # GEMV: top_k = 8, partial super-steps only
-    (8, 512, 256, 2, 12, True),      # GEMV: experts with several items, shared expert
+    (8, 512, 256, 2, 7, True),       # GEMV: experts with several items, shared expert
     (8, 256, 128, 2, 40, False),     # tiles on the tiny shape (2 row blocks)
     (16, 640, 384, 2, 72, True),     # tiles with a shared expert, partial super-steps
-    (1, 256, 128, 1, 3, False),      # one expert, GEMV (a plain quantized SwiGLU MLP)
+    (1, 256, 128, 1, 1, False),      # one expert, GEMV (a plain quantized SwiGLU MLP)
     (1, 256, 128, 1, 5, False),      # one expert, tiles
     (32, 256, 128, 32, 3, False),    # top_k = 32 = E (the largest top_k)
     (1024, 128, 128, 8, 20, True),   # 1024 experts (the most), shared expert
@@ -162,8 +163,8 @@ def test_forward_parity(E, H, I, k, M, shared):
     assert err <= REL_TOL
 
 
-@pytest.mark.parametrize("E,H,I,k,M,shared", [FWD_CASES[2], FWD_CASES[4], FWD_CASES[5], FWD_CASES[9],
-                                               FWD_CASES[10], FWD_CASES[12], FWD_CASES[14]])
+@pytest.mark.parametrize("E,H,I,k,M,shared", [FWD_CASES[3], FWD_CASES[5], FWD_CASES[6], FWD_CASES[10],
+                                               FWD_CASES[11], FWD_CASES[13], FWD_CASES[15]])
 def test_steps_match_oracle_intermediates(E, H, I, k, M, shared):
     """h = SiLU(gate)*up after the gate+up step and w*y after the down step,
     per routed slot, against the oracle's float64 values."""
@@ -194,7 +195,7 @@ def test_steps_match_oracle_intermediates(E, H, I, k, M, shared):
 
 @pytest.mark.parametrize("split", ["2", "4"])
 @pytest.mark.parametrize("case", [(64, 1152, 640, 2, 20, False), (32, 2048, 1536, 4, 8, True),
-                                  (8, 512, 256, 2, 12, True)])
+                                  (8, 512, 256, 2, 7, True)])
 def test_gemv_split_k_parity(monkeypatch, split, case):
     """The GEMV with K split over 2 or 4 waves of a block (fixed-order LDS
     reduction) against the oracle, and against the unsplit layer."""
