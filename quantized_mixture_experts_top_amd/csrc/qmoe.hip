@@ -704,19 +704,21 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
 
 // -------------------------------------------------------- GEMV (1-2 rows)
 
-// Work items of at most kGemvRows routed rows, used when a call averages at
-// most one routed row per expert (small M).  There each expert's product is
-// a weight-streaming matrix-vector product, so it runs on packed fp16 dot
-// products (v_dot2_f32_f16) rather than 16-row MFMA tiles: on MI355X, MFMAs
-// fed from a full-rate weight stream hold back the stream's load issue,
-// while the dot-product form keeps it close to the read bandwidth.
+// Work items of at most kGemvRows routed rows, used while a call averages
+// at most 1.75 routed rows per expert (small M).  There each expert's
+// product is a weight-streaming matrix-vector product, so it runs on packed
+// fp16 dot products (v_dot2_f32_f16) rather than MFMA tiles: on MI355X,
+// MFMAs fed from a full-rate weight stream hold back the stream's load
+// issue, while the dot-product form keeps it close to the read bandwidth.
 //
-// Lane (r, kq) of a wave owns weight row r of each 16-row block.  K is
-// walked in super-steps of 512 inputs (a 256-byte chunk of each row); in
-// sub-step u the four lanes of a row read its 64 contiguous bytes 64u..64u+63,
-// lane kq taking group 4u + kq.  Lane kq loads the row's scale quad kq (8
-// bytes, groups 4kq..4kq+3) and two cross-row lane swaps transpose the four
-// quads so that lane kq holds the scales of groups kq, 4+kq, 8+kq, 12+kq.
+// K is walked in super-steps of 512 inputs: a 256-byte chunk of each
+// weight row, 16 groups of 32.  Lane (q, j) of a wave (q = lane/16) takes
+// group j of every super-step, for rows 4m + q (m = 0..3) of each 16-row
+// weight block, so one load instruction reads four whole 256-byte chunks
+// (eight full cache lines), and a lane reads its group's activations once
+// per super-step for all of its rows.  Each lane loads its group's scale
+// per row.  The 16 lanes of a row hold partial sums over different groups;
+// a butterfly over those lanes adds them once, after the K loop.
 //
 // Arithmetic: a nibble q OR-ed into fp16 1024.0 is 1024+q exactly; minus
 // 1032 it is q-8 (for the odd inputs, whose nibble sits 4 bits up: 1024+16q
@@ -725,33 +727,25 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
 // fp32 (exact products); the group's scale multiplies it in fp32.  A zero
 // weight (code 8) contributes exactly zero.
 //
-// The item's activation rows are staged in LDS once per block.
+// The item's activation rows are staged in LDS once per block, each
+// group's 64 bytes padded to 80 so that the 16 groups a wave reads at once
+// fall in distinct banks.
 constexpr int kGemvRows = 2;
 constexpr int kGemvMaxRowsPer4Experts = 7;  // GEMV while 4*M*top_k <= 7E
-constexpr int kGemvMaxK = 15360;  // largest K the GEMV stages (two rows in 64 KiB of LDS)
+constexpr int kGemvGroupBytes = 80;         // one staged group of 32 fp16 inputs, padded
+constexpr int kGemvMaxK = 13056;            // largest K the GEMV stages (two rows in 64 KiB of LDS)
 
 // LDS bytes of a block: the activation rows
-__host__ __device__ constexpr size_t gemv_lds_bytes(int K) { return (size_t)kGemvRows * K * 2; }
-
-// the row swaps above on fp32 values
-__device__ __forceinline__ void swap16(float& a, float& b) {
-  uint32_t x = __builtin_bit_cast(uint32_t, a), y = __builtin_bit_cast(uint32_t, b);
-  swap16(x, y);
-  a = __builtin_bit_cast(float, x);
-  b = __builtin_bit_cast(float, y);
-}
-__device__ __forceinline__ void swap32(float& a, float& b) {
-  uint32_t x = __builtin_bit_cast(uint32_t, a), y = __builtin_bit_cast(uint32_t, b);
-  swap32(x, y);
-  a = __builtin_bit_cast(float, x);
-  b = __builtin_bit_cast(float, y);
+__host__ __device__ constexpr size_t gemv_lds_bytes(int K) {
+  return (size_t)kGemvRows * (K / 32) * kGemvGroupBytes;
 }
 
-#ifndef QMOE_GEMV_WPE
-#define QMOE_GEMV_WPE 3
-#endif
+// Two waves per SIMD: the ping-pong of whole super-steps holds 80 registers
+// of weights; capped at three waves the compiler spills inside the K loop,
+// which measured slower on MI355X than two waves without spills.
+constexpr int kGemvWPE = 2;
 template <int WN, int WK, bool GATEUP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QMOE_GEMV_WPE))) void gemv_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kGemvWPE))) void gemv_kernel(
     GemmArgs g) {
   static_assert(WN * WK == 4, "4 waves per block");
   constexpr int NBB = 2;                 // weight blocks of 16 rows per wave
@@ -759,7 +753,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QMOE_G
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave % WN, wk = wave / WN;
-  const int r = lane & 15, kq = lane >> 4;
+  const int q = lane >> 4, j = lane & 15;
 
   // consecutive blocks take consecutive column blocks of one item, so each
   // item's stream is spread over all XCDs
@@ -784,20 +778,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QMOE_G
   const __amdgpu_buffer_rsrc_t rS = buffer_rsrc(sbase, (uint32_t)g.Nw * KG * 2);
   const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(g.a, g.a_bytes);
 
-  uint32_t boff[NBB], soff[NBB];
+  // lane part of the code and scale offsets (row q, group j), and each
+  // block's first weight row (wave-uniform, in the scalar offset; every
+  // in-range lane stays inside the weights)
+  const uint32_t bl = (uint32_t)q * K2 + 16 * j, sl = (uint32_t)q * KG * 2 + 2 * j;
+  uint32_t brow[NBB];
   int col0[NBW];
 #pragma unroll
   for (int c = 0; c < NBW; ++c) {
     col0[c] = ((nb * WN + wn) * NBW + c) * 16;
-    const uint32_t n = col0[c] < g.N ? col0[c] + r : 0;
-    if (GATEUP) {  // gate row n and up row N + n
-      boff[0] = n * K2 + 16 * kq;
-      soff[0] = n * KG * 2 + 8 * kq;
-      boff[1] = (g.N + n) * K2 + 16 * kq;
-      soff[1] = (g.N + n) * KG * 2 + 8 * kq;
+    const uint32_t n0 = col0[c] < g.N ? col0[c] : 0;
+    if (GATEUP) {  // gate rows n0.. and up rows N + n0..
+      brow[0] = n0;
+      brow[1] = g.N + n0;
     } else {
-      boff[c] = n * K2 + 16 * kq;
-      soff[c] = n * KG * 2 + 8 * kq;
+      brow[c] = n0;
     }
   }
 
@@ -807,35 +802,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QMOE_G
   const bool has_tail = S_end > nss_full;
   const int ngroups = g.K / 32;
 
-  // one super-step of this lane's weights: 4 sub-steps of codes and the
-  // scale quad (2 dwords) per weight block
+  // one super-step of this lane's weights: group j of rows 4m + q of each
+  // block (16 code bytes and the fp16 scale each)
   struct Super {
     u32x4_t b[NBB][4];
-    uint32_t sc[NBB][2];
+    uint32_t sc[NBB][4];
   };
-  // sub_ok: sub-step u's groups exist (uniform); quad_ok: this lane's quad
-  auto load_super = [&](int S, Super& f, int n_sub, bool quad_ok) __attribute__((always_inline)) {
+  // ok: this lane's group exists (false: codes and scale read 0)
+  auto load_super = [&](int S, Super& f, bool ok) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int b = 0; b < NBB; ++b)
-        f.b[b][u] = __builtin_bit_cast(
-            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rB, u < n_sub ? boff[b] + 64 * u : kOob, S * (kSuper / 2), 0));
+        f.b[b][m] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rB, ok ? bl : kOob,
+                                                           (brow[b] + 4 * m) * K2 + S * (kSuper / 2), 0));
 #pragma unroll
-    for (int b = 0; b < NBB; ++b) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rS, quad_ok ? soff[b] : kOob, S * 32, 0);
-      f.sc[b][0] = v[0];
-      f.sc[b][1] = v[1];
-    }
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int b = 0; b < NBB; ++b)
+        f.sc[b][m] = __builtin_amdgcn_raw_buffer_load_b16(rS, ok ? sl : kOob, (brow[b] + 4 * m) * KG * 2 + S * 32, 0);
   };
 
   // the first super-step's loads go out before the rows are staged
   Super fa, fb;
-  if (S_end_full > S_begin) load_super(S_begin, fa, 4, true);
+  if (S_end_full > S_begin) load_super(S_begin, fa, true);
 
-  // ---- stage the item's activation rows (operand format) in LDS
+  // ---- stage the item's activation rows (operand format) in LDS: group
+  // gi's four 16-byte runs at gi * 80 bytes
   extern __shared__ __attribute__((aligned(16))) uint32_t gemv_lds[];
   u32x4_t* lds_x = reinterpret_cast<u32x4_t*>(gemv_lds);
+  constexpr int kGroupRuns = kGemvGroupBytes / 16;  // 5: 4 runs + 1 of padding
   const int runs = g.K / 8;
   for (int t = 0; t < nr; ++t) {
     uint32_t off;
@@ -846,58 +843,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QMOE_G
     } else {
       off = (uint32_t)(pos0 + t) * (uint32_t)g.K * 2;
     }
-    for (int q = tid; q < runs; q += kThreads)
-      lds_x[t * runs + q] = __builtin_bit_cast(
-          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rA, off == kOob ? kOob : off + 16 * q, 0, 0));
+    for (int v = tid; v < runs; v += kThreads)
+      lds_x[(t * ngroups + (v >> 2)) * kGroupRuns + (v & 3)] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rA, off == kOob ? kOob : off + 16 * v, 0, 0));
   }
   __syncthreads();
 
-  float acc[NBB][kGemvRows];
+  float acc[NBB][4][kGemvRows];
 #pragma unroll
   for (int b = 0; b < NBB; ++b)
 #pragma unroll
-    for (int t = 0; t < kGemvRows; ++t) acc[b][t] = 0.f;
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int t = 0; t < kGemvRows; ++t) acc[b][m][t] = 0.f;
 
   // Super-step S from registers.  A group past K (partial last super-step)
   // has scale 0 and reads the row's last group, so it adds exactly zero.
   auto compute_super = [&](int S, const Super& f, auto rows_tag) __attribute__((always_inline)) {
     constexpr int NR = decltype(rows_tag)::value;
     const half2_t b_lo = as_half2(0xE408E408u), b_hi = as_half2(0xE480E480u);  // -1032, -1152
-    // scales: lane kq holds quad kq; transpose so that sc[b][u] = group 4u+kq
-    float sc[NBB][4];
+    const int gi = min(S * 16 + j, ngroups - 1);
+    u32x4_t xv[NR][4];
 #pragma unroll
-    for (int b = 0; b < NBB; ++b) {
-      const half2_t lo = as_half2(f.sc[b][0]), hi = as_half2(f.sc[b][1]);
-      float q0 = (float)lo[0], q1 = (float)lo[1], q2 = (float)hi[0], q3 = (float)hi[1];
-      swap16(q0, q1);
-      swap16(q2, q3);
-      swap32(q0, q2);
-      swap32(q1, q3);
-      sc[b][0] = q0;
-      sc[b][1] = q1;
-      sc[b][2] = q2;
-      sc[b][3] = q3;
-    }
+    for (int t = 0; t < NR; ++t)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int xq = min((S * 16 + 4 * u + kq) * 4, runs - 4);  // first 16-byte run of the group
-      u32x4_t xv[NR][4];
+      for (int i = 0; i < 4; ++i) xv[t][i] = lds_x[(t * ngroups + gi) * kGroupRuns + i];
 #pragma unroll
-      for (int t = 0; t < NR; ++t)
+    for (int b = 0; b < NBB; ++b)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xv[t][i] = lds_x[t * runs + xq + i];
-#pragma unroll
-      for (int b = 0; b < NBB; ++b) {
+      for (int m = 0; m < 4; ++m) {
         float p[NR];
 #pragma unroll
         for (int t = 0; t < NR; ++t) p[t] = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t q = word(f.b[b][u], i), q8 = q >> 8;
-          const half2_t w0 = as_half2(and_or(q, 0x000F000Fu, 0x64006400u)) + b_lo;   // inputs 0, 4
-          const half2_t w1 = as_half2(and_or(q, 0x00F000F0u, 0x64006400u)) + b_hi;   // 1, 5 (x16)
-          const half2_t w2 = as_half2(and_or(q8, 0x000F000Fu, 0x64006400u)) + b_lo;  // 2, 6
-          const half2_t w3 = as_half2(and_or(q8, 0x00F000F0u, 0x64006400u)) + b_hi;  // 3, 7 (x16)
+          const uint32_t w = word(f.b[b][m], i), w8 = w >> 8;
+          const half2_t w0 = as_half2(and_or(w, 0x000F000Fu, 0x64006400u)) + b_lo;   // inputs 0, 4
+          const half2_t w1 = as_half2(and_or(w, 0x00F000F0u, 0x64006400u)) + b_hi;   // 1, 5 (x16)
+          const half2_t w2 = as_half2(and_or(w8, 0x000F000Fu, 0x64006400u)) + b_lo;  // 2, 6
+          const half2_t w3 = as_half2(and_or(w8, 0x00F000F0u, 0x64006400u)) + b_hi;  // 3, 7 (x16)
 #pragma unroll
           for (int t = 0; t < NR; ++t) {
             p[t] = __builtin_amdgcn_fdot2(w0, as_half2(xv[t][i][0]), p[t], false);
@@ -906,10 +890,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QMOE_G
             p[t] = __builtin_amdgcn_fdot2(w3, as_half2(xv[t][i][3]), p[t], false);
           }
         }
+        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)f.sc[b][m]);
 #pragma unroll
-        for (int t = 0; t < NR; ++t) acc[b][t] += sc[b][u] * p[t];
+        for (int t = 0; t < NR; ++t) acc[b][m][t] += s * p[t];
       }
-    }
   };
 
   // Ping-pong over whole super-steps: the next one's loads are issued
@@ -921,49 +905,59 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QMOE_G
     const int last = S_end_full - 1;
     int S = S_begin;
     for (; S + 2 <= last; S += 2) {
-      load_super(S + 1, fb, 4, true);
+      load_super(S + 1, fb, true);
       __builtin_amdgcn_sched_barrier(0);
       compute_super(S, fa, rows_tag);
-      load_super(S + 2, fa, 4, true);
+      load_super(S + 2, fa, true);
       __builtin_amdgcn_sched_barrier(0);
       compute_super(S + 1, fb, rows_tag);
     }
     if (S + 1 == last) {
-      load_super(S + 1, fb, 4, true);
+      load_super(S + 1, fb, true);
       __builtin_amdgcn_sched_barrier(0);
       compute_super(S, fa, rows_tag);
       compute_super(S + 1, fb, rows_tag);
     } else if (S == last) {
       compute_super(S, fa, rows_tag);
     }
-    if (has_tail) {  // the partial super-step: whole quads of groups remain
-      const int n_sub = (ngroups - nss_full * 16) / 4;
-      load_super(nss_full, fa, n_sub, kq < n_sub);
+    if (has_tail) {  // the partial super-step: lanes past the last group read 0
+      load_super(nss_full, fa, nss_full * 16 + j < ngroups);
       compute_super(nss_full, fa, rows_tag);
     }
   };
   if (nr == 1) run(std::integral_constant<int, 1>{});
   else run(std::integral_constant<int, 2>{});
 
-  // ---- reduce over the 4 lane groups (they hold different groups of a row)
+  // ---- add over the 16 lanes of a row (they hold different groups); then
+  // lane (q, j < 4) takes row 4j + q of each block
+  float res[NBB][kGemvRows];
 #pragma unroll
   for (int b = 0; b < NBB; ++b)
 #pragma unroll
     for (int t = 0; t < kGemvRows; ++t) {
-      acc[b][t] += __shfl_xor(acc[b][t], 16, 64);
-      acc[b][t] += __shfl_xor(acc[b][t], 32, 64);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        float v = acc[b][m][t];
+        v += __shfl_xor(v, 1, 64);
+        v += __shfl_xor(v, 2, 64);
+        v += __shfl_xor(v, 4, 64);
+        v += __shfl_xor(v, 8, 64);
+        acc[b][m][t] = v;
+      }
+      res[b][t] = j == 0 ? acc[b][0][t] : j == 1 ? acc[b][1][t] : j == 2 ? acc[b][2][t] : acc[b][3][t];
     }
+  const int r = 4 * j + q;  // this lane's row in each block (lanes with j < 4)
   // ---- then over the WK waves along K (fixed order: wave wk=0 adds 1, 2, 3)
   if constexpr (WK > 1) {
     float* red = reinterpret_cast<float*>(gemv_lds);  // the staged rows are dead by now
     constexpr int kVals = NBB * kGemvRows;
     __syncthreads();
-    if (wk > 0 && kq == 0) {
+    if (wk > 0 && j < 4) {
 #pragma unroll
       for (int b = 0; b < NBB; ++b)
 #pragma unroll
         for (int t = 0; t < kGemvRows; ++t)
-          red[(((wk - 1) * WN + wn) * kVals + b * kGemvRows + t) * 16 + r] = acc[b][t];
+          red[(((wk - 1) * WN + wn) * kVals + b * kGemvRows + t) * 16 + r] = res[b][t];
     }
     __syncthreads();
     if (wk > 0) return;
@@ -972,11 +966,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QMOE_G
 #pragma unroll
       for (int b = 0; b < NBB; ++b)
 #pragma unroll
-        for (int t = 0; t < kGemvRows; ++t) acc[b][t] += red[(((w - 1) * WN + wn) * kVals + b * kGemvRows + t) * 16 + r];
+        for (int t = 0; t < kGemvRows; ++t)
+          if (j < 4) res[b][t] += red[(((w - 1) * WN + wn) * kVals + b * kGemvRows + t) * 16 + r];
   }
-  if (kq != 0) return;
+  if (j >= 4) return;
 
-  // ---- epilogue: lane r holds weight row r of each block for the item's rows
+  // ---- epilogue: lane (q, j) holds weight row r = 4j + q of each block
 #pragma unroll
   for (int t = 0; t < kGemvRows; ++t) {
     if (t >= nr) continue;
@@ -984,7 +979,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QMOE_G
     if (GATEUP) {
       if (col0[0] >= g.N) continue;
       const int col = col0[0] + r;
-      const float gt = acc[0][t], up = acc[1][t];
+      const float gt = res[0][t], up = res[1][t];
       // odd columns are stored divided by 16 (operand format)
       const float hv = gt / (1.0f + __expf(-gt)) * up * ((col & 1) ? 0.0625f : 1.0f);
       g.h_out[(size_t)pos * g.N + ((col & ~7) | inv_perm8(col & 7))] = (_Float16)hv;
@@ -995,7 +990,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QMOE_G
 #pragma unroll
       for (int c = 0; c < NBW; ++c) {
         if (col0[c] >= g.N) continue;
-        g.y_out[(size_t)slot * g.N + col0[c] + r] = wv * acc[c][t];
+        g.y_out[(size_t)slot * g.N + col0[c] + r] = wv * res[c][t];
       }
     }
   }

@@ -138,8 +138,8 @@ FWD_CASES = [
     (1, 256, 128, 1, 5, False),      # one expert, tiles
     (32, 256, 128, 32, 3, False),    # top_k = 32 = E (the largest top_k)
     (1024, 128, 128, 8, 20, True),   # 1024 experts (the most), shared expert
-    (4, 15360, 128, 2, 3, False),    # the largest K the GEMV stages in LDS
-    (4, 15488, 128, 1, 2, False),    # K past the GEMV's LDS: small M on tiles
+    (4, 13056, 128, 2, 3, False),    # the largest K the GEMV stages in LDS
+    (4, 13184, 128, 1, 2, False),    # K past the GEMV's LDS: small M on tiles
 ]
 
 
