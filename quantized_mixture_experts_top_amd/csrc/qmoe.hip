@@ -73,6 +73,7 @@ struct RouteArgs {
 
 constexpr int kRouteThreads = 1024;  // routing blocks: 16 waves
 constexpr int kRouteWaves = kRouteThreads / 64;
+constexpr int kXRuns = 8 * kRouteThreads;  // 16-byte runs of x per conversion block
 
 // Exclusive scan of in[0..n) into out[0..n] (out[n] = total) by the 1024
 // threads of a routing block: each thread sums 2 consecutive entries, a
@@ -154,7 +155,9 @@ __device__ void route_finish_single(const RouteArgs& a, const uint32_t (*cm)[2],
 
 // One block per chunk of 64 tokens; the last block to finish (atomic ticket,
 // no waiting) turns the per-chunk token masks into counts, offsets,
-// positions and work items.  EPL = logits per lane (E <= 64 * EPL).
+// positions and work items.  The blocks after those convert x to the fp16
+// operand format in slices (they take no part in the ticket).  EPL =
+// logits per lane (E <= 64 * EPL).
 template <int EPL>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   __shared__ uint32_t cm[QMOE_MAX_EXPERTS][2];
@@ -169,50 +172,60 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   const int c = blockIdx.x, E = a.E, k = a.k;
   const int rows = min(kChunk, a.M - c * kChunk);
 
-  for (int e = tid; e < E; e += kRouteThreads) cm[e][0] = cm[e][1] = 0u;
-
-  // x rows of the chunk, as 16-byte runs; the first kXPre runs of each
-  // thread are loaded before the top-k so their latency overlaps it
-  constexpr int kXPre = 8;
-  const long long xn = (long long)rows * (a.H / 8);
-  const uint4* xs = a.x + (size_t)c * kChunk * (a.H / 8);
-  uint4* xd = a.xa + (size_t)c * kChunk * (a.H / 8);
-  uint4 xpre[kXPre];
+  // blocks past the C routing blocks convert x to the fp16 operand format,
+  // kXRuns 16-byte runs each, spread over the GPU
+  if (c >= a.C) {
+    const long long n = (long long)a.M * (a.H / 8);
+    const long long q0 = (long long)(c - a.C) * kXRuns + tid;
+    uint4 v[kXRuns / kRouteThreads];
 #pragma unroll
-  for (int u = 0; u < kXPre; ++u) xpre[u] = xs[min(tid + (long long)u * kRouteThreads, xn - 1)];  // clamped
+    for (int u = 0; u < kXRuns / kRouteThreads; ++u) v[u] = a.x[min(q0 + (long long)u * kRouteThreads, n - 1)];  // clamped
+#pragma unroll
+    for (int u = 0; u < kXRuns / kRouteThreads; ++u) {
+      const long long q = q0 + (long long)u * kRouteThreads;
+      if (q < n) a.xa[q] = bf16x8_to_aformat(v[u]);
+    }
+    return;
+  }
+
+  for (int e = tid; e < E; e += kRouteThreads) cm[e][0] = cm[e][1] = 0u;
   __syncthreads();
 
   // ---- phase 1a: top-k of each token, one wave per token
   for (int tl = wave; tl < rows; tl += kRouteWaves) {
     const int t = c * kChunk + tl;
     const float* row = a.logits + (size_t)t * E;
-    // key = (order-preserving logit bits, ~expert): the maximum key is the
-    // largest logit, ties to the lowest expert index.  Absent experts = 0.
+    // key = order-preserving bits of the logit (every finite logit maps
+    // above 0; absent and taken experts are 0).  Each round takes the
+    // largest key and, among experts holding it, the lowest index: the
+    // first slot s with a lane holding it, lowest lane first.
     // (loads clamped into the row rather than predicated, so they all
     // issue before the first wait)
     float lv[EPL];
 #pragma unroll
     for (int s = 0; s < EPL; ++s) lv[s] = row[min(s * 64 + lane, E - 1)];
-    uint64_t key[EPL];
+    uint32_t key[EPL];
 #pragma unroll
-    for (int s = 0; s < EPL; ++s) {
-      const int e = s * 64 + lane;
-      key[s] = (e < E) ? (((uint64_t)ordered_key(lv[s]) << 32) | (uint32_t)(~e)) : 0ull;
-    }
+    for (int s = 0; s < EPL; ++s) key[s] = (s * 64 + lane < E) ? ordered_key(lv[s]) : 0u;
     int my_e = 0;
     float my_l = 0.0f;
     for (int j = 0; j < k; ++j) {
-      uint64_t best = 0;
+      uint32_t best = 0;
 #pragma unroll
       for (int s = 0; s < EPL; ++s) best = key[s] > best ? key[s] : best;
-      best = wave_max_u64(best);
-      const int e_sel = (int)(~(uint32_t)best);
+      best = wave_max_u32(best);
+      int e_sel = -1;
+#pragma unroll
+      for (int s = 0; s < EPL; ++s) {
+        const uint64_t m = __ballot(key[s] == best);
+        if (e_sel < 0 && m != 0) e_sel = s * 64 + __ffsll((long long)m) - 1;
+      }
 #pragma unroll
       for (int s = 0; s < EPL; ++s)
         if (s * 64 + lane == e_sel) key[s] = 0;
       if (lane == j) {
         my_e = e_sel;
-        my_l = from_ordered_key((uint32_t)(best >> 32));
+        my_l = from_ordered_key(best);
       }
     }
     // renormalised softmax over the selected logits: the full-softmax
@@ -231,25 +244,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     }
   }
 
-  // ---- phase 1b: the chunk's x rows -> fp16 operand format (contiguous)
-  {
-#pragma unroll
-    for (int u = 0; u < kXPre; ++u) {
-      const long long q = tid + (long long)u * kRouteThreads;
-      if (q < xn) xd[q] = bf16x8_to_aformat(xpre[u]);
-    }
-    const long long n = xn;
-    for (long long q0 = tid + (long long)kXPre * kRouteThreads; q0 < n; q0 += 4 * kRouteThreads) {
-      uint4 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = xs[min(q0 + u * kRouteThreads, n - 1)];  // clamped
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const long long q = q0 + u * kRouteThreads;
-        if (q < n) xd[q] = bf16x8_to_aformat(v[u]);
-      }
-    }
-  }
   __syncthreads();
   if (a.C == 1) {
     route_finish_single(a, cm, s_ids, s_cnt, s_off, s_ni, s_ioff, s_wsum);
@@ -589,19 +583,26 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
 #define QMOE_COMPUTE(F, SC, U, BUF)                                                              \
   do {                                                                                           \
     uint32_t s2_[NBB];                                                                           \
-    _Pragma("unroll") for (int b = 0; b < NBB; ++b) s2_[b] = (SC)[b][(U)];                   \
+    _Pragma("unroll") for (int b = 0; b < NBB; ++b) s2_[b] = (SC)[b][(U)];                       \
+    half8_t bfa_[NBB], bfb_[NBB];                                                                \
+    _Pragma("unroll") for (int b = 0; b < NBB; ++b) bfa_[b] = dq8p(word((F).b[b], 0), s2_[b]);   \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                              \
-      half8_t bf[NBB];                                                                           \
-      _Pragma("unroll") for (int b = 0; b < NBB; ++b) bf[b] = dq8p(word((F).b[b], i), s2_[b]);   \
+      /* k-slice i's MFMAs, and the decode of slice i+1 in the same */                           \
+      /* scheduling region so the two can interleave */                                          \
+      half8_t* cur_ = (i & 1) ? bfb_ : bfa_;                                                     \
+      half8_t* nxt_ = (i & 1) ? bfa_ : bfb_;                                                     \
       _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                                        \
         if (mb < NMBC) {                                                                         \
           const half8_t av =                                                                     \
               *reinterpret_cast<const half8_t*>(&QMOE_LDS_A(BUF)[mb * 4 * kBlkHalves + rd_half + 8 * i]); \
-          _Pragma("unroll") for (int b = 0; b < NBB; ++b) acc[mb][b] = mfma16x16x32(av, bf[b], acc[mb][b]); \
+          _Pragma("unroll") for (int b = 0; b < NBB; ++b) acc[mb][b] = mfma16x16x32(av, cur_[b], acc[mb][b]); \
         }                                                                                        \
       }                                                                                          \
-      /* gate+up: one k-slice at a time, which keeps its 4 weight blocks */                      \
-      /* and 128 accumulators within 256 registers */                                            \
+      if (i < 3) {                                                                               \
+        _Pragma("unroll") for (int b = 0; b < NBB; ++b) nxt_[b] = dq8p(word((F).b[b], i + 1), s2_[b]); \
+      }                                                                                          \
+      /* gate+up: one slice at a time keeps 128 accumulators and 4 weight */                     \
+      /* blocks within 256 registers */                                                          \
       if (GATEUP) __builtin_amdgcn_sched_barrier(0);                                             \
     }                                                                                            \
   } while (0)
@@ -1231,7 +1232,9 @@ int do_route(qmoe_layer* L, const void* x, const float* logits, int64_t M, void*
     const int rc = check_launch(L, "ticket clear");
     if (rc != QMOE_OK) return rc;
   }
-  const dim3 grid((unsigned)lay.C);
+  // routing blocks, then the blocks that convert x
+  const int64_t xblocks = ceil_div(M * (L->d.H / 8), (int64_t)kXRuns);
+  const dim3 grid((unsigned)(lay.C + xblocks));
   const int epl = (L->d.E + 63) / 64;
   if (epl <= 1) route_kernel<1><<<grid, kRouteThreads, 0, st>>>(a);
   else if (epl <= 2) route_kernel<2><<<grid, kRouteThreads, 0, st>>>(a);

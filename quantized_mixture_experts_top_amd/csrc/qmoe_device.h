@@ -111,37 +111,23 @@ __device__ __forceinline__ float from_ordered_key(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
-  uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Maximum of a 64-bit value over the 64 lanes of a wave, returned to every
+// Maximum of a 32-bit value over the 64 lanes of a wave, returned to every
 // lane.  DPP steps (quad permutes, row mirrors, row broadcasts) combine
 // lanes within and across rows of 16 without going through LDS; lane 63
 // ends with the maximum, which readlane broadcasts.
 template <int kCtrl, int kRowMask>
-__device__ __forceinline__ void dpp_max_step(uint32_t& lo, uint32_t& hi) {
-  const uint32_t plo = __builtin_amdgcn_update_dpp(lo, lo, kCtrl, kRowMask, 0xF, false);
-  const uint32_t phi = __builtin_amdgcn_update_dpp(hi, hi, kCtrl, kRowMask, 0xF, false);
-  const uint64_t p = ((uint64_t)phi << 32) | plo, c = ((uint64_t)hi << 32) | lo;
-  const uint64_t m = p > c ? p : c;
-  lo = (uint32_t)m;
-  hi = (uint32_t)(m >> 32);
+__device__ __forceinline__ uint32_t dpp_max_step_u32(uint32_t v) {
+  const uint32_t p = __builtin_amdgcn_update_dpp(v, v, kCtrl, kRowMask, 0xF, false);
+  return p > v ? p : v;
 }
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  dpp_max_step<0xB1, 0xF>(lo, hi);   // quad_perm [1,0,3,2]
-  dpp_max_step<0x4E, 0xF>(lo, hi);   // quad_perm [2,3,0,1]
-  dpp_max_step<0x141, 0xF>(lo, hi);  // row_half_mirror
-  dpp_max_step<0x140, 0xF>(lo, hi);  // row_mirror
-  dpp_max_step<0x142, 0xA>(lo, hi);  // row_bcast:15 into rows 1, 3
-  dpp_max_step<0x143, 0xC>(lo, hi);  // row_bcast:31 into rows 2, 3
-  lo = __builtin_amdgcn_readlane(lo, 63);
-  hi = __builtin_amdgcn_readlane(hi, 63);
-  return ((uint64_t)hi << 32) | lo;
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_step_u32<0xB1, 0xF>(v);
+  v = dpp_max_step_u32<0x4E, 0xF>(v);
+  v = dpp_max_step_u32<0x141, 0xF>(v);
+  v = dpp_max_step_u32<0x140, 0xF>(v);
+  v = dpp_max_step_u32<0x142, 0xA>(v);
+  v = dpp_max_step_u32<0x143, 0xC>(v);
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 __device__ __forceinline__ float4_t mfma16x16x32(half8_t a, half8_t b, float4_t c) {
