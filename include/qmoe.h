@@ -38,8 +38,9 @@
  *   > 1.75    128-row MFMA tiles: codes decoded to fp16 operands
  *             ((c-8)*scale rounded to nearest even), products accumulated
  *             in fp32 by MFMA.
- * The weighted per-slot results are fp32 and out is rounded to bf16
- * (nearest even).  Results are deterministic for a given M.
+ * The weighted per-slot results are rounded to bf16 (nearest even) in the
+ * workspace, summed per token in fp32 in slot order, and out is rounded to
+ * bf16 (nearest even).  Results are deterministic for a given M.
  *
  * Ownership: the caller owns every buffer.  The layer handle borrows the
  * weight pointers for its lifetime and copies nothing.  The library never
@@ -161,6 +162,7 @@ int qmoe_read_routing(qmoe_layer* layer, int64_t M, const void* workspace, size_
                       int32_t* perm, void* stream);
 
 /* Copy an intermediate of the last call into fp32 rows in slot order
+   (h is held as fp16, y as bf16; both convert to fp32 exactly)
    (row t*k+j for routed slot j of token t; rows M*k+t for the shared expert):
    which = 0: h = SiLU(gate)*up, [M*k (+M), I]  (after qmoe_gate_up)
    which = 1: y = w * Down(h),   [M*k (+M), H]  (after qmoe_down) */

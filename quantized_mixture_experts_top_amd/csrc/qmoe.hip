@@ -347,7 +347,7 @@ struct GemmArgs {
   const _Float16* a;  // A rows in A-format: x (gate+up) or h (down)
   uint32_t a_bytes;      // bytes of the A buffer (loads past it read 0)
   _Float16* h_out;    // gate+up: h [R, N] in A-format
-  float* y_out;       // down: y [R, N] in slot order
+  uint16_t* y_out;    // down: y [R, N] bf16 in slot order
 };
 
 template <int NBB>
@@ -696,7 +696,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
           const int slot = g.perm[pos];
           if (slot < 0 || slot >= g.R) continue;
           const float wv = slot < g.T ? g.wts[slot] : 1.0f;
-          g.y_out[(size_t)slot * g.N + col] = wv * acc[mb][c][i];
+          g.y_out[(size_t)slot * g.N + col] = (uint16_t)f32_to_bf16_rne(wv * acc[mb][c][i]);
         }
       }
     }
@@ -991,7 +991,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kGemvW
 #pragma unroll
       for (int c = 0; c < NBW; ++c) {
         if (col0[c] >= g.N) continue;
-        g.y_out[(size_t)slot * g.N + col0[c] + r] = wv * res[c][t];
+        g.y_out[(size_t)slot * g.N + col0[c] + r] = (uint16_t)f32_to_bf16_rne(wv * res[c][t]);
       }
     }
   }
@@ -1000,34 +1000,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kGemvW
 // ---------------------------------------------------------------- combine
 
 // out[t, n] = sum_{j<k} y[t*k + j, n] (in j order) + y[T + t, n] if shared,
-// rounded to bf16.  One thread per 4 consecutive columns; the k slots are
-// loaded in batches of 8 before they are summed, so a thread waits for one
-// round trip per batch rather than one per slot.
-__global__ __launch_bounds__(kThreads) void combine_kernel(const float* y, uint2* out, int M, int H,
+// summed in fp32 from the bf16 slot rows and rounded to bf16.  One thread
+// per 4 consecutive columns; the k slots are loaded in batches of 8 before
+// they are summed, so a thread waits for one round trip per batch rather
+// than one per slot.
+__global__ __launch_bounds__(kThreads) void combine_kernel(const uint2* y, uint2* out, int M, int H,
                                                             int k, int T, int S) {
   const long long q = (long long)blockIdx.x * kThreads + threadIdx.x;
   const int per_row = H / 4;
   if (q >= (long long)M * per_row) return;
   const int t = (int)(q / per_row), c4 = (int)(q % per_row);
-  const float4* base = reinterpret_cast<const float4*>(y) + (size_t)c4;
+  const uint2* base = y + (size_t)c4;
   const size_t row4 = (size_t)H / 4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   const int n = k + (S ? 1 : 0);  // slot rows to add, the shared expert last
   for (int j0 = 0; j0 < n; j0 += 8) {
-    float4 v[8];
+    uint2 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int j = j0 + u;
       const size_t r = j < k ? (size_t)t * k + j : (size_t)T + t;
-      v[u] = j < n ? base[r * row4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[u] = j < n ? base[r * row4] : make_uint2(0u, 0u);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (j0 + u < n) {
-        acc.x += v[u].x;
-        acc.y += v[u].y;
-        acc.z += v[u].z;
-        acc.w += v[u].w;
+        acc.x += __uint_as_float(v[u].x << 16);
+        acc.y += __uint_as_float(v[u].x & 0xFFFF0000u);
+        acc.z += __uint_as_float(v[u].y << 16);
+        acc.w += __uint_as_float(v[u].y & 0xFFFF0000u);
       }
     }
   }
@@ -1065,6 +1066,11 @@ __global__ __launch_bounds__(kThreads) void read_h_kernel(const _Float16* h, con
   if (pos < 0 || pos >= R) pos = f;
   const float v = (float)h[pos * I + ((col & ~7) | inv_perm8(col & 7))];
   out[q] = (col & 1) ? v * 16.0f : v;  // odd columns are stored divided by 16
+}
+
+__global__ __launch_bounds__(kThreads) void read_y_kernel(const uint16_t* y, long long n, float* out) {
+  const long long q = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (q < n) out[q] = __uint_as_float((uint32_t)y[q] << 16);
 }
 
 __global__ void init_ctrl_kernel(int* ctrl) {
@@ -1132,7 +1138,7 @@ Layout make_layout(const qmoe_layer* L, int64_t M) {
   l.items = take(l.max_items_all * 16);
   l.xa = take(M * H * 2);
   l.h = take(l.R * I * 2);
-  l.y = take(l.R * H * 4);
+  l.y = take(l.R * H * 2);
   l.total = off;
   return l;
 }
@@ -1280,7 +1286,7 @@ void fill_gemm_args(const qmoe_layer* L, int64_t M, void* ws, const Layout& lay,
     g.a = at<_Float16>(ws, lay.h);
     g.a_bytes = (uint32_t)(lay.R * I * 2);
     g.h_out = nullptr;
-    g.y_out = at<float>(ws, lay.y);
+    g.y_out = at<uint16_t>(ws, lay.y);
   }
 }
 
@@ -1343,7 +1349,7 @@ int do_combine(qmoe_layer* L, int64_t M, void* out, void* ws, const Layout& lay,
   if (!aligned16(out)) return fail(QMOE_ERR_ARG, "out must be 16-byte aligned");
   const int64_t n = M * (L->d.H / 4);
   combine_kernel<<<dim3((unsigned)ceil_div(n, kThreads)), kThreads, 0, st>>>(
-      at<float>(ws, lay.y), static_cast<uint2*>(out), (int)M, L->d.H, L->d.top_k, (int)lay.T, (int)lay.S);
+      at<uint2>(ws, lay.y), static_cast<uint2*>(out), (int)M, L->d.H, L->d.top_k, (int)lay.T, (int)lay.S);
   return check_launch(L, "combine_kernel");
 }
 
@@ -1503,10 +1509,9 @@ int qmoe_read_intermediate(qmoe_layer* L, int64_t M, const void* ws, size_t ws_b
     return check_launch(L, "read_h_kernel");
   }
   if (which == 1) {
-    if (hipMemcpyAsync(out_f32, at<float>(w, lay.y), (size_t)lay.R * L->d.H * 4, hipMemcpyDeviceToDevice, st) !=
-        hipSuccess)
-      return fail(QMOE_ERR_LAUNCH, "hipMemcpyAsync of y failed");
-    return QMOE_OK;
+    const int64_t n = lay.R * L->d.H;
+    read_y_kernel<<<dim3((unsigned)ceil_div(n, kThreads)), kThreads, 0, st>>>(at<uint16_t>(w, lay.y), n, out_f32);
+    return check_launch(L, "read_y_kernel");
   }
   return fail(QMOE_ERR_ARG, "which must be 0 (h) or 1 (y)");
 }
