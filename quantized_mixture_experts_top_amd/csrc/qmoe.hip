@@ -601,9 +601,9 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
       if (i < 3) {                                                                               \
         _Pragma("unroll") for (int b = 0; b < NBB; ++b) nxt_[b] = dq8p(word((F).b[b], i + 1), s2_[b]); \
       }                                                                                          \
-      /* gate+up: one slice at a time keeps 128 accumulators and 4 weight */                     \
-      /* blocks within 256 registers */                                                          \
-      if (GATEUP) __builtin_amdgcn_sched_barrier(0);                                             \
+      /* 4 weight blocks: one slice at a time keeps their 128 accumulators */                    \
+      /* within 256 registers */                                                                 \
+      if (NBB >= 4) __builtin_amdgcn_sched_barrier(0);                                           \
     }                                                                                            \
   } while (0)
   // One sub-step with one barrier: start the next sub-step's activation

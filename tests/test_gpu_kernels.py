@@ -274,6 +274,36 @@ def test_uninitialised_workspace(M):
     assert torch.equal(out.view(torch.int16), want.view(torch.int16))
 
 
+@pytest.mark.parametrize("M", [9, 130])  # GEMV items, one routing block; tiles, three meeting at a ticket
+def test_graph_capture_replays_match_eager(M):
+    """The whole forward captured into a HIP graph (fixed M; workspace,
+    inputs and output allocated before the capture) replays to the eager
+    result, bit for bit, four times, with eager calls on other inputs
+    through the same workspace and synchronisations between the replays."""
+    import torch
+    shape = synth.LayerShape(E=64, H=256, I=128, top_k=4)
+    layer, _ = make_layer(shape, 3, M)
+    x, lg = dev_bf16(synth.hidden(4, M, shape.H)), dev(synth.logits(4, M, shape.E))
+    x2, lg2 = dev_bf16(synth.hidden(5, M, shape.H)), dev(synth.logits(5, M, shape.E))
+    want = layer.forward(x, lg).clone()
+    want2 = layer.forward(x2, lg2).clone()
+    assert not torch.equal(want.view(torch.int16), want2.view(torch.int16))
+    out = torch.empty_like(want)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(x, lg, out=out)
+    for rep in range(4):
+        say(f"graph M={M} replay {rep}")
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16)), f"replay {rep}"
+        got2 = layer.forward(x2, lg2)  # eager work in between, same workspace
+        torch.cuda.synchronize()
+        assert torch.equal(got2.view(torch.int16), want2.view(torch.int16))
+
+
 def test_side_stream():
     """The layer enqueues only on the stream it is given."""
     import torch
