@@ -721,16 +721,17 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
 // per row.  The 16 lanes of a row hold partial sums over different groups;
 // a butterfly over those lanes adds them once, after the K loop.
 //
-// Arithmetic: a nibble q OR-ed into fp16 1024.0 is 1024+q exactly; minus
-// 1032 it is q-8 (for the odd inputs, whose nibble sits 4 bits up: 1024+16q
-// minus 1152 = 16(q-8), and their activations are stored divided by 16).
-// Dot products with the activations give the group's sum of x*(q-8) in
-// fp32 (exact products); the group's scale multiplies it in fp32.  A zero
-// weight (code 8) contributes exactly zero.
+// Arithmetic: a nibble q masked in place is read as an fp16 bit pattern,
+// the subnormal q * 2^-24 (for the odd inputs, whose nibble sits 4 bits up,
+// 16q * 2^-24, and their activations are stored divided by 16), so the
+// decode is one AND per pair of codes.  Dot products with the activations
+// give 2^-24 * sum(x*q) in fp32 (exact products); the zero point comes back
+// as 8 * sum(x) per group, computed once per staged row, and the group's
+// scale multiplies 2^24 * p - 8 * sum(x) in fp32.
 //
 // The item's activation rows are staged in LDS once per block, each
 // group's 64 bytes padded to 80 so that the 16 groups a wave reads at once
-// fall in distinct banks.
+// fall in distinct banks; the padding holds the group's 8 * sum(x).
 constexpr int kGemvRows = 2;
 constexpr int kGemvMaxRowsPer4Experts = 7;  // GEMV while 4*M*top_k <= 7E
 constexpr int kGemvGroupBytes = 80;         // one staged group of 32 fp16 inputs, padded
@@ -835,6 +836,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kGemvW
   u32x4_t* lds_x = reinterpret_cast<u32x4_t*>(gemv_lds);
   constexpr int kGroupRuns = kGemvGroupBytes / 16;  // 5: 4 runs + 1 of padding
   const int runs = g.K / 8;
+  // and the group's code offset 8 * sum(x) as fp32 in the first word of its
+  // padding (the four runs of a group sit in four adjacent lanes)
   for (int t = 0; t < nr; ++t) {
     uint32_t off;
     if (GATEUP) {
@@ -844,9 +847,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kGemvW
     } else {
       off = (uint32_t)(pos0 + t) * (uint32_t)g.K * 2;
     }
-    for (int v = tid; v < runs; v += kThreads)
-      lds_x[(t * ngroups + (v >> 2)) * kGroupRuns + (v & 3)] = __builtin_bit_cast(
-          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rA, off == kOob ? kOob : off + 16 * v, 0, 0));
+    for (int v0 = 0; v0 < runs; v0 += kThreads) {  // runs is a multiple of 4: groups stay whole
+      const int v = v0 + tid;
+      const bool in = v < runs;
+      const u32x4_t xr = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rA, (off == kOob || !in) ? kOob : off + 16 * v, 0, 0));
+      float sx = 0.f;  // sum of the run's 8 inputs (positions 2, 3, 6, 7 are stored divided by 16)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const half2_t hv = as_half2(xr[i]);
+        sx += ((i & 1) ? 16.f : 1.f) * ((float)hv[0] + (float)hv[1]);
+      }
+      sx += __shfl_xor(sx, 1, 64);
+      sx += __shfl_xor(sx, 2, 64);
+      if (in) {
+        u32x4_t* grp = lds_x + (t * ngroups + (v >> 2)) * kGroupRuns;
+        grp[v & 3] = xr;
+        if ((v & 3) == 0) reinterpret_cast<float*>(grp + 4)[0] = 8.f * sx;
+      }
+    }
   }
   __syncthreads();
 
@@ -862,13 +881,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kGemvW
   // has scale 0 and reads the row's last group, so it adds exactly zero.
   auto compute_super = [&](int S, const Super& f, auto rows_tag) __attribute__((always_inline)) {
     constexpr int NR = decltype(rows_tag)::value;
-    const half2_t b_lo = as_half2(0xE408E408u), b_hi = as_half2(0xE480E480u);  // -1032, -1152
     const int gi = min(S * 16 + j, ngroups - 1);
     u32x4_t xv[NR][4];
+    float cx[NR];  // 8 * sum(x) of the group
 #pragma unroll
-    for (int t = 0; t < NR; ++t)
+    for (int t = 0; t < NR; ++t) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) xv[t][i] = lds_x[(t * ngroups + gi) * kGroupRuns + i];
+      cx[t] = reinterpret_cast<const float*>(lds_x + (t * ngroups + gi) * kGroupRuns + 4)[0];
+    }
 #pragma unroll
     for (int b = 0; b < NBB; ++b)
 #pragma unroll
@@ -878,11 +899,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kGemvW
         for (int t = 0; t < NR; ++t) p[t] = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+          // the masked nibbles as fp16 bit patterns: q * 2^-24 (subnormal),
+          // or 16q * 2^-24 for the odd inputs
           const uint32_t w = word(f.b[b][m], i), w8 = w >> 8;
-          const half2_t w0 = as_half2(and_or(w, 0x000F000Fu, 0x64006400u)) + b_lo;   // inputs 0, 4
-          const half2_t w1 = as_half2(and_or(w, 0x00F000F0u, 0x64006400u)) + b_hi;   // 1, 5 (x16)
-          const half2_t w2 = as_half2(and_or(w8, 0x000F000Fu, 0x64006400u)) + b_lo;  // 2, 6
-          const half2_t w3 = as_half2(and_or(w8, 0x00F000F0u, 0x64006400u)) + b_hi;  // 3, 7 (x16)
+          const half2_t w0 = as_half2(w & 0x000F000Fu);   // inputs 0, 4
+          const half2_t w1 = as_half2(w & 0x00F000F0u);   // 1, 5 (x16)
+          const half2_t w2 = as_half2(w8 & 0x000F000Fu);  // 2, 6
+          const half2_t w3 = as_half2(w8 & 0x00F000F0u);  // 3, 7 (x16)
 #pragma unroll
           for (int t = 0; t < NR; ++t) {
             p[t] = __builtin_amdgcn_fdot2(w0, as_half2(xv[t][i][0]), p[t], false);
@@ -891,9 +914,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kGemvW
             p[t] = __builtin_amdgcn_fdot2(w3, as_half2(xv[t][i][3]), p[t], false);
           }
         }
+        // sum x*(q-8) = 2^24 * p - 8 * sum(x), times the group's scale
         const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)f.sc[b][m]);
 #pragma unroll
-        for (int t = 0; t < NR; ++t) acc[b][m][t] += s * p[t];
+        for (int t = 0; t < NR; ++t) acc[b][m][t] = fmaf(s, fmaf(p[t], 16777216.f, -cx[t]), acc[b][m][t]);
       }
   };
 

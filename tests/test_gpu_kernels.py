@@ -239,7 +239,13 @@ def test_diagonal_weights_closed_form_on_gpu(M):
             v = xf[t, n]
             g = 0.5 * v
             expect[t, n] = 0.25 * (2.0 * v) * (g / (1.0 + math.exp(-g)))
-    assert np.all(out[:, I:] == 0.0)
+    if M > 2:
+        # MFMA tiles: a code-8 weight decodes to exactly zero
+        assert np.all(out[:, I:] == 0.0)
+    else:
+        # dot-product GEMV: the zero point is taken back as 8 * sum(x) per
+        # group, so all-8 rows leave only fp32 cancellation, far inside the bar
+        assert np.max(np.abs(out[:, I:])) <= 2.0 ** -10 * np.max(np.abs(expect))
     assert rel_err(out, expect) <= REL_TOL
 
 
