@@ -829,6 +829,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kGemvW
   // the first super-step's loads go out before the rows are staged
   Super fa, fb;
   if (S_end_full > S_begin) load_super(S_begin, fa, true);
+  // down: each row's slot and routing weight are read now, so their two
+  // dependent round trips overlap the weight stream instead of following it
+  int slot_of[kGemvRows];
+  float w_of[kGemvRows];
+  if (!GATEUP) {
+#pragma unroll
+    for (int t = 0; t < kGemvRows; ++t) slot_of[t] = t < nr ? g.perm[pos0 + t] : -1;
+#pragma unroll
+    for (int t = 0; t < kGemvRows; ++t) {
+      const int sl = slot_of[t];
+      w_of[t] = (sl >= 0 && sl < g.T) ? g.wts[sl] : 1.0f;
+    }
+  }
 
   // ---- stage the item's activation rows (operand format) in LDS: group
   // gi's four 16-byte runs at gi * 80 bytes
@@ -1009,9 +1022,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kGemvW
       const float hv = gt / (1.0f + __expf(-gt)) * up * ((col & 1) ? 0.0625f : 1.0f);
       g.h_out[(size_t)pos * g.N + ((col & ~7) | inv_perm8(col & 7))] = (_Float16)hv;
     } else {
-      const int slot = g.perm[pos];
+      const int slot = slot_of[t];
       if (slot < 0 || slot >= g.R) continue;
-      const float wv = slot < g.T ? g.wts[slot] : 1.0f;
+      const float wv = w_of[t];
 #pragma unroll
       for (int c = 0; c < NBW; ++c) {
         if (col0[c] >= g.N) continue;
