@@ -120,7 +120,18 @@ def main():
     ap.add_argument("--workload", default="decode", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--also-m", default="1", help="comma list of extra M values timed the same way")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only copy 1 GiB device to device 5 times (reference reading for the HBM byte counters)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied 1 GiB 5 times")
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
               "the layer would shard by experts across GPUs, which is not built.", file=sys.stderr)
