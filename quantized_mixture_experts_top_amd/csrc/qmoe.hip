@@ -124,8 +124,11 @@ __device__ void route_items(const RouteArgs& a, int* s_cnt, int* s_off, int* s_n
   block_exclusive_scan(s_ni, s_ioff, E + 1, s_wsum);
   for (int e = tid; e <= E; e += kRouteThreads) a.counts[e] = s_cnt[e];
   for (int e = tid; e <= E + 1; e += kRouteThreads) a.offsets[e] = s_off[e];
+  // the shared expert's items go first: it has a row for every token, so
+  // its tiles are the longest and should not be the last to start
+  const int nsh = s_ni[E];
   for (int e = tid; e <= E; e += kRouteThreads) {
-    const int base = s_ioff[e], n = s_cnt[e];
+    const int base = e == E ? 0 : s_ioff[e] + nsh, n = s_cnt[e];
     for (int i = 0; i < s_ni[e]; ++i) {
       const int r0 = i * a.bmc;
       if (base + i < a.max_items) a.items[base + i] = make_int4(e, r0, min(a.bmc, n - r0), s_off[e] + r0);
