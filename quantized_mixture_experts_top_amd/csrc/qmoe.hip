@@ -544,8 +544,30 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   __shared__ __attribute__((aligned(16))) _Float16 lds_a0[MB * 4 * kBlkHalves];
   __shared__ __attribute__((aligned(16))) _Float16 lds_a1[MB * 4 * kBlkHalves];
 #define QMOE_LDS_A(BUF) ((BUF) ? lds_a1 : lds_a0)
+  uint32_t sc_cur[NBB][4], sc_nxt[NBB][2];  // this super-step's scales by sub-step; the next one's, raw
+  Frag<NBB> fb0, fb1, fb2, fb3;  // the weights of sub-steps 0..3
+  // Down: the first weights go out before the item's rows are looked up,
+  // so the round trips of the lookups (sorted slot, routing weight) overlap
+  // theirs instead of preceding them.  (Gate+up issues them after: its
+  // 128 accumulators leave no room to hold them across the lookups.)
+  if (!GATEUP && S_end_full > S_begin) {
+    load_sc(S_begin, sc_nxt, true);
+    load_b(S_begin, 0, fb0, true);
+    load_b(S_begin, 1, fb1, true);
+  }
+  // per tile row: activation offset; down: also its slot and routing
+  // weight, read by the epilogue
   __shared__ uint32_t lds_row[MB * 16];
-  for (int m = tid; m < MB * 16; m += 64 * WN) lds_row[m] = m < nr ? a_off_of(m) : kOob;
+  __shared__ int lds_slot[GATEUP ? 1 : MB * 16];
+  __shared__ float lds_w[GATEUP ? 1 : MB * 16];
+  for (int m = tid; m < MB * 16; m += 64 * WN) {
+    lds_row[m] = m < nr ? a_off_of(m) : kOob;
+    if (!GATEUP) {
+      const int slot = m < nr ? g.perm[pos0 + m] : -1;
+      lds_slot[m] = slot;
+      lds_w[m] = (slot >= 0 && slot < g.T) ? g.wts[slot] : 1.0f;
+    }
+  }
   __syncthreads();
   // loads: per row block this wave loads, this lane's row (q = wave mod 4,
   // rr = lane/16) offset plus its segment and piece; rows past the item
@@ -566,8 +588,6 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   }
   // operand reads: lane (r, kq) reads row r = q + 4rr, segment kq, piece i
   const int rd_half = (r & 3) * kBlkHalves + 128 * (r >> 2) + 32 * ((kq + (r >> 2)) & 3);
-  uint32_t sc_cur[NBB][4], sc_nxt[NBB][2];  // this super-step's scales by sub-step; the next one's, raw
-  Frag<NBB> fb0, fb1, fb2, fb3;  // the weights of sub-steps 0..3
   auto promote_scales = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int b = 0; b < NBB; ++b) transpose_scales(sc_nxt[b][0], sc_nxt[b][1], sc_cur[b]);
@@ -634,11 +654,16 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
     constexpr int NMBC = decltype(nmbc_tag)::value;
     const int n = S_end_full - S_begin;
     if (n > 0) {
-      load_sc(S_begin, sc_nxt, true);
-      load_b(S_begin, 0, fb0, true);
-      QMOE_LOAD_A_TILE(S_begin, 0, true, 0);
-      load_b(S_begin, 1, fb1, true);
-      wait_vmcnt<NBB>();
+      if (GATEUP) {
+        load_sc(S_begin, sc_nxt, true);
+        load_b(S_begin, 0, fb0, true);
+        QMOE_LOAD_A_TILE(S_begin, 0, true, 0);
+        load_b(S_begin, 1, fb1, true);
+        wait_vmcnt<NBB>();
+      } else {  // the first two sub-steps' weights are already in flight
+        QMOE_LOAD_A_TILE(S_begin, 0, true, 0);
+        wait_vmcnt<0>();
+      }
       __syncthreads();
       promote_scales();
       for (int S = S_begin; S < S_end_full; ++S) {
@@ -696,9 +721,9 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
           const float hv = gt / (1.0f + __expf(-gt)) * up * ((col & 1) ? 0.0625f : 1.0f);
           g.h_out[(size_t)pos * g.N + ((col & ~7) | inv_perm8(col & 7))] = (_Float16)hv;
         } else {
-          const int slot = g.perm[pos];
+          const int slot = lds_slot[row];
           if (slot < 0 || slot >= g.R) continue;
-          const float wv = slot < g.T ? g.wts[slot] : 1.0f;
+          const float wv = lds_w[row];
           g.y_out[(size_t)slot * g.N + col] = (uint16_t)f32_to_bf16_rne(wv * acc[mb][c][i]);
         }
       }
