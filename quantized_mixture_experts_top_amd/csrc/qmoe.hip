@@ -442,9 +442,11 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   // 8), so the item's activation rows are reused from that XCD's L2
   const int bid = blockIdx.x, xcd = bid & 7, jj = bid >> 3;
   const int item = (jj / g.nblk) * 8 + xcd, nb = jj % g.nblk;
+  // the item is read together with the item count (clamped into the list,
+  // so both loads go out at once; a block past the count then returns)
+  const int4 it = g.items[min(item, g.max_items - 1)];
   const int n_items = min(g.ctrl[1], g.max_items);
   if (item >= n_items) return;
-  const int4 it = g.items[item];
   const int e = it.x, nr = it.z, pos0 = it.w;
   // work items come from the workspace: reject any that do not fit it
   if (e < 0 || e > g.E || nr <= 0 || nr > MB * 16 || pos0 < 0 || pos0 > g.R - nr) return;
@@ -788,9 +790,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kGemvW
   // consecutive blocks take consecutive column blocks of one item, so each
   // item's stream is spread over all XCDs
   const int item = blockIdx.x / g.nblk, nb = blockIdx.x % g.nblk;
+  // the item is read together with the item count (clamped into the list,
+  // so both loads go out at once; a block past the count then returns)
+  const int4 it = g.items[min(item, g.max_items - 1)];
   const int n_items = min(g.ctrl[1], g.max_items);
   if (item >= n_items) return;
-  const int4 it = g.items[item];
   const int e = it.x, nr = it.z, pos0 = it.w;
   if (e < 0 || e > g.E || nr <= 0 || nr > kGemvRows || pos0 < 0 || pos0 > g.R - nr) return;
   const uint32_t K2 = (uint32_t)g.K / 2, KG = (uint32_t)g.K / 32;
