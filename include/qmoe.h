@@ -32,9 +32,10 @@
  * = SiLU(gate)*up is held in fp16, so |x| and |h| must stay below 65504.
  * Which kernel a call uses depends on the average number of routed rows per
  * expert, M*top_k/E:
- *   <= 1.75   dot-product GEMV on items of <= 2 rows: sum of x*(c-8) per
- *             32-input group in fp32 (exact integer codes), times the
- *             group's scale in fp32;
+ *   <= 1.75   dot-product GEMV on items of <= 2 rows: per 32-input group,
+ *             sum(x*c) in fp32 (exact products) minus 8*sum(x), times the
+ *             group's scale in fp32 (an all-8 group is zero only up to
+ *             fp32 cancellation);
  *   > 1.75    128-row MFMA tiles: codes decoded to fp16 operands
  *             ((c-8)*scale rounded to nearest even), products accumulated
  *             in fp32 by MFMA.
