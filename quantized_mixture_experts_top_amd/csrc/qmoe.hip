@@ -75,74 +75,72 @@ constexpr int kRouteThreads = 1024;  // routing blocks: 16 waves
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kXRuns = 8 * kRouteThreads;  // 16-byte runs of x per conversion block
 
-// Exclusive scan of in[0..n) into out[0..n] (out[n] = total) by the 1024
-// threads of a routing block: each thread sums 2 consecutive entries, a
-// wave-wide Hillis-Steele scan over lanes combines them, then the 16 wave
-// totals.  This replaces a serial loop over the expert counts.
-__device__ void block_exclusive_scan(const int* in, int* out, int n, int* wsum) {
-  constexpr int kPer = 2;  // 1024 * 2 >= QMOE_MAX_EXPERTS + 1
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int v[kPer];
-  int local = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int idx = tid * kPer + i;
-    v[i] = idx < n ? in[idx] : 0;
-    local += v[i];
-  }
-  int incl = local;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  int run = incl - local;
-  for (int w = 0; w < wave; ++w) run += wsum[w];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int idx = tid * kPer + i;
-    if (idx < n) out[idx] = run;
-    run += v[i];
-  }
-  if (tid == kRouteThreads - 1) out[n] = run;
-  __syncthreads();
-}
-
-// Counts, offsets, work items and positions from the per-expert token masks
-// of a chunk, all in LDS: used when the whole call is one chunk (M <= 64).
-// Shared by the multi-chunk path's tail: the items and the scan are built
-// the same way there from counts gathered over chunks.
-__device__ void route_items(const RouteArgs& a, int* s_cnt, int* s_off, int* s_ni, int* s_ioff, int* s_wsum) {
-  const int tid = threadIdx.x, E = a.E;
+// Counts, offsets and the flat work list from the per-expert row counts in
+// s_cnt[0..E) (the caller's threads wrote them before calling), all in LDS:
+// used when the whole call is one chunk (M <= 64) and by the multi-chunk
+// path's last block.  One wave does both exclusive scans (row offsets and
+// work-item offsets) over the E+1 entries at once: lane l sums its run of
+// ceil((E+1)/64) consecutive experts, a 6-step shuffle scan combines the
+// 64 lane totals, and each lane walks its run again to write offsets and
+// items.  This replaces a serial loop over the expert counts, and needs no
+// block barrier between the two scans.  The shared expert (entry E, a row
+// per token) gets the first items: its tiles are the longest of a call and
+// should not be the last to start.
+__device__ void route_items(const RouteArgs& a, int* s_cnt, int* s_off) {
+  const int tid = threadIdx.x, E = a.E, n = E + 1, bmc = a.bmc;
   if (tid == 0) s_cnt[E] = a.S;  // the shared expert takes every token
   __syncthreads();
-  for (int e = tid; e <= E; e += kRouteThreads) s_ni[e] = (s_cnt[e] + a.bmc - 1) / a.bmc;
-  __syncthreads();
-  block_exclusive_scan(s_cnt, s_off, E + 1, s_wsum);
-  block_exclusive_scan(s_ni, s_ioff, E + 1, s_wsum);
-  for (int e = tid; e <= E; e += kRouteThreads) a.counts[e] = s_cnt[e];
-  for (int e = tid; e <= E + 1; e += kRouteThreads) a.offsets[e] = s_off[e];
-  // the shared expert's items go first: it has a row for every token, so
-  // its tiles are the longest and should not be the last to start
-  const int nsh = s_ni[E];
-  for (int e = tid; e <= E; e += kRouteThreads) {
-    const int base = e == E ? 0 : s_ioff[e] + nsh, n = s_cnt[e];
-    for (int i = 0; i < s_ni[e]; ++i) {
-      const int r0 = i * a.bmc;
-      if (base + i < a.max_items) a.items[base + i] = make_int4(e, r0, min(a.bmc, n - r0), s_off[e] + r0);
+  if (tid < 64) {
+    const int lane = tid, per = (n + 63) / 64, e0 = lane * per;
+    int c_loc = 0, i_loc = 0;
+    for (int u = 0; u < per; ++u) {
+      const int e = e0 + u;
+      if (e < n) {
+        const int c = s_cnt[e];
+        c_loc += c;
+        i_loc += (c + bmc - 1) / bmc;
+      }
+    }
+    int c_inc = c_loc, i_inc = i_loc;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int oc = __shfl_up(c_inc, off, 64), oi = __shfl_up(i_inc, off, 64);
+      if (lane >= off) {
+        c_inc += oc;
+        i_inc += oi;
+      }
+    }
+    const int nsh = (a.S + bmc - 1) / bmc;  // the shared expert's items
+    int c_run = c_inc - c_loc, i_run = i_inc - i_loc;
+    for (int u = 0; u < per; ++u) {
+      const int e = e0 + u;
+      if (e >= n) break;
+      const int c = s_cnt[e], ni = (c + bmc - 1) / bmc;
+      s_off[e] = c_run;
+      a.counts[e] = c;
+      a.offsets[e] = c_run;
+      const int base = e == E ? 0 : i_run + nsh;
+      for (int i = 0; i < ni; ++i) {
+        const int r0 = i * bmc;
+        if (base + i < a.max_items) a.items[base + i] = make_int4(e, r0, min(bmc, c - r0), c_run + r0);
+      }
+      c_run += c;
+      i_run += ni;
+    }
+    if (lane == 63) {
+      s_off[n] = c_run;
+      a.offsets[n] = c_run;
+      a.ctrl[1] = min(i_run, a.max_items);
     }
   }
-  if (tid == 0) a.ctrl[1] = min(s_ioff[E + 1], a.max_items);
+  __syncthreads();
 }
 
 __device__ void route_finish_single(const RouteArgs& a, const uint32_t (*cm)[2], const int* s_ids, int* s_cnt,
-                                    int* s_off, int* s_ni, int* s_ioff, int* s_wsum) {
+                                    int* s_off) {
   const int tid = threadIdx.x, E = a.E, k = a.k;
   for (int e = tid; e < E; e += kRouteThreads) s_cnt[e] = __popc(cm[e][0]) + __popc(cm[e][1]);
-  route_items(a, s_cnt, s_off, s_ni, s_ioff, s_wsum);
-  __syncthreads();
+  route_items(a, s_cnt, s_off);
   // slot (t, j): its expert's offset plus the number of lower tokens routed
   // to that expert (each token selects an expert at most once)
   for (int f = tid; f < a.M * k; f += kRouteThreads) {
@@ -166,9 +164,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   __shared__ uint32_t cm[QMOE_MAX_EXPERTS][2];
   __shared__ int s_cnt[QMOE_MAX_EXPERTS + 2];
   __shared__ int s_off[QMOE_MAX_EXPERTS + 2];
-  __shared__ int s_ni[QMOE_MAX_EXPERTS + 2];
-  __shared__ int s_ioff[QMOE_MAX_EXPERTS + 2];
-  __shared__ int s_wsum[kRouteWaves];
   __shared__ int s_last;
   __shared__ int s_ids[kChunk * QMOE_MAX_TOPK];  // the chunk's selected experts
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -249,7 +244,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
 
   __syncthreads();
   if (a.C == 1) {
-    route_finish_single(a, cm, s_ids, s_cnt, s_off, s_ni, s_ioff, s_wsum);
+    route_finish_single(a, cm, s_ids, s_cnt, s_off);
     return;
   }
   for (int e = tid; e < E; e += kRouteThreads)
@@ -293,7 +288,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
       s_cnt[e] = run;
     }
   }
-  route_items(a, s_cnt, s_off, s_ni, s_ioff, s_wsum);
+  route_items(a, s_cnt, s_off);
   __threadfence();
   __syncthreads();
   // sorted position of every routed slot: expert offset + rank of the
