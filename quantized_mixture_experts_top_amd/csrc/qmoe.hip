@@ -7,6 +7,9 @@
 //                   (expert, row tile) work items, x -> fp16 operand format
 //   gemm_kernel<..., true>   stacked gate+up product with h = SiLU(g)*u
 //   gemm_kernel<..., false>  down product times the routing weight
+//                   (128-row MFMA tiles; calls averaging at most 1.75 routed
+//                   rows per expert run gemv_kernel<..., true / false>, the
+//                   same two products as packed fp16 dot products)
 //   combine_kernel  out[t] = sum over slots in order (+ shared expert)
 //
 // Layer definition: "The MoE Throughput Lever: Quantifying the INT4 Marlin
