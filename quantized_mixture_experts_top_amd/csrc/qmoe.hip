@@ -595,15 +595,17 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   // this wave's blocks of sub-step U of super-step S into buffer BUF, for
   // the NMBC row blocks in use (NMBC is a multiple of WN/4); lanes whose
   // group is past K (OK false) read zeros
-#define QMOE_LOAD_A_TILE(S, U, OK, BUF)                                                          \
+#define QMOE_LOAD_A_TILE_AT(S, U, OK, BUF, SLOT0)                                                \
   do {                                                                                           \
     _Pragma("unroll") for (int t = 0; t < NA; ++t) {                                             \
       if (t < NMBC / MBS)                                                                        \
-        load_lds16(rA, &QMOE_LDS_A(BUF)[((amb0 + MBS * t) * 4 + aq) * kBlkHalves],                \
+        load_lds16(rA, &QMOE_LDS_A(BUF)[(((SLOT0) + amb0 + MBS * t) * 4 + aq) * kBlkHalves],      \
                    (OK) ? aoffs[t] : kOob, (S) * (kSuper * 2) + 256 * (U));                      \
     }                                                                                            \
   } while (0)
-#define QMOE_COMPUTE(F, SC, U, BUF)                                                              \
+#define QMOE_LOAD_A_TILE(S, U, OK, BUF) QMOE_LOAD_A_TILE_AT(S, U, OK, BUF, 0)
+#define QMOE_COMPUTE(F, SC, U, BUF) QMOE_COMPUTE_AT(F, SC, U, BUF, 0)
+#define QMOE_COMPUTE_AT(F, SC, U, BUF, SLOT0)                                                    \
   do {                                                                                           \
     uint32_t s2_[NBB];                                                                           \
     _Pragma("unroll") for (int b = 0; b < NBB; ++b) s2_[b] = (SC)[b][(U)];                       \
@@ -617,7 +619,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
       _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                                        \
         if (mb < NMBC) {                                                                         \
           const half8_t av =                                                                     \
-              *reinterpret_cast<const half8_t*>(&QMOE_LDS_A(BUF)[mb * 4 * kBlkHalves + rd_half + 8 * i]); \
+              *reinterpret_cast<const half8_t*>(&QMOE_LDS_A(BUF)[((SLOT0) + mb) * 4 * kBlkHalves + rd_half + 8 * i]); \
           _Pragma("unroll") for (int b = 0; b < NBB; ++b) acc[mb][b] = mfma16x16x32(av, cur_[b], acc[mb][b]); \
         }                                                                                        \
       }                                                                                          \
@@ -693,13 +695,92 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
       }
     }
   };
-  if (nmb <= 2) kloop(std::integral_constant<int, (MB < 2 ? MB : 2)>{});
-  else if (nmb <= 4) kloop(std::integral_constant<int, (MB < 4 ? MB : 4)>{});
+  // Down items of at most 32 rows: a whole super-step of their activation
+  // tile (4 sub-steps x 2 row blocks) fits one buffer, so the block loads
+  // the next super-step's tile and weights at once, one super-step ahead,
+  // and meets one barrier per super-step instead of one per sub-step.  With
+  // so few rows a sub-step is only 8 MFMAs per wave, far shorter than a trip
+  // to memory; this doubles the bytes each wave keeps in flight.
+  auto kloop_ss = [&]() __attribute__((always_inline)) {
+    constexpr int NMBC = 2;
+    static_assert(MB >= 4 * NMBC, "a super-step of 2-block tiles fits one buffer");
+    Frag<NBB> fc0, fc1, fc2, fc3;  // the other super-step's weights
+    if (S_end_full > S_begin) {
+      // fb0, fb1 and the scales of the first super-step are in flight
+      load_b(S_begin, 2, fb2, true);
+      load_b(S_begin, 3, fb3, true);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) QMOE_LOAD_A_TILE_AT(S_begin, u, true, 0, u * NMBC);
+      wait_vmcnt<0>();
+      __syncthreads();
+      promote_scales();
+      for (int S = S_begin; S < S_end_full; S += 2) {
+        // super-step S from buffer 0 and fb*, while S + 1 comes into
+        // buffer 1 and fc* (past the range every lane reads zeros)
+        const bool more1 = S + 1 < S_end_full;
+        load_sc(S + 1, sc_nxt, more1);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) QMOE_LOAD_A_TILE_AT(S + 1, u, more1, 1, u * NMBC);
+        load_b(S + 1, 0, fc0, more1);
+        load_b(S + 1, 1, fc1, more1);
+        load_b(S + 1, 2, fc2, more1);
+        load_b(S + 1, 3, fc3, more1);
+        __builtin_amdgcn_sched_barrier(0);
+        QMOE_COMPUTE_AT(fb0, sc_cur, 0, 0, 0 * NMBC);
+        QMOE_COMPUTE_AT(fb1, sc_cur, 1, 0, 1 * NMBC);
+        QMOE_COMPUTE_AT(fb2, sc_cur, 2, 0, 2 * NMBC);
+        QMOE_COMPUTE_AT(fb3, sc_cur, 3, 0, 3 * NMBC);
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (!more1) break;
+        promote_scales();
+        // super-step S + 1 from buffer 1 and fc*, while S + 2 comes into
+        // buffer 0 and fb*
+        const bool more2 = S + 2 < S_end_full;
+        load_sc(S + 2, sc_nxt, more2);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) QMOE_LOAD_A_TILE_AT(S + 2, u, more2, 0, u * NMBC);
+        load_b(S + 2, 0, fb0, more2);
+        load_b(S + 2, 1, fb1, more2);
+        load_b(S + 2, 2, fb2, more2);
+        load_b(S + 2, 3, fb3, more2);
+        __builtin_amdgcn_sched_barrier(0);
+        QMOE_COMPUTE_AT(fc0, sc_cur, 0, 1, 0 * NMBC);
+        QMOE_COMPUTE_AT(fc1, sc_cur, 1, 1, 1 * NMBC);
+        QMOE_COMPUTE_AT(fc2, sc_cur, 2, 1, 2 * NMBC);
+        QMOE_COMPUTE_AT(fc3, sc_cur, 3, 1, 3 * NMBC);
+        wait_vmcnt<0>();
+        __syncthreads();
+        promote_scales();
+      }
+    }
+    if (has_tail) {  // the partial super-step: groups past K read zeros
+      load_sc(nss_full, sc_nxt, true);
+      promote_scales();
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool okb = nss_full * 16 + 4 * u + kq < ngroups;
+        const bool oka = nss_full * 16 + 4 * u + aseg < ngroups;
+        __syncthreads();  // every wave is done reading buffer 0
+        load_b(nss_full, u, fb0, okb);
+        QMOE_LOAD_A_TILE(nss_full, u, oka, 0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        QMOE_COMPUTE(fb0, sc_cur, u, 0);
+      }
+    }
+  };
+  if (nmb <= 2) {
+    if constexpr (!GATEUP && MB >= 8) kloop_ss();
+    else kloop(std::integral_constant<int, (MB < 2 ? MB : 2)>{});
+  } else if (nmb <= 4) kloop(std::integral_constant<int, (MB < 4 ? MB : 4)>{});
   else if (nmb <= 6) kloop(std::integral_constant<int, (MB < 6 ? MB : 6)>{});
   else kloop(std::integral_constant<int, MB>{});
 #undef QMOE_SUBSTEP
 #undef QMOE_COMPUTE
+#undef QMOE_COMPUTE_AT
 #undef QMOE_LOAD_A_TILE
+#undef QMOE_LOAD_A_TILE_AT
 #undef QMOE_LDS_A
 
   // ---- epilogue: lane holds rows mb*16 + 4*kq + i of column r of each block
