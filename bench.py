@@ -114,12 +114,18 @@ def cpu_baseline(shape, M, skew, budget_s=20.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # defaults: small calls (at most 64 tokens, well under a millisecond each)
+    # get 50 warmup and 100 timed steps so the timed region runs at the
+    # GPU's steady clocks; larger calls 5 and 20 (each step has its own
+    # inputs, generated on the host)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--m", type=int, default=9)
     ap.add_argument("--workload", default="decode", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--also-m", default="1", help="comma list of extra M values timed the same way")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the forward captured into one HIP graph per step and replayed back to back")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy 1 GiB device to device 5 times (reference reading for the HBM byte counters)")
     args = ap.parse_args()
@@ -144,6 +150,11 @@ def main():
     shape = wl.shape
     Ms = [args.m] + [int(v) for v in args.also_m.split(",") if v.strip() and int(v) != args.m]
     max_rows = max(Ms)
+    small = max_rows <= 64
+    if args.steps is None:
+        args.steps = 100 if small else 20
+    if args.warmup is None:
+        args.warmup = 50 if small else 5
     t0 = time.time()
     w, shared = upload_weights(0, shape)
     log(f"weights uploaded in {time.time() - t0:.1f} s")
@@ -194,6 +205,31 @@ def main():
             e[4].record(stream)
         torch.cuda.synchronize()
         stage = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)] for i in range(args.steps)])
+        # ---- optional: the same steps as captured graphs (one per step's inputs)
+        graph = None
+        if args.graph:
+            outs = [torch.empty_like(out) for _ in range(n)]
+            graphs = []
+            torch.cuda.synchronize()
+            for s in range(n):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    layer.forward(xs[s], ls[s], out=outs[s])
+                graphs.append(g)
+            for s in range(args.warmup):
+                graphs[s].replay()
+            torch.cuda.synchronize()
+            gv0, gv1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            gv0.record(stream)
+            for s in range(args.warmup, n):
+                graphs[s].replay()
+            gv1.record(stream)
+            torch.cuda.synchronize()
+            eager_last = layer.forward(xs[n - 1], ls[n - 1])
+            torch.cuda.synchronize()
+            graph = {"us_per_call": gv0.elapsed_time(gv1) / args.steps * 1e3,
+                     "matches_eager": bool(torch.equal(outs[n - 1].view(torch.int16), eager_last.view(torch.int16)))}
+            del graphs, outs
         st_ms = stage.mean(axis=0)
         tt = np.array(touched[args.warmup:], dtype=np.float64)
         alg_bytes = tt * (b13 + b2) + M * shape.H * 2 + M * shape.E * 4 + M * shape.H * 2
@@ -214,6 +250,11 @@ def main():
             "gate_up_bytes_per_launch": float(gu_bytes.mean()),
             "gate_up_us": float(st_ms[1] * 1e3),
         }
+        if graph is not None:
+            results[M]["graph_us_per_call"] = graph["us_per_call"]
+            results[M]["graph_matches_eager"] = graph["matches_eager"]
+        if graph is not None:
+            log(f"M={M}: graph replay {graph['us_per_call']:.1f} us/call (matches eager: {graph['matches_eager']})")
         log(f"M={M}: {ms * 1e3:.1f} us/call, {results[M]['tokens_per_s']:.0f} tok/s, "
             f"{results[M]['layer_GBps']:.0f} GB/s layer, stages(us) "
             + ", ".join(f"{k}={v:.1f}" for k, v in results[M]["stage_us"].items()))
