@@ -649,9 +649,10 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
     __syncthreads();                                                                             \
   } while (0)
   // The row blocks that hold routed rows are computed without a branch per
-  // block: the loop is instantiated for 2, 4, 6 and 8 blocks and the
-  // item's count rounds up to the next of these (blocks past the item's
-  // rows multiply zero rows, which are never stored).
+  // block: the loop is instantiated for 2, 4, 6 and 8 blocks (gate+up also
+  // 5 and 7: about 85 rows per expert at 4096 tokens) and the item's count
+  // rounds up to the next of these (blocks past the item's rows multiply
+  // zero rows, which are never stored).
   auto kloop = [&](auto nmbc_tag) __attribute__((always_inline)) {
     constexpr int NMBC = decltype(nmbc_tag)::value;
     const int n = S_end_full - S_begin;
@@ -774,7 +775,9 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
     if constexpr (!GATEUP && MB >= 8) kloop_ss();
     else kloop(std::integral_constant<int, (MB < 2 ? MB : 2)>{});
   } else if (nmb <= 4) kloop(std::integral_constant<int, (MB < 4 ? MB : 4)>{});
+  else if (GATEUP && MB == 8 && nmb == 5) kloop(std::integral_constant<int, 5>{});
   else if (nmb <= 6) kloop(std::integral_constant<int, (MB < 6 ? MB : 6)>{});
+  else if (GATEUP && MB == 8 && nmb == 7) kloop(std::integral_constant<int, 7>{});
   else kloop(std::integral_constant<int, MB>{});
 #undef QMOE_SUBSTEP
 #undef QMOE_COMPUTE
