@@ -140,6 +140,10 @@ FWD_CASES = [
     (1024, 128, 128, 8, 20, True),   # 1024 experts (the most), shared expert
     (4, 13056, 128, 2, 3, False),    # the largest K the GEMV stages in LDS
     (4, 13184, 128, 1, 2, False),    # K past the GEMV's LDS: small M on tiles
+    (16, 256, 1664, 2, 64, False),   # tiles: down items of <= 32 rows, 3 whole super-steps + a partial one
+    (16, 256, 1024, 2, 64, True),    # tiles: down items of <= 32 rows, 2 whole super-steps; shared expert
+    (4, 256, 128, 1, 300, False),    # tiles: items of 4, 5 and 6 row blocks
+    (4, 256, 128, 1, 400, False),    # tiles: items of 6 and 7 row blocks
 ]
 
 
