@@ -61,6 +61,8 @@ struct RouteArgs {
   const float* logits;
   const uint4* x;  // bf16 [M, H] as 16-byte runs
   int M, E, H, k, S, C, bmc, max_items;
+  int subs;  // routing blocks per chunk (1, or kSubs for 2..kMaxSplitChunks chunks)
+  int nrb;   // routing blocks: C * subs
   int* ctrl;
   int* ids;
   float* wts;
@@ -77,6 +79,8 @@ struct RouteArgs {
 constexpr int kRouteThreads = 1024;  // routing blocks: 16 waves
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kXRuns = 8 * kRouteThreads;  // 16-byte runs of x per conversion block
+constexpr int kSubs = 4;                    // routing blocks per chunk for calls of 2..kMaxSplitChunks chunks
+constexpr int kMaxSplitChunks = 16;         // beyond, one block per chunk: the per-block fences dominate
 
 // Counts, offsets and the flat work list from the per-expert row counts in
 // s_cnt[0..E) (the caller's threads wrote them before calling), all in LDS:
@@ -157,11 +161,15 @@ __device__ void route_finish_single(const RouteArgs& a, const uint32_t (*cm)[2],
   for (int t = tid; t < a.S; t += kRouteThreads) a.perm[T + t] = T + t;
 }
 
-// One block per chunk of 64 tokens; the last block to finish (atomic ticket,
-// no waiting) turns the per-chunk token masks into counts, offsets,
-// positions and work items.  The blocks after those convert x to the fp16
-// operand format in slices (they take no part in the ticket).  EPL =
-// logits per lane (E <= 64 * EPL).
+// A call of at most 64 tokens (one chunk) is routed by one block, which
+// finishes in LDS.  With several chunks, each chunk of 64 tokens gets one
+// block, or, for up to kMaxSplitChunks chunks, kSubs blocks of 16 tokens
+// (one per wave: the top-k is compute bound inside a CU) that OR their
+// tokens' bits into the chunk's masks in global memory; the last block to
+// finish (atomic ticket, no waiting) turns the masks into counts, offsets,
+// positions and work items.  The blocks after the routing blocks convert x
+// to the fp16 operand format in slices (they take no part in the ticket).
+// EPL = logits per lane (E <= 64 * EPL).
 template <int EPL>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   __shared__ uint32_t cm[QMOE_MAX_EXPERTS][2];
@@ -170,14 +178,18 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   __shared__ int s_last;
   __shared__ int s_ids[kChunk * QMOE_MAX_TOPK];  // the chunk's selected experts
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = blockIdx.x, E = a.E, k = a.k;
-  const int rows = min(kChunk, a.M - c * kChunk);
+  const int E = a.E, k = a.k;
+  const int c = blockIdx.x / a.subs;                // chunk
+  const int rows = min(kChunk, a.M - c * kChunk);    // the chunk's tokens
+  // this block's tokens of the chunk: [t_lo, t_hi)
+  const int t_lo = (blockIdx.x % a.subs) * (kChunk / a.subs);
+  const int t_hi = min(rows, t_lo + kChunk / a.subs);
 
-  // blocks past the C routing blocks convert x to the fp16 operand format,
+  // blocks past the routing blocks convert x to the fp16 operand format,
   // kXRuns 16-byte runs each, spread over the GPU
-  if (c >= a.C) {
+  if ((int)blockIdx.x >= a.nrb) {
     const long long n = (long long)a.M * (a.H / 8);
-    const long long q0 = (long long)(c - a.C) * kXRuns + tid;
+    const long long q0 = (long long)((int)blockIdx.x - a.nrb) * kXRuns + tid;
     uint4 v[kXRuns / kRouteThreads];
 #pragma unroll
     for (int u = 0; u < kXRuns / kRouteThreads; ++u) v[u] = a.x[min(q0 + (long long)u * kRouteThreads, n - 1)];  // clamped
@@ -193,7 +205,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   __syncthreads();
 
   // ---- phase 1a: top-k of each token, one wave per token
-  for (int tl = wave; tl < rows; tl += kRouteWaves) {
+  for (int tl = t_lo + wave; tl < t_hi; tl += kRouteWaves) {
     const int t = c * kChunk + tl;
     const float* row = a.logits + (size_t)t * E;
     // key = order-preserving bits of the logit (every finite logit maps
@@ -250,20 +262,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     route_finish_single(a, cm, s_ids, s_cnt, s_off);
     return;
   }
-  for (int e = tid; e < E; e += kRouteThreads)
-    a.cmask[(size_t)c * E + e] = (unsigned long long)cm[e][0] | ((unsigned long long)cm[e][1] << 32);
-  if (a.C > 1) {
-    // several blocks: the last one to arrive (device-scope ticket) finishes
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(a.ctrl, 1) == a.C - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-  } else {
-    // one block (M <= 64): its own writes are visible to it after a barrier
-    __syncthreads();
+  // this block's token bits into the chunk's masks: stored by the chunk's
+  // only block, or OR-ed into masks zeroed before the call
+  for (int e = tid; e < E; e += kRouteThreads) {
+    const unsigned long long m = (unsigned long long)cm[e][0] | ((unsigned long long)cm[e][1] << 32);
+    if (a.subs == 1) a.cmask[(size_t)c * E + e] = m;
+    else if (m != 0ull) atomicOr(&a.cmask[(size_t)c * E + e], m);
   }
+  // the last routing block to arrive (device-scope ticket) finishes
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = (atomicAdd(a.ctrl, 1) == a.nrb - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
 
   // ---- phase 2 (last block only)
   // per expert (one thread each), walk the chunks in order: the count, and
@@ -1228,6 +1240,14 @@ __global__ void init_ctrl_kernel(int* ctrl) {
   if (threadIdx.x < kCtrlWords) ctrl[threadIdx.x] = 0;
 }
 
+// Clears the routing ticket and the n per-chunk token masks of a call with
+// several chunks (the routing blocks OR their tokens' bits into them).
+__global__ __launch_bounds__(kThreads) void init_route_kernel(int* ctrl, unsigned long long* cmask, long long n) {
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (blockIdx.x == 0 && threadIdx.x < kCtrlWords) ctrl[threadIdx.x] = 0;
+  if (i < n) cmask[i] = 0ull;
+}
+
 // ============================================================= host side
 
 thread_local std::string g_err;
@@ -1382,16 +1402,21 @@ int do_route(qmoe_layer* L, const void* x, const float* logits, int64_t M, void*
   a.inv_perm = at<int>(ws, lay.inv_perm);
   a.items = at<int4>(ws, lay.items);
   a.xa = at<uint4>(ws, lay.xa);
+  a.subs = (lay.C > 1 && lay.C <= kMaxSplitChunks) ? kSubs : 1;
+  a.nrb = (int)lay.C * a.subs;
   if (lay.C > 1) {
-    // several routing blocks meet at a ticket: clear it first (the call
-    // then does not depend on what the workspace held before)
-    init_ctrl_kernel<<<1, kCtrlWords, 0, st>>>(a.ctrl);
-    const int rc = check_launch(L, "ticket clear");
+    // several routing blocks meet at a ticket (and, when chunks are split,
+    // OR into the chunk masks): clear them first (the call then does not
+    // depend on what the workspace held before)
+    const long long n = a.subs > 1 ? lay.C * (long long)L->d.E : 0;
+    init_route_kernel<<<dim3((unsigned)std::max<long long>(1, ceil_div(n, kThreads))), kThreads, 0, st>>>(
+        a.ctrl, a.cmask, n);
+    const int rc = check_launch(L, "ticket and mask clear");
     if (rc != QMOE_OK) return rc;
   }
   // routing blocks, then the blocks that convert x
   const int64_t xblocks = ceil_div(M * (L->d.H / 8), (int64_t)kXRuns);
-  const dim3 grid((unsigned)(lay.C + xblocks));
+  const dim3 grid((unsigned)(a.nrb + xblocks));
   const int epl = (L->d.E + 63) / 64;
   if (epl <= 1) route_kernel<1><<<grid, kRouteThreads, 0, st>>>(a);
   else if (epl <= 2) route_kernel<2><<<grid, kRouteThreads, 0, st>>>(a);
