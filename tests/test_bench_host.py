@@ -1,0 +1,41 @@
+"""Host-side parts of the benchmark that need no GPU: the one-GPU guard,
+the CPU oracle baseline record, and the algorithmic byte count the
+roofline is priced on."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
+    assert res.stdout == ""  # no JSON line for a configuration that was not run
+
+
+def test_cpu_baseline_record():
+    rec = bench.cpu_baseline(synth.TINY, 16, False)
+    assert rec["kind"] == "oracle" and rec["unit"] == "tokens/s"
+    assert rec["value"] > 0 and rec["cores"] >= 1
+    assert "routing for all 16" in rec["sample"]  # the sample says what was timed
+
+
+@pytest.mark.parametrize("shape", [synth.TINY, synth.FULL])
+def test_bytes_per_expert_closed_form(shape):
+    """Codes are half a byte per weight and every 32 inputs of a row share
+    one 2-byte scale: gate+up has 2I rows of H inputs, down H rows of I."""
+    H, I = shape.H, shape.I
+    w13, w2 = bench.bytes_per_expert(shape)
+    assert w13 == 2 * I * H // 2 + 2 * (2 * I * H // 32)
+    assert w2 == H * I // 2 + 2 * (H * I // 32)
+    if shape is synth.FULL:  # the 384-expert layer's figures
+        assert (w13, w2) == (16_515_072, 8_257_536)
