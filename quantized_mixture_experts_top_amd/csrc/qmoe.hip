@@ -1421,6 +1421,7 @@ int do_route(qmoe_layer* L, const void* x, const float* logits, int64_t M, void*
   if (epl <= 1) route_kernel<1><<<grid, kRouteThreads, 0, st>>>(a);
   else if (epl <= 2) route_kernel<2><<<grid, kRouteThreads, 0, st>>>(a);
   else if (epl <= 4) route_kernel<4><<<grid, kRouteThreads, 0, st>>>(a);
+  else if (epl <= 6) route_kernel<6><<<grid, kRouteThreads, 0, st>>>(a);  // 257-384 experts
   else if (epl <= 8) route_kernel<8><<<grid, kRouteThreads, 0, st>>>(a);
   else route_kernel<16><<<grid, kRouteThreads, 0, st>>>(a);
   L->route_calls++;
