@@ -205,6 +205,8 @@ def main():
             e[4].record(stream)
         torch.cuda.synchronize()
         stage = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)] for i in range(args.steps)])
+        # per-call distribution from the same bracketed loop (first to last event of each call)
+        per_call_us = np.array([evs[i][0].elapsed_time(evs[i][4]) for i in range(args.steps)]) * 1e3
         # ---- optional: the same steps as captured graphs (one per step's inputs)
         graph = None
         if args.graph:
@@ -249,6 +251,7 @@ def main():
                                             * shape.I / (stage[:, 1] * 1e-3)) / 1e12),
             "gate_up_bytes_per_launch": float(gu_bytes.mean()),
             "gate_up_us": float(st_ms[1] * 1e3),
+            "bracketed_call_us_p10_p50_p90": [float(np.percentile(per_call_us, q)) for q in (10, 50, 90)],
         }
         if graph is not None:
             results[M]["graph_us_per_call"] = graph["us_per_call"]
@@ -307,7 +310,8 @@ def main():
         "us_per_token": round(r["us_per_token"], 3),
         "roofline": roof,
         "per_M": {str(m): {k: (round(v, 3) if isinstance(v, float) else
-                               {kk: round(vv, 2) for kk, vv in v.items()} if isinstance(v, dict) else v)
+                               {kk: round(vv, 2) for kk, vv in v.items()} if isinstance(v, dict) else
+                               [round(vv, 2) for vv in v] if isinstance(v, list) else v)
                            for k, v in results[m].items()} for m in Ms},
     }
     if not args.no_cpu_baseline:
