@@ -125,7 +125,8 @@ int qmoe_workspace_size(const qmoe_layer* layer, int64_t M, size_t* bytes);
 
 /* Enqueue a clear of a workspace's control words.  Optional: the calls do
    not depend on what a workspace held before (a call that routes more than
-   64 tokens clears the routing ticket itself, one extra tiny launch). */
+   64 tokens clears the routing ticket, and for up to 1024 tokens the
+   per-chunk token masks, itself: one extra small launch). */
 int qmoe_workspace_init(qmoe_layer* layer, void* workspace, size_t ws_bytes, void* stream);
 
 /* The whole layer: route, gate+up, down, combine (four kernel launches).
