@@ -697,6 +697,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
       promote_scales();
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
+        if (nss_full * 16 + 4 * u >= ngroups) break;  // sub-steps wholly past K (wave-uniform)
         const bool okb = nss_full * 16 + 4 * u + kq < ngroups;
         const bool oka = nss_full * 16 + 4 * u + aseg < ngroups;
         __syncthreads();  // every wave is done reading buffer 0
@@ -772,6 +773,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
       promote_scales();
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
+        if (nss_full * 16 + 4 * u >= ngroups) break;  // sub-steps wholly past K (wave-uniform)
         const bool okb = nss_full * 16 + 4 * u + kq < ngroups;
         const bool oka = nss_full * 16 + 4 * u + aseg < ngroups;
         __syncthreads();  // every wave is done reading buffer 0

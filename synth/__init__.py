@@ -66,6 +66,9 @@ class Workload:
 TINY = LayerShape(E=8, H=256, I=128, top_k=2)
 FULL = LayerShape(E=384, H=7168, I=2048, top_k=8)
 FULL_SHARED = LayerShape(E=384, H=7168, I=2048, top_k=8, shared=True)
+# one GPU's share of the same layer under 8-way tensor parallelism over I:
+# every expert, an eighth of its intermediate width
+TP8_SLICE = LayerShape(E=384, H=7168, I=256, top_k=8)
 
 WORKLOADS = {
     "tiny": Workload("tiny", TINY, (16,)),
@@ -73,6 +76,7 @@ WORKLOADS = {
     "transition": Workload("transition", FULL, (90, 256)),
     "plateau": Workload("plateau", FULL, (1024, 4096)),
     "skew": Workload("skew", FULL_SHARED, (512,), skew=True),
+    "tp8": Workload("tp8", TP8_SLICE, (1, 9, 256, 4096)),
 }
 
 
@@ -179,7 +183,7 @@ def inputs(seed: int, shape: LayerShape, M: int, skew: bool = False, logits_seed
 
 
 __all__ = [
-    "GROUP", "LayerShape", "Workload", "WORKLOADS", "TINY", "FULL", "FULL_SHARED",
+    "GROUP", "LayerShape", "Workload", "WORKLOADS", "TINY", "FULL", "FULL_SHARED", "TP8_SLICE",
     "f32_to_bf16_bits", "hidden", "logits", "zipf_bias", "expert", "all_experts",
     "inputs", "expected_touched",
 ]

@@ -61,3 +61,39 @@ def test_full_size_parity(full, workload, M, nsample):
     err = rel_err(out[tokens], ref["out"])
     say(f"  tokens {tokens.tolist()} rel err {err:.3e}")
     assert err <= REL_TOL
+
+
+@pytest.fixture(scope="module")
+def tp8():
+    """One GPU's share under 8-way tensor parallelism over I: all 384
+    experts, I = 256 (synthetic weights of that shape)."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from quantized_mixture_experts_top_amd import Layer
+    shape = synth.TP8_SLICE
+    say("uploading the tensor-parallel slice (384 experts, I=256, seed 0)")
+    r = upload_full(SEED, shape)["routed"]
+    layer = Layer(E=shape.E, H=shape.H, I=shape.I, top_k=shape.top_k, max_rows=4096,
+                  w13=r["w13"], s13=r["s13"], w2=r["w2"], s2=r["s2"])
+    yield layer
+    layer.close()
+
+
+@pytest.mark.parametrize("M,nsample", [(1, None), (9, None), (256, 6), (4096, 6)])
+def test_tp8_slice_parity(tp8, M, nsample):
+    shape = synth.TP8_SLICE
+    say(f"tp8 slice M={M}")
+    inp = synth.inputs(SEED, shape, M)
+    out = tp8.forward(dev_bf16(inp["x"]), dev(inp["logits"])).float().cpu().numpy()
+    check_routing(tp8, M, oracle_moe.route(inp["logits"], shape.top_k), shape.E)
+    if nsample is None:
+        tokens = np.arange(M)
+    else:
+        rng = np.random.default_rng(2000 + M)
+        tokens = np.unique(np.concatenate([[0, M - 1], rng.choice(M, nsample, replace=False)]))
+    ref = oracle_moe.forward(inp["x"], inp["logits"], shape.top_k, lambda e: synth.expert(SEED, shape, e),
+                             shape.I, tokens=tokens)
+    err = rel_err(out[tokens], ref["out"])
+    say(f"  tokens {tokens.tolist()} rel err {err:.3e}")
+    assert err <= REL_TOL
