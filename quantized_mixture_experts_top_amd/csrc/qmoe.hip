@@ -8,8 +8,8 @@
 //   gemm_kernel<..., true>   stacked gate+up product with h = SiLU(g)*u
 //   gemm_kernel<..., false>  down product times the routing weight
 //                   (128-row MFMA tiles; calls averaging at most 1.75 routed
-//                   rows per expert run gemv_kernel<..., true / false>, the
-//                   same two products as packed fp16 dot products)
+//                   rows per expert run gemv_kernel<..., true / false, NT>,
+//                   the same two products as packed fp16 dot products)
 //   combine_kernel  out[t] = sum over slots in order (+ shared expert)
 //
 // Layer definition: "The MoE Throughput Lever: Quantifying the INT4 Marlin
@@ -872,7 +872,12 @@ __host__ __device__ constexpr size_t gemv_lds_bytes(int K) {
 // of weights; capped at three waves the compiler spills inside the K loop,
 // which measured slower on MI355X than two waves without spills.
 constexpr int kGemvWPE = 2;
-template <int WN, int WK, bool GATEUP>
+// NT: weight codes are read with the non-temporal cache policy.  A plain
+// streaming read measured about 6.7 TB/s that way against 6.2 TB/s with the
+// default policy on MI355X; it pays only while each expert's codes are read
+// once (about one routed row per expert or fewer).  Scales keep the default
+// policy (non-temporal scales measured slower at every M).
+template <int WN, int WK, bool GATEUP, bool NT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kGemvWPE))) void gemv_kernel(
     GemmArgs g) {
   static_assert(WN * WK == 4, "4 waves per block");
@@ -946,7 +951,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kGemvW
       for (int b = 0; b < NBB; ++b)
         f.b[b][m] = __builtin_bit_cast(
             u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rB, ok ? bl : kOob,
-                                                           (brow[b] + 4 * m) * K2 + S * (kSuper / 2), 0));
+                                                           (brow[b] + 4 * m) * K2 + S * (kSuper / 2), NT ? 2 : 0));
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -1495,7 +1500,14 @@ int launch_gemv(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream
   const int64_t blocks = (int64_t)g.nblk * g.max_items;
   if (blocks > 0x7FFFFFFF) return fail(QMOE_ERR_UNSUPPORTED, "grid too large");
   const size_t lds = std::max<size_t>(gemv_lds_bytes(g.K), (size_t)(WK - 1) * WN * 2 * kGemvRows * 16 * 4);
-  gemv_kernel<WN, WK, GATEUP><<<dim3((unsigned)blocks), kThreads, lds, st>>>(g);
+  // non-temporal code reads while each expert's codes are read about once:
+  // at most one routed row per expert on average and no shared expert (whose
+  // codes every item of the call reads)
+  const bool nt = M * L->d.top_k <= L->d.E && L->d.shared_w13 == nullptr;
+  if (nt)
+    gemv_kernel<WN, WK, GATEUP, true><<<dim3((unsigned)blocks), kThreads, lds, st>>>(g);
+  else
+    gemv_kernel<WN, WK, GATEUP, false><<<dim3((unsigned)blocks), kThreads, lds, st>>>(g);
   L->gemm_launches++;
   return check_launch(L, GATEUP ? "gate_up gemv" : "down gemv");
 }
