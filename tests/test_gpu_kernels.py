@@ -117,7 +117,12 @@ def test_routing_repeatable_and_workspace_reuse():
 
 FWD_CASES = [
     # E, H, I, k, M, shared   (dot-product GEMV items of <= 2 rows when
-    #                          4*M*k <= 7E, else 128-row MFMA tiles)
+    #                          4*M*k <= 7E, else 128-row MFMA tiles; the
+    #                          GEMV reads codes non-temporal when M*k <= E
+    #                          and there is no shared expert: the cases
+    #                          with M=1 on 8 experts, M=20 on 64, M=2 on 16
+    #                          and M=1 on 1, and the default cache policy in
+    #                          the other GEMV cases)
     (8, 256, 128, 2, 16, False),     # the tiny configuration (tiles)
     (8, 256, 128, 2, 7, False),      # GEMV, several items per expert
     (8, 256, 128, 2, 1, False),      # GEMV, one row
