@@ -268,6 +268,27 @@ def test_repeat_runs_bitwise_identical(case):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("E,H,I,k,M,m,path", [
+    # GEMV both times: 8 tokens alone read the codes non-temporal, 40 do not
+    (64, 1152, 640, 2, 40, 8, "gemv_tiles"),
+    # tiles both times: 60 tokens alone take the 2-row-block K loops (paired
+    # weight loads), all 400 the 6- and 7-block loops
+    (4, 256, 128, 1, 400, 60, "prefill_tiles"),
+])
+def test_token_results_do_not_depend_on_the_call(E, H, I, k, M, m, path):
+    """A token's output is a function of its own row and logits only: each
+    routed row's sums run in the same order whatever items it shares, so the
+    first m tokens alone give the same bits as inside the M-token call."""
+    import torch
+    layer, w = make_layer(synth.LayerShape(E=E, H=H, I=I, top_k=k), 5, M)
+    xs, ls = dev_bf16(synth.hidden(6, M, H)), dev(synth.logits(7, M, E))
+    say(f"call invariance E={E} M={M} first {m} ({path})")
+    full = layer.forward(xs, ls).clone()
+    part = layer.forward(xs[:m].contiguous(), ls[:m].contiguous()).clone()
+    assert layer.stats()[path] == 2  # both calls took the regime named
+    assert torch.equal(full[:m].view(torch.int16), part.view(torch.int16))
+
+
 @pytest.mark.parametrize("M", [9, 130])  # one routing block; three meeting at a ticket
 def test_uninitialised_workspace(M):
     """A workspace full of stale bytes, never initialised, gives the same
