@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define QMOE_VERSION 1
+#define QMOE_VERSION 2
 
 enum qmoe_status {
   QMOE_OK = 0,
@@ -189,6 +189,9 @@ typedef struct {
   uint64_t workspace_bytes_peak;
   uint64_t prefill_tiles;     /* gate+up launches on 128-row MFMA tiles */
   uint64_t gemv_tiles;        /* gate+up launches on <= 2-row dot-product items */
+  uint64_t gemv_nt_launches;  /* dot-product launches (gate+up and down) reading the
+                                 weight codes with the non-temporal cache policy:
+                                 calls with M*top_k <= E and no shared expert */
 } qmoe_stats;
 
 int qmoe_get_stats(const qmoe_layer* layer, qmoe_stats* out);

@@ -41,7 +41,8 @@ class LayerDesc(ctypes.Structure):
 class Stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "forward_calls", "route_calls", "gemm_launches", "launches", "workspace_inits",
-        "workspace_bytes_last", "workspace_bytes_peak", "prefill_tiles", "gemv_tiles")]
+        "workspace_bytes_last", "workspace_bytes_peak", "prefill_tiles", "gemv_tiles",
+        "gemv_nt_launches")]
 
     def as_dict(self) -> dict:
         return {n: int(getattr(self, n)) for n, _ in self._fields_}
@@ -69,6 +70,7 @@ SIGNATURES = {
     "qmoe_reset_stats": (ctypes.c_int, [_VP]),
 }
 
+ABI_VERSION = 2  # QMOE_VERSION of include/qmoe.h
 _lib = None
 
 
@@ -89,6 +91,9 @@ def load_library():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    if lib.qmoe_version() != ABI_VERSION:  # the structs above follow this version's header
+        raise RuntimeError(f"{path} has ABI version {lib.qmoe_version()}, this binding expects "
+                           f"{ABI_VERSION}: rebuild it")
     _lib = lib
     return lib
 

@@ -1334,7 +1334,7 @@ struct qmoe_layer {
   int device = 0;
   bool shared = false;
   std::atomic<uint64_t> forward_calls{0}, route_calls{0}, gemm_launches{0}, launches{0}, inits{0},
-      ws_last{0}, ws_peak{0}, prefill_tiles{0}, gemv_tiles{0};
+      ws_last{0}, ws_peak{0}, prefill_tiles{0}, gemv_tiles{0}, gemv_nt{0};
   int split_k = 1;  // GEMV K split (1, 2 or 4 waves along K)
 };
 
@@ -1554,9 +1554,10 @@ int launch_gemv(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream
   // at most one routed row per expert on average and no shared expert (whose
   // codes every item of the call reads)
   const bool nt = M * L->d.top_k <= L->d.E && L->d.shared_w13 == nullptr;
-  if (nt)
+  if (nt) {
     gemv_kernel<WN, WK, GATEUP, true><<<dim3((unsigned)blocks), kThreads, lds, st>>>(g);
-  else
+    L->gemv_nt++;
+  } else
     gemv_kernel<WN, WK, GATEUP, false><<<dim3((unsigned)blocks), kThreads, lds, st>>>(g);
   L->gemm_launches++;
   return check_launch(L, GATEUP ? "gate_up gemv" : "down gemv");
@@ -1792,6 +1793,7 @@ int qmoe_get_stats(const qmoe_layer* L, qmoe_stats* s) {
   s->workspace_bytes_peak = L->ws_peak.load();
   s->prefill_tiles = L->prefill_tiles.load();
   s->gemv_tiles = L->gemv_tiles.load();
+  s->gemv_nt_launches = L->gemv_nt.load();
   return QMOE_OK;
 }
 
@@ -1806,6 +1808,7 @@ int qmoe_reset_stats(qmoe_layer* L) {
   L->ws_peak = 0;
   L->prefill_tiles = 0;
   L->gemv_tiles = 0;
+  L->gemv_nt = 0;
   return QMOE_OK;
 }
 

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert lib.qmoe_version() == 1
+    assert lib.qmoe_version() == 2
 
 
 def _desc(**kw):

@@ -285,7 +285,11 @@ def test_token_results_do_not_depend_on_the_call(E, H, I, k, M, m, path):
     say(f"call invariance E={E} M={M} first {m} ({path})")
     full = layer.forward(xs, ls).clone()
     part = layer.forward(xs[:m].contiguous(), ls[:m].contiguous()).clone()
-    assert layer.stats()[path] == 2  # both calls took the regime named
+    s = layer.stats()
+    assert s[path] == 2  # both calls took the regime named
+    # the GEMV's m tokens alone read the codes non-temporal (gate+up and
+    # down), all M with the default policy; the tiles never do
+    assert s["gemv_nt_launches"] == (2 if path == "gemv_tiles" else 0)
     assert torch.equal(full[:m].view(torch.int16), part.view(torch.int16))
 
 
@@ -376,6 +380,7 @@ def test_counters_and_workspace_accounting():
     assert s["workspace_inits"] == 0
     assert s["workspace_bytes_last"] == s["workspace_bytes_peak"] == layer.workspace_bytes(16) > 0
     assert s["prefill_tiles"] + s["gemv_tiles"] == 1
+    assert s["gemv_nt_launches"] == 0  # 16 tokens x top-2 > 8 experts
 
 
 def test_errors_from_the_library():
