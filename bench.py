@@ -84,6 +84,20 @@ def source_hash():
     return hashlib.sha256(b"".join(open(f, "rb").read() for f in KERNEL_SOURCES)).hexdigest()[:16]
 
 
+def stored_traffic(workload: str, M: int, path: str = COUNTERS):
+    """HBM bytes per gate+up launch that the counter passes measured for this
+    workload and M, or None when none were taken on the current kernel sources."""
+    if not os.path.exists(path):
+        return None
+    try:
+        c = json.load(open(path))
+        if c.get("source_sha256_16") != source_hash():
+            return None
+        return c.get("gate_up_bytes_per_launch", {}).get(f"{workload}:M={M}")
+    except (ValueError, AttributeError):
+        return None
+
+
 def cpu_baseline(shape, M, skew, budget_s=20.0):
     """The float64 oracle on the host: a full call when it fits the budget,
     else a sample of tokens; scaled to tokens/s."""
@@ -266,15 +280,7 @@ def main():
     M = args.m
     r = results[M]
     mfma_bound = r["gate_up_TFLOPs"] / MFMA_PEAK_TFLOPS > r["gate_up_GBps"] / HBM_PEAK_GBS
-    traffic = None
-    if os.path.exists(COUNTERS):
-        try:
-            c = json.load(open(COUNTERS))
-            key = f"{args.workload}:M={M}"
-            if c.get("source_sha256_16") == source_hash() and key in c.get("gate_up_bytes_per_launch", {}):
-                traffic = c["gate_up_bytes_per_launch"][key]
-        except (ValueError, KeyError):
-            traffic = None
+    traffic = stored_traffic(args.workload, M)
     if mfma_bound:
         roof = {"bound": "mfma", "achieved": round(r["gate_up_TFLOPs"], 2), "peak": MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(r["gate_up_TFLOPs"] / MFMA_PEAK_TFLOPS, 4)}

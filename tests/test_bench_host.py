@@ -1,6 +1,7 @@
 """Host-side parts of the benchmark that need no GPU: the one-GPU guard,
 the CPU oracle baseline record, and the algorithmic byte count the
 roofline is priced on."""
+import json
 import os
 import subprocess
 import sys
@@ -39,3 +40,20 @@ def test_bytes_per_expert_closed_form(shape):
     assert w2 == H * I // 2 + 2 * (H * I // 32)
     if shape is synth.FULL:  # the 384-expert layer's figures
         assert (w13, w2) == (16_515_072, 8_257_536)
+
+
+def test_stored_traffic_only_for_the_current_sources(tmp_path):
+    """The bench line's traffic figure is the stored counter reading for its
+    workload and M, and null once the kernel sources differ from those the
+    counters were taken on."""
+    p = tmp_path / "traffic.json"
+    p.write_text(json.dumps({"source_sha256_16": bench.source_hash(),
+                             "gate_up_bytes_per_launch": {"decode:M=9": 123}}))
+    assert bench.stored_traffic("decode", 9, str(p)) == 123
+    assert bench.stored_traffic("decode", 1, str(p)) is None
+    assert bench.stored_traffic("plateau", 9, str(p)) is None
+    p.write_text(json.dumps({"source_sha256_16": "0" * 16, "gate_up_bytes_per_launch": {"decode:M=9": 123}}))
+    assert bench.stored_traffic("decode", 9, str(p)) is None
+    p.write_text("not json")
+    assert bench.stored_traffic("decode", 9, str(p)) is None
+    assert bench.stored_traffic("decode", 9, str(tmp_path / "missing.json")) is None
