@@ -568,9 +568,9 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   // lanes that read one MFMA operand column (rows 0..15, one segment, one
   // 16-byte piece) then meet no LDS bank conflict (measured on MI355X with
   // the LDS counters), down at 4096 tokens 12% faster.  Gate+up keeps slot
-  // (kq + rr) mod 4 (4 conflict cycles per 8-cycle read), which measured
-  // 2-3% faster there.  Wave w loads block q = w mod 4 of every (WN/4)-th
-  // row block, starting at w / 4.
+  // (kq + rr) mod 4 (4 conflict cycles per 8-cycle read): with the new slots
+  // it measured up to 1% slower, so these reads do not bound it.  Wave w
+  // loads block q = w mod 4 of every (WN/4)-th row block, starting at w / 4.
   static_assert(WK == 1, "128-row tiles split N across waves, not K");
   constexpr int kBlkHalves = 520;  // 1040-byte LDS block
   // two buffers as separate arrays, so that the compiler can tell loads
