@@ -1,6 +1,7 @@
 """Benchmark of the fused int4 MoE layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--m 9] [--workload decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]       # the whole M sweep
+    python bench.py --only plateau:4096 [--steps K ...]       # one configuration
 
 A step is one call of the whole layer (route, gate+up, down, combine) on one
 batch of M tokens.  Each step gets its own seeded activations and router
@@ -8,20 +9,30 @@ logits (uploaded before timing), so consecutive steps touch different
 experts and the weight stream is not served from the 256 MB last-level
 cache.  Inputs are resident in HBM when the timed region starts.
 
-Prints one JSON line: throughput in tokens/s for the workload, the
-roofline of the dominant kernel (gate+up) from HIP events on the stream the
-kernels run on, and the CPU oracle timed on the host's cores on a bounded
-sample.  The layer's shapes are those of the M-sweep in "The MoE Throughput
-Lever: Quantifying the INT4 Marlin GEMM on Blackwell PRO 6000" (section
-"The Benchmark: What Was Measured"); its per-M figures for one RTX PRO 6000
-Blackwell are reported as context (vs_baseline), not as a target.
+The default run times every configuration of the M sweep in one process:
+the 384-expert layer (H=7168, I=2048, top-8, int4 group-32) at M = 1, 9
+(decode), 90, 256 (transition), 1024, 4096 (plateau), and the skewed-routing
+layer with a shared expert at M = 512.  The shapes and the sweep are those of
+"The MoE Throughput Lever: Quantifying the INT4 Marlin GEMM on Blackwell PRO
+6000" (sections "The Benchmark: What Was Measured" and "The Two Regimes:
+Weight-Streaming vs. Compute-Bound"); its per-M figures for one RTX PRO 6000
+Blackwell are reported as context, not as a target.
+
+Prints one JSON line: the headline (M=4096, the largest configuration) as
+tokens/s, the roofline of its dominant kernel (gate+up) from HIP events on
+the stream the kernels run on, every configuration's figures under per_M,
+and the CPU oracle timed on the host's cores on a bounded sample of the
+headline call.
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import os
+import platform
+import statistics
 import sys
 import time
 from concurrent.futures import ThreadPoolExecutor
@@ -37,13 +48,25 @@ METRIC = "MoE layer µs/call & tokens/s vs M (1..4096); % HBM BW / % bf16 MFMA p
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA, published
 # ms/call of the INT4 Marlin MoE on one RTX PRO 6000 Blackwell, same layer
+# ("The MoE Throughput Lever ...", section "The Benchmark: What Was Measured")
 PAGE_MS_PER_CALL = {1: 0.151, 9: 1.18, 90: 5.19, 256: 7.02, 512: 7.01, 1024: 7.02}
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_mixture_experts_top_amd", "csrc", f) for f in ("qmoe.hip", "qmoe_device.h")]
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+# the default sweep: (workload, M); the last one is the headline
+SWEEP = [("decode", 1), ("decode", 9), ("transition", 90), ("transition", 256), ("plateau", 1024),
+         ("skew", 512), ("plateau", 4096)]
+HEADLINE = ("plateau", 4096)
+# counter scaling factors: what FETCH_SIZE / WRITE_SIZE (KiB per dispatch) read
+# for a plain device copy of known size (bench.py --calibrate-copy)
+FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def key_of(workload: str, M: int) -> str:
+    return f"{workload}:M={M}"
 
 
 def upload_weights(seed, shape, threads=16, chunk=32):
@@ -64,10 +87,8 @@ def upload_weights(seed, shape, threads=16, chunk=32):
                 if a.dtype == np.uint16:
                     a = a.view(np.int16)
                 out[key][e0:e0 + len(es)].copy_(torch.from_numpy(a))
-    shared = None
-    if shape.shared:
-        sh = synth.expert(seed, shape, "shared")
-        shared = {k: torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).cuda() for k, v in sh.items()}
+    sh = synth.expert(seed, shape, "shared")
+    shared = {k: torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).cuda() for k, v in sh.items()}
     torch.cuda.synchronize()
     return out, shared
 
@@ -77,6 +98,12 @@ def bytes_per_expert(shape):
     w13 = 2 * I * H // 2 + 2 * (2 * I * H // 32)
     w2 = H * I // 2 + 2 * (H * I // 32)
     return w13, w2
+
+
+def flops_per_row(shape):
+    """Multiply-adds x2 of one routed row through the stacked gate+up
+    product (2I x H) and the down product (H x I)."""
+    return 2.0 * 2 * shape.I * shape.H, 2.0 * shape.H * shape.I
 
 
 def source_hash():
@@ -93,56 +120,258 @@ def stored_traffic(workload: str, M: int, path: str = COUNTERS):
         c = json.load(open(path))
         if c.get("source_sha256_16") != source_hash():
             return None
-        return c.get("gate_up_bytes_per_launch", {}).get(f"{workload}:M={M}")
+        return c.get("gate_up_bytes_per_launch", {}).get(key_of(workload, M))
     except (ValueError, AttributeError):
         return None
 
 
-def cpu_baseline(shape, M, skew, budget_s=20.0):
-    """The float64 oracle on the host: a full call when it fits the budget,
-    else a sample of tokens; scaled to tokens/s."""
-    from oracle import moe as oracle_moe
-    inp = synth.inputs(0, shape, M, skew=skew)
-    get = lambda e: synth.expert(0, shape, e)
-    shared = synth.expert(0, shape, "shared") if shape.shared else None
-    ntok = M if M <= 9 else 2
-    tokens = np.arange(ntok)
-    reps, dt = 0, 0.0
-    while reps < 3 and (reps == 0 or dt < 10.0):  # at least ~10 s of work when one call is quick
-        t0 = time.perf_counter()
-        oracle_moe.forward(inp["x"], inp["logits"], shape.top_k, get, shape.I, shared=shared, tokens=tokens)
-        dt += time.perf_counter() - t0
-        reps += 1
+def is_gate_up_kernel(name: str) -> bool:
+    """The gate+up launches of a trace: the 128-row tiles or the dot-product
+    GEMV instantiated with GATEUP = true."""
+    n = name.replace("(anonymous namespace)::", "")
+    return ("gemm_kernel<" in n and ", true>" in n) or "gemv_kernel<true" in n
+
+
+def summarize_counters(key: str, fetch_csv: str, write_csv: str, path: str = COUNTERS) -> int:
+    """Mean HBM bytes per gate+up dispatch from one FETCH_SIZE and one
+    WRITE_SIZE counter pass (rocprofv3 csv), scaled by the copy calibration,
+    stored under `key` with the current source hash (entries taken on other
+    sources are dropped)."""
+    def per_dispatch(p, counter):
+        vals = {}
+        for r in csv.DictReader(open(p)):
+            if r["Counter_Name"] == counter and is_gate_up_kernel(r["Kernel_Name"]):
+                vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        if not vals:
+            raise SystemExit(f"no gate+up dispatches with {counter} in {p}")
+        return statistics.mean(vals.values())
+    b = per_dispatch(fetch_csv, "FETCH_SIZE") * 1024 * FETCH_FACTOR + \
+        per_dispatch(write_csv, "WRITE_SIZE") * 1024 * WRITE_FACTOR
+    c = {}
+    if os.path.exists(path):
+        try:
+            c = json.load(open(path))
+        except ValueError:
+            c = {}
+    if c.get("source_sha256_16") != source_hash():
+        c = {"source_sha256_16": source_hash()}
+    c["note"] = (f"HBM bytes per gate+up launch (read + written, mean over the launches of `bench.py --only "
+                 f"<workload>:<M>`), FETCH_SIZE x {FETCH_FACTOR:.3f} and WRITE_SIZE x {WRITE_FACTOR:.3f} "
+                 f"(factors from a 1 GiB device copy: bench.py --calibrate-copy)")
+    c.setdefault("gate_up_bytes_per_launch", {})[key] = int(round(b))
+    with open(path, "w") as f:
+        json.dump(c, f, indent=1)
+        f.write("\n")
+    return int(round(b))
+
+
+def host_info():
+    model = platform.processor() or ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas, threads = "unknown", 1
     try:
         from threadpoolctl import threadpool_info
-        blas = [p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
+        for p in threadpool_info():
+            if p.get("user_api") == "blas":
+                blas = f"{p.get('internal_api')} {p.get('version')}"
+                threads = max(threads, int(p.get("num_threads", 1)))
     except ImportError:
-        blas = []
-    cores = max(blas) if blas else 1  # BLAS threads of the matmuls; the rest is one thread
-    sample = (f"oracle (float64 numpy) on {ntok} of the {M} tokens of one call, routing for all {M}, "
-              f"experts regenerated and decoded on the fly; {reps} run(s), {dt:.1f} s")
-    return {"value": round(reps * ntok / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": sample}
+        pass
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = os.cpu_count() or 1
+    return {"cpu_model": model, "blas": blas, "blas_threads": threads, "host_cpus_visible": aff}
+
+
+def cpu_baseline(shape, M, skew, budget_s=20.0, seed=0):
+    """The float64 oracle on the host, on a bounded sample of one call: the
+    routing of all M tokens, then the MLP of a seeded sample of the experts
+    the call touches, each on all of its routed rows (and the shared expert
+    on every token, when the layer has one); the time is scaled to the whole
+    call by (touched experts / sampled experts) and reported as tokens/s."""
+    from oracle import moe as oracle_moe
+    inp = synth.inputs(seed, shape, M, skew=skew)
+    k = shape.top_k
+    t0 = time.perf_counter()
+    xf = oracle_moe.decode_bf16(inp["x"])
+    r = oracle_moe.route(inp["logits"], k)
+    t_route = time.perf_counter() - t0
+    touched = np.nonzero(r["counts"])[0]
+    order = np.random.default_rng(seed).permutation(touched)
+    t_exp, n = 0.0, 0
+    for e in order:
+        rows = r["perm"][r["offsets"][e]:r["offsets"][e + 1]] // k
+        w = synth.expert(seed, shape, int(e))  # weights are inputs: generated outside the timed part
+        t1 = time.perf_counter()
+        oracle_moe.expert_mlp(xf[rows], w, shape.I)
+        t_exp += time.perf_counter() - t1
+        n += 1
+        if t_exp >= budget_s:
+            break
+    t_sh = 0.0
+    if shape.shared:
+        w = synth.expert(seed, shape, "shared")
+        t1 = time.perf_counter()
+        oracle_moe.expert_mlp(xf, w, shape.I)
+        t_sh = time.perf_counter() - t1
+    est = t_route + t_exp / n * len(touched) + t_sh
+    info = host_info()
+    sample = (f"oracle (float64 numpy) on one {M}-token call: routing of all {M} tokens ({t_route:.2f} s), "
+              f"MLPs of {n} of the {len(touched)} touched experts on all their routed rows ({t_exp:.1f} s)"
+              + (f", shared expert on all tokens ({t_sh:.1f} s)" if shape.shared else "")
+              + f"; call time scaled by {len(touched)}/{n} = {est:.1f} s; slot combine not timed")
+    return {"value": round(M / est, 4), "unit": "tokens/s", "cores": info["blas_threads"], "kind": "oracle",
+            "sample": sample, **info}
+
+
+def time_config(layer, shape, wl, M, steps, warmup, graph=False):
+    """Whole-layer throughput and per-kernel durations of M-token calls."""
+    import torch
+    stream = torch.cuda.current_stream()
+    n = warmup + steps
+    xs, ls = [], []
+    for s in range(n):
+        inp = synth.inputs(0, shape, M, skew=wl.skew, logits_seed=1 + s)
+        xs.append(torch.from_numpy(inp["x"].view(np.int16)).cuda().view(torch.bfloat16))
+        ls.append(torch.from_numpy(inp["logits"]).cuda())
+    out = torch.empty((M, shape.H), dtype=torch.bfloat16, device="cuda")
+    layer.workspace(M)
+    # experts touched by each step, from the layer's own routing
+    touched = []
+    for s in range(n):
+        layer.route(xs[s], ls[s])
+        c = layer.read_routing(M)["counts"]
+        touched.append(int((c > 0).sum().item()) + (1 if shape.shared else 0))
+    torch.cuda.synchronize()
+    # ---- whole-layer throughput: back-to-back calls
+    for s in range(warmup):
+        layer.forward(xs[s], ls[s], out=out)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for s in range(warmup, n):
+        layer.forward(xs[s], ls[s], out=out)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    # ---- per-kernel durations: the same four steps, bracketed by events on
+    # the stream the kernels run on
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for i, s in enumerate(range(warmup, n)):
+        e = evs[i]
+        e[0].record(stream)
+        layer.route(xs[s], ls[s])
+        e[1].record(stream)
+        layer.gate_up(M)
+        e[2].record(stream)
+        layer.down(M)
+        e[3].record(stream)
+        layer.combine(M, out=out)
+        e[4].record(stream)
+    torch.cuda.synchronize()
+    stage = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)] for i in range(steps)])
+    per_call_us = np.array([evs[i][0].elapsed_time(evs[i][4]) for i in range(steps)]) * 1e3
+    graph_res = None
+    if graph:
+        outs = [torch.empty_like(out) for _ in range(n)]
+        graphs = []
+        torch.cuda.synchronize()
+        for s in range(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                layer.forward(xs[s], ls[s], out=outs[s])
+            graphs.append(g)
+        for s in range(warmup):
+            graphs[s].replay()
+        torch.cuda.synchronize()
+        gv0, gv1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gv0.record(stream)
+        for s in range(warmup, n):
+            graphs[s].replay()
+        gv1.record(stream)
+        torch.cuda.synchronize()
+        eager_last = layer.forward(xs[n - 1], ls[n - 1])
+        torch.cuda.synchronize()
+        graph_res = {"us_per_call": gv0.elapsed_time(gv1) / steps * 1e3,
+                     "matches_eager": bool(torch.equal(outs[n - 1].view(torch.int16), eager_last.view(torch.int16)))}
+        del graphs, outs
+    del xs, ls
+    b13, b2 = bytes_per_expert(shape)
+    f13, f2 = flops_per_row(shape)
+    st_ms = stage.mean(axis=0)
+    tt = np.array(touched[warmup:], dtype=np.float64)
+    rows = M * shape.top_k + (M if shape.shared else 0)
+    alg_bytes = tt * (b13 + b2) + M * shape.H * 2 + M * shape.E * 4 + M * shape.H * 2
+    gu_bytes = tt * b13 + M * shape.H * 2
+    dn_bytes = tt * b2 + M * shape.H * 2
+    flops = rows * (f13 + f2)
+    gu_gbps = float(np.mean(gu_bytes / (stage[:, 1] * 1e-3)) / 1e9)
+    dn_gbps = float(np.mean(dn_bytes / (stage[:, 2] * 1e-3)) / 1e9)
+    gu_tf = float(np.mean(rows * f13 / (stage[:, 1] * 1e-3)) / 1e12)
+    dn_tf = float(np.mean(rows * f2 / (stage[:, 2] * 1e-3)) / 1e12)
+    layer_gbps = float(alg_bytes.mean() / (ms * 1e-3) / 1e9)
+    layer_tf = flops / (ms * 1e-3) / 1e12
+    res = {
+        "us_per_call": ms * 1e3, "us_per_token": ms * 1e3 / M, "tokens_per_s": M / (ms * 1e-3),
+        "experts_touched_mean": float(tt.mean()),
+        "layer_GBps": layer_gbps, "layer_hbm_frac": layer_gbps / HBM_PEAK_GBS,
+        "layer_TFLOPs": layer_tf, "layer_mfma_frac": layer_tf / MFMA_PEAK_TFLOPS,
+        "stage_us": {"route": st_ms[0] * 1e3, "gate_up": st_ms[1] * 1e3, "down": st_ms[2] * 1e3,
+                     "combine": st_ms[3] * 1e3},
+        "gate_up_GBps": gu_gbps, "gate_up_hbm_frac": gu_gbps / HBM_PEAK_GBS,
+        "gate_up_TFLOPs": gu_tf, "gate_up_mfma_frac": gu_tf / MFMA_PEAK_TFLOPS,
+        "down_GBps": dn_gbps, "down_hbm_frac": dn_gbps / HBM_PEAK_GBS,
+        "down_TFLOPs": dn_tf, "down_mfma_frac": dn_tf / MFMA_PEAK_TFLOPS,
+        "gate_up_bytes_per_launch": float(gu_bytes.mean()),
+        "gate_up_flops_per_launch": rows * f13,
+        "gate_up_us": float(st_ms[1] * 1e3),
+        "bracketed_call_us_p10_p50_p90": [float(np.percentile(per_call_us, q)) for q in (10, 50, 90)],
+    }
+    if graph_res is not None:
+        res["graph_us_per_call"] = graph_res["us_per_call"]
+        res["graph_matches_eager"] = graph_res["matches_eager"]
+    return res
+
+
+def _round(v):
+    if isinstance(v, float):
+        return round(v, 4) if abs(v) < 10 else round(v, 2)
+    if isinstance(v, dict):
+        return {k: _round(x) for k, x in v.items()}
+    if isinstance(v, list):
+        return [_round(x) for x in v]
+    return v
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # defaults: small calls (at most 64 tokens, well under a millisecond each)
-    # get 50 warmup and 100 timed steps so the timed region runs at the
-    # GPU's steady clocks; larger calls 5 and 20 (each step has its own
-    # inputs, generated on the host)
+    # defaults: calls of at most 64 tokens (well under a millisecond each) get
+    # 50 warmup and 100 timed steps, so the timed region runs at the GPU's
+    # steady clocks; larger calls 5 and 20 (each step has its own inputs)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--m", type=int, default=9)
-    ap.add_argument("--workload", default="decode", choices=sorted(synth.WORKLOADS))
-    ap.add_argument("--also-m", default="1", help="comma list of extra M values timed the same way")
+    ap.add_argument("--only", default=None,
+                    help="time one configuration, as workload:M (e.g. plateau:4096); default: the whole sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="also time the forward captured into one HIP graph per step and replayed back to back")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy 1 GiB device to device 5 times (reference reading for the HBM byte counters)")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("KEY", "FETCH_CSV", "WRITE_CSV"),
+                    help="store the mean gate+up HBM bytes of two rocprofv3 counter passes under KEY")
     args = ap.parse_args()
+    if args.summarize_counters:
+        key, f, w = args.summarize_counters
+        print(key, summarize_counters(key, f, w))
+        return
     if args.calibrate_copy:
         import torch
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
@@ -160,169 +389,103 @@ def main():
     import torch
     from quantized_mixture_experts_top_amd import Layer
 
-    wl = synth.WORKLOADS[args.workload]
-    shape = wl.shape
-    Ms = [args.m] + [int(v) for v in args.also_m.split(",") if v.strip() and int(v) != args.m]
-    max_rows = max(Ms)
-    small = max_rows <= 64
-    if args.steps is None:
-        args.steps = 100 if small else 20
-    if args.warmup is None:
-        args.warmup = 50 if small else 5
+    if args.only:
+        wname, m = args.only.split(":")
+        configs = [(wname, int(m.replace("M=", "")))]
+        if wname not in synth.WORKLOADS:
+            raise SystemExit(f"unknown workload {wname}")
+    else:
+        configs = list(SWEEP)
+    headline = configs[-1] if args.only else HEADLINE
     t0 = time.time()
-    w, shared = upload_weights(0, shape)
+    shapes = {synth.WORKLOADS[w].shape for w, _ in configs}
+    base = synth.WORKLOADS[configs[0][0]].shape
+    w, shared = upload_weights(0, base)
     log(f"weights uploaded in {time.time() - t0:.1f} s")
-    layer = Layer(E=shape.E, H=shape.H, I=shape.I, top_k=shape.top_k, max_rows=max_rows,
-                  w13=w["w13"], s13=w["s13"], w2=w["w2"], s2=w["s2"], shared=shared)
-    b13, b2 = bytes_per_expert(shape)
-    stream = torch.cuda.current_stream()
-    results = {}
-    for M in Ms:
-        n = args.warmup + args.steps
-        xs, ls = [], []
-        for s in range(n):
-            inp = synth.inputs(0, shape, M, skew=wl.skew, logits_seed=1 + s)
-            xs.append(torch.from_numpy(inp["x"].view(np.int16)).cuda().view(torch.bfloat16))
-            ls.append(torch.from_numpy(inp["logits"]).cuda())
-        out = torch.empty((M, shape.H), dtype=torch.bfloat16, device="cuda")
-        layer.workspace(M)
-        # experts touched by each step, from the layer's own routing
-        touched = []
-        for s in range(n):
-            layer.route(xs[s], ls[s])
-            c = layer.read_routing(M)["counts"]
-            touched.append(int((c > 0).sum().item()) + (1 if shape.shared else 0))
+    max_rows = max(m for _, m in configs)
+    layers = {}
+    for shp in shapes:
+        assert (shp.E, shp.H, shp.I, shp.top_k) == (base.E, base.H, base.I, base.top_k)
+        layers[shp.shared] = Layer(E=shp.E, H=shp.H, I=shp.I, top_k=shp.top_k, max_rows=max_rows,
+                                   w13=w["w13"], s13=w["s13"], w2=w["w2"], s2=w["s2"],
+                                   shared=shared if shp.shared else None)
+    # warm the GPU up to its steady clocks before anything is timed: a few
+    # calls of the largest configuration
+    wl0, m0 = max(configs, key=lambda c: c[1])
+    wl0 = synth.WORKLOADS[wl0]
+    xw = torch.from_numpy(synth.hidden(99, m0, base.H).view(np.int16)).cuda().view(torch.bfloat16)
+    lw = torch.from_numpy(synth.logits(99, m0, base.E, wl0.skew)).cuda()
+    t1 = time.time()
+    while time.time() - t1 < 1.0:
+        layers[wl0.shape.shared].forward(xw, lw)
         torch.cuda.synchronize()
-        # ---- whole-layer throughput
-        for s in range(args.warmup):
-            layer.forward(xs[s], ls[s], out=out)
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        for s in range(args.warmup, n):
-            layer.forward(xs[s], ls[s], out=out)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        ms = ev0.elapsed_time(ev1) / args.steps
-        # ---- per-kernel durations: the same four kernels, bracketed by events
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-        for i, s in enumerate(range(args.warmup, n)):
-            e = evs[i]
-            e[0].record(stream)
-            layer.route(xs[s], ls[s])
-            e[1].record(stream)
-            layer.gate_up(M)
-            e[2].record(stream)
-            layer.down(M)
-            e[3].record(stream)
-            layer.combine(M, out=out)
-            e[4].record(stream)
-        torch.cuda.synchronize()
-        stage = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)] for i in range(args.steps)])
-        # per-call distribution from the same bracketed loop (first to last event of each call)
-        per_call_us = np.array([evs[i][0].elapsed_time(evs[i][4]) for i in range(args.steps)]) * 1e3
-        # ---- optional: the same steps as captured graphs (one per step's inputs)
-        graph = None
-        if args.graph:
-            outs = [torch.empty_like(out) for _ in range(n)]
-            graphs = []
-            torch.cuda.synchronize()
-            for s in range(n):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    layer.forward(xs[s], ls[s], out=outs[s])
-                graphs.append(g)
-            for s in range(args.warmup):
-                graphs[s].replay()
-            torch.cuda.synchronize()
-            gv0, gv1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            gv0.record(stream)
-            for s in range(args.warmup, n):
-                graphs[s].replay()
-            gv1.record(stream)
-            torch.cuda.synchronize()
-            eager_last = layer.forward(xs[n - 1], ls[n - 1])
-            torch.cuda.synchronize()
-            graph = {"us_per_call": gv0.elapsed_time(gv1) / args.steps * 1e3,
-                     "matches_eager": bool(torch.equal(outs[n - 1].view(torch.int16), eager_last.view(torch.int16)))}
-            del graphs, outs
-        st_ms = stage.mean(axis=0)
-        tt = np.array(touched[args.warmup:], dtype=np.float64)
-        alg_bytes = tt * (b13 + b2) + M * shape.H * 2 + M * shape.E * 4 + M * shape.H * 2
-        gu_bytes = tt * b13 + M * shape.H * 2
-        dn_bytes = tt * b2 + M * shape.H * 2
-        flops = 2.0 * (M * shape.top_k + (M if shape.shared else 0)) * 3 * shape.H * shape.I
-        results[M] = {
-            "us_per_call": ms * 1e3, "us_per_token": ms * 1e3 / M, "tokens_per_s": M / (ms * 1e-3),
-            "experts_touched_mean": float(tt.mean()),
-            "layer_GBps": float(alg_bytes.mean() / (ms * 1e-3) / 1e9),
-            "layer_TFLOPs": flops / (ms * 1e-3) / 1e12,
-            "stage_us": {"route": st_ms[0] * 1e3, "gate_up": st_ms[1] * 1e3, "down": st_ms[2] * 1e3,
-                         "combine": st_ms[3] * 1e3},
-            "gate_up_GBps": float(np.mean(gu_bytes / (stage[:, 1] * 1e-3)) / 1e9),
-            "down_GBps": float(np.mean(dn_bytes / (stage[:, 2] * 1e-3)) / 1e9),
-            "gate_up_TFLOPs": float(np.mean(2.0 * (M * shape.top_k + (M if shape.shared else 0)) * 2 * shape.H
-                                            * shape.I / (stage[:, 1] * 1e-3)) / 1e12),
-            "gate_up_bytes_per_launch": float(gu_bytes.mean()),
-            "gate_up_us": float(st_ms[1] * 1e3),
-            "bracketed_call_us_p10_p50_p90": [float(np.percentile(per_call_us, q)) for q in (10, 50, 90)],
-        }
-        if graph is not None:
-            results[M]["graph_us_per_call"] = graph["us_per_call"]
-            results[M]["graph_matches_eager"] = graph["matches_eager"]
-        if graph is not None:
-            log(f"M={M}: graph replay {graph['us_per_call']:.1f} us/call (matches eager: {graph['matches_eager']})")
-        log(f"M={M}: {ms * 1e3:.1f} us/call, {results[M]['tokens_per_s']:.0f} tok/s, "
-            f"{results[M]['layer_GBps']:.0f} GB/s layer, stages(us) "
-            + ", ".join(f"{k}={v:.1f}" for k, v in results[M]["stage_us"].items()))
-        del xs, ls
+    del xw, lw
 
-    M = args.m
-    r = results[M]
-    mfma_bound = r["gate_up_TFLOPs"] / MFMA_PEAK_TFLOPS > r["gate_up_GBps"] / HBM_PEAK_GBS
-    traffic = stored_traffic(args.workload, M)
+    results = {}
+    for wname, M in configs:
+        wl = synth.WORKLOADS[wname]
+        small = M <= 64
+        steps = args.steps if args.steps is not None else (100 if small else 20)
+        warmup = args.warmup if args.warmup is not None else (50 if small else 5)
+        r = time_config(layers[wl.shape.shared], wl.shape, wl, M, steps, warmup, graph=args.graph)
+        page = PAGE_MS_PER_CALL.get(M) if wname in ("decode", "transition", "plateau", "skew") else None
+        r["page_us_per_call_context"] = page * 1e3 if page else None
+        r["gate_up_traffic_bytes"] = stored_traffic(wname, M)
+        r["steps"], r["warmup"] = steps, warmup
+        results[key_of(wname, M)] = r
+        log(f"{key_of(wname, M)}: {r['us_per_call']:.1f} us/call, {r['tokens_per_s']:.0f} tok/s, "
+            f"layer {r['layer_hbm_frac'] * 100:.1f}% HBM / {r['layer_mfma_frac'] * 100:.1f}% MFMA, stages(us) "
+            + ", ".join(f"{k}={v:.1f}" for k, v in r["stage_us"].items())
+            + (f", graph {r['graph_us_per_call']:.1f} us" if "graph_us_per_call" in r else ""))
+
+    hw, hm = headline
+    r = results[key_of(hw, hm)]
+    # the plateau's gate+up sits at the ridge (about 300 flop per algorithmic
+    # byte against 2500/8 = 312 for MI355X): it is priced against the MFMA
+    # peak; other configurations against whichever fraction is larger
+    mfma_bound = hw == "plateau" or r["gate_up_mfma_frac"] > r["gate_up_hbm_frac"]
     if mfma_bound:
         roof = {"bound": "mfma", "achieved": round(r["gate_up_TFLOPs"], 2), "peak": MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(r["gate_up_TFLOPs"] / MFMA_PEAK_TFLOPS, 4)}
+                "unit": "TFLOP/s", "frac": round(r["gate_up_mfma_frac"], 4)}
     else:
         roof = {"bound": "hbm", "achieved": round(r["gate_up_GBps"], 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(r["gate_up_GBps"] / HBM_PEAK_GBS, 4)}
-    roof["traffic"] = traffic
-    # both fractions, whichever binds (the plateau sits near the ridge)
-    roof["hbm_frac"] = round(r["gate_up_GBps"] / HBM_PEAK_GBS, 4)
-    roof["mfma_frac"] = round(r["gate_up_TFLOPs"] / MFMA_PEAK_TFLOPS, 4)
+                "unit": "GB/s", "frac": round(r["gate_up_hbm_frac"], 4)}
+    roof["traffic"] = r["gate_up_traffic_bytes"]
+    roof["hbm_frac"] = round(r["gate_up_hbm_frac"], 4)
+    roof["mfma_frac"] = round(r["gate_up_mfma_frac"], 4)
     roof["kernel"] = "gate_up (stacked gate+up grouped GEMM, SiLU*up epilogue)"
     roof["kernel_us"] = round(r["gate_up_us"], 2)
     roof["algorithmic_bytes_per_launch"] = round(r["gate_up_bytes_per_launch"])
-    page = PAGE_MS_PER_CALL.get(M) if args.workload in ("decode", "transition", "plateau") else None
+    roof["algorithmic_flops_per_launch"] = round(r["gate_up_flops_per_launch"])
+    shape = synth.WORKLOADS[hw].shape
+    page = r["page_us_per_call_context"]
     line = {
         "metric": METRIC,
         "value": round(r["tokens_per_s"], 2),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": r["steps"],
+        "warmup": r["warmup"],
         "ms_per_step": round(r["us_per_call"] / 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(r["tokens_per_s"] / (M / (page * 1e-3)), 3) if page else None,
+        # the page's figure is another GPU's (RTX PRO 6000): context only
+        "vs_baseline": None,
         "dtype": "fp16",
         "data": "synthetic",
-        "config": {"workload": f"{wl.name} E={shape.E} H={shape.H} I={shape.I} top-{shape.top_k} "
-                               f"int4-g32{' +shared' if shape.shared else ''} M={M}",
-                   "E": shape.E, "H": shape.H, "I": shape.I, "top_k": shape.top_k, "M": M,
-                   "group_size": 32, "shared_expert": shape.shared, "skew": wl.skew},
+        "config": {"workload": f"{synth.WORKLOADS[hw].name} E={shape.E} H={shape.H} I={shape.I} "
+                               f"top-{shape.top_k} int4-g32{' +shared' if shape.shared else ''} M={hm}",
+                   "E": shape.E, "H": shape.H, "I": shape.I, "top_k": shape.top_k, "M": hm,
+                   "group_size": 32, "shared_expert": shape.shared, "skew": synth.WORKLOADS[hw].skew},
         "us_per_call": round(r["us_per_call"], 2),
-        "us_per_token": round(r["us_per_token"], 3),
+        "us_per_token": round(r["us_per_token"], 4),
+        "page_us_per_call_context": page,
         "roofline": roof,
-        "per_M": {str(m): {k: (round(v, 3) if isinstance(v, float) else
-                               {kk: round(vv, 2) for kk, vv in v.items()} if isinstance(v, dict) else
-                               [round(vv, 2) for vv in v] if isinstance(v, list) else v)
-                           for k, v in results[m].items()} for m in Ms},
+        "per_M": {k: _round(v) for k, v in results.items()},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
-        line["cpu_baseline"] = cpu_baseline(shape, M, wl.skew)
+        line["cpu_baseline"] = cpu_baseline(shape, hm, synth.WORKLOADS[hw].skew)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -28,8 +28,16 @@
  * Activations x: bf16 [M, H]; router logits: fp32 [M, E]; out: bf16 [M, H].
  * All row-major and contiguous.
  *
- * Arithmetic: x is converted to fp16 (exact for normal-range values) and h
- * = SiLU(gate)*up is held in fp16, so |x| and |h| must stay below 65504.
+ * Arithmetic and ranges: each token's hidden row is scaled by a power of two
+ * 2^-e chosen from its largest |x| (2^e <= max|x_t| < 2^(e+1), e clamped to
+ * [-60, 60]) and converted to fp16; the scaling is exact, so any finite bf16
+ * row with max|x_t| in [2^-60, 2^61) enters the products with fp16 rounding
+ * only below 2^-14 of its largest value.  h = SiLU(gate)*up is held in fp16
+ * times 2^-2e, so |h_t| must stay below 65504 * 4^e (and is rounded to fp16
+ * subnormals below 2^-14 * 4^e); an overflow gives inf/NaN in that token's
+ * output.  The MFMA tiles hold decoded weights at odd input offsets times 16
+ * in fp16, so group scales must not exceed 511.75 (16*8*s <= 65504); scales
+ * are otherwise any finite fp16, subnormals included.  Logits must be finite.
  * Which kernel a call uses depends on the average number of routed rows per
  * expert, M*top_k/E:
  *   <= 1.75   dot-product GEMV on items of <= 2 rows: per 32-input group,
@@ -111,12 +119,9 @@ typedef struct qmoe_layer qmoe_layer;
 /* Validate the description and create a handle (host memory only).  Fails
    with QMOE_ERR_ARG on a bad field (the message names it), then with
    QMOE_ERR_DEVICE if no HIP device can be queried and QMOE_ERR_UNSUPPORTED
-   if the current device is not gfx950.
-   The environment variable QMOE_SPLIT_K (1, 2 or 4; default 1), read here,
-   splits K of the dot-product GEMV over that many of a block's 4 waves
-   (partial sums reduced through LDS in a fixed order); any other value is
-   QMOE_ERR_ARG.  It changes the speed and the fp32 summation order, not the
-   result's tolerance. */
+   if the current device is not gfx950.  The weights are not read here: the
+   ranges above (group scales <= 511.75) are the caller's to keep.  Nothing
+   is read from the environment. */
 int qmoe_layer_create(const qmoe_layer_desc* desc, qmoe_layer** out);
 void qmoe_layer_destroy(qmoe_layer* layer);
 
@@ -129,9 +134,12 @@ int qmoe_workspace_size(const qmoe_layer* layer, int64_t M, size_t* bytes);
    per-chunk token masks, itself: one extra small launch). */
 int qmoe_workspace_init(qmoe_layer* layer, void* workspace, size_t ws_bytes, void* stream);
 
-/* The whole layer: route, gate+up, down, combine (four kernel launches).
-   x: bf16 [M,H]; logits: fp32 [M,E]; out: bf16 [M,H] (device pointers).
-   M == 0 is a no-op.  Graph-capturable for a fixed M. */
+/* The whole layer: route, gate+up, down, combine: four kernel launches,
+   five for calls of more than 64 tokens (a small kernel first clears the
+   routing ticket the routing blocks meet at).
+   x: bf16 [M,H] (any finite values; see the ranges above); logits: fp32
+   [M,E], finite; out: bf16 [M,H] (device pointers, 16-byte aligned).
+   M == 0 is a no-op.  Graph-capturable for a fixed M (no memset nodes). */
 int qmoe_forward(qmoe_layer* layer, const void* x, const float* logits, int64_t M,
                  void* out, void* workspace, size_t ws_bytes, void* stream);
 

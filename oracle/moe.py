@@ -176,6 +176,20 @@ def expert_mlp(X: np.ndarray, w: dict, I: int, return_h: bool = False):
 # ------------------------------------------------------------------- layer
 
 
+def combine(w_row: np.ndarray, y_rows, shared_row=None) -> np.ndarray:
+    """One token's output: sum over its slots j = 0..k-1, in j order, of
+    w[j] * y[j] (y[j] the MLP output of its j-th selected expert), then the
+    shared expert's row, when there is one, with weight 1.0.  Source: "perf(exl3):
+    accelerate fat-expert prefill", description (results scattered back to
+    their tokens) and the routing-weighted sum of the layer."""
+    acc = np.zeros(np.asarray(y_rows[0]).shape, dtype=np.float64)
+    for j in range(len(w_row)):
+        acc += w_row[j] * y_rows[j]
+    if shared_row is not None:
+        acc = acc + shared_row
+    return acc
+
+
 def forward(x_bits: np.ndarray, logits: np.ndarray, k: int, get_expert, I: int,
             shared=None, tokens=None, return_h: bool = False) -> dict:
     """The layer: out[t] = sum_j w[t,j] * MLP_{ids[t,j]}(x[t]) (+ shared
@@ -208,14 +222,10 @@ def forward(x_bits: np.ndarray, logits: np.ndarray, k: int, get_expert, I: int,
             Y[(t, j)] = y[n]
             if return_h:
                 Hs[t * k + j] = out[1][n]
+    Ys = expert_mlp(xf[sel], shared, I) if shared is not None and sel.size else None
     res = np.zeros((sel.size, H), dtype=np.float64)
     for n, t in enumerate(sel):
-        acc = np.zeros(H, dtype=np.float64)
-        for j in range(k):
-            acc += w[t, j] * Y[(int(t), j)]
-        res[n] = acc
-    if shared is not None and sel.size:
-        res += expert_mlp(xf[sel], shared, I)
+        res[n] = combine(w[t], [Y[(int(t), j)] for j in range(k)], None if Ys is None else Ys[n])
     r.update({"out": res, "tokens": sel})
     if return_h:
         r["h"] = Hs

@@ -78,13 +78,13 @@ struct RouteArgs {
   int* perm;
   int* inv_perm;
   int4* items;
-  uint4* xa;  // fp16 A-format [M, H]
+  uint4* xa;   // fp16 A-format [M, H], row t times 2^-xexp[t]
+  int* xexp;   // [M] per-token exponent
 };
 
 constexpr int kRouteThreads = 1024;  // routing blocks: 16 waves
-constexpr int kRouteWaves = kRouteThreads / 64;
-constexpr int kXRuns = 8 * kRouteThreads;  // 16-byte runs of x per conversion block
-constexpr int kSubs = 4;                    // routing blocks per chunk for calls of 2..kMaxSplitChunks chunks
+constexpr int kRouteWaves = kRouteThreads / 64;  // also token rows per conversion block
+constexpr int kSubs = 4;                   // routing blocks per chunk for calls of 2..kMaxSplitChunks chunks
 constexpr int kMaxSplitChunks = 16;         // beyond, one block per chunk: the per-block fences dominate
 
 // Counts, offsets and the flat work list from the per-expert row counts in
@@ -190,19 +190,29 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
   const int t_lo = (blockIdx.x % a.subs) * (kChunk / a.subs);
   const int t_hi = min(rows, t_lo + kChunk / a.subs);
 
-  // blocks past the routing blocks convert x to the fp16 operand format,
-  // kXRuns 16-byte runs each, spread over the GPU
+  // blocks past the routing blocks convert x to the fp16 operand format, one
+  // wave per token row: the row's largest |x| sets its exponent e, and the
+  // row is stored times 2^-e (exact), so any finite bf16 row fits fp16
   if ((int)blockIdx.x >= a.nrb) {
-    const long long n = (long long)a.M * (a.H / 8);
-    const long long q0 = (long long)((int)blockIdx.x - a.nrb) * kXRuns + tid;
-    uint4 v[kXRuns / kRouteThreads];
+    const int t = ((int)blockIdx.x - a.nrb) * kRouteWaves + wave;
+    if (t >= a.M) return;
+    const int runs = a.H / 8;
+    const uint4* __restrict__ row = a.x + (size_t)t * runs;
+    uint32_t amax = 0;
+    int v = lane;
+    for (; v + 3 * 64 < runs; v += 4 * 64) {  // four loads in flight per lane
+      uint4 r[4];
 #pragma unroll
-    for (int u = 0; u < kXRuns / kRouteThreads; ++u) v[u] = a.x[min(q0 + (long long)u * kRouteThreads, n - 1)];  // clamped
+      for (int u = 0; u < 4; ++u) r[u] = row[v + u * 64];
 #pragma unroll
-    for (int u = 0; u < kXRuns / kRouteThreads; ++u) {
-      const long long q = q0 + (long long)u * kRouteThreads;
-      if (q < n) a.xa[q] = bf16x8_to_aformat(v[u]);
+      for (int u = 0; u < 4; ++u) amax = max(amax, absmax_bf16x8(r[u]));
     }
+    for (; v < runs; v += 64) amax = max(amax, absmax_bf16x8(row[v]));
+    const int e = row_exponent(wave_max_u32(amax));
+    const float sc = pow2f(-e);
+    uint4* __restrict__ dst = a.xa + (size_t)t * runs;
+    for (v = lane; v < runs; v += 64) dst[v] = bf16x8_to_aformat(row[v], sc);  // the row again, from cache
+    if (lane == 0) a.xexp[t] = e;
     return;
   }
 
@@ -362,6 +372,7 @@ struct GemmArgs {
   const int4* items;
   const int* perm;
   const float* wts;
+  const int* xexp;    // [M] per-token exponent e: x rows are held times 2^-e, h rows times 2^-2e
   const _Float16* a;  // A rows in A-format: x (gate+up) or h (down)
   uint32_t a_bytes;      // bytes of the A buffer (loads past it read 0)
   _Float16* h_out;    // gate+up: h [R, N] in A-format
@@ -442,7 +453,6 @@ constexpr int kSuper = 4 * kKStep;     // inputs per super-step (16 groups)
 // per-step offset (no vector address arithmetic); inputs past K read zeros.
 template <int MB, int WN, int NBW, bool GATEUP>
 __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP ? kGuWPE : kDnWPE))) void gemm_kernel(GemmArgs g) {
-  constexpr int WK = 1;
   static_assert(WN == 4 || WN == 8, "4 or 8 waves along N");
   static_assert(MB > 1, "row tiles of at least 32 rows");
   constexpr int NBB = GATEUP ? 2 * NBW : NBW;
@@ -450,7 +460,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   // wave index as a wave-uniform (scalar) value, so loop bounds derived
   // from it give scalar branches and exact load counters
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave % WN, wk = wave / WN;
+  const int wn = wave;
   const int r = lane & 15, kq = lane >> 4;
 
   // all blocks of one item land on one XCD (block ids go round-robin over
@@ -499,12 +509,11 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
     }
   }
 
-  // super-steps: nss_full whole ones, then (if K % 512 != 0) one partial,
-  // taken by the last wave along K with its missing groups masked
+  // super-steps: nss_full whole ones, then (if K % 512 != 0) one partial
+  // with its missing groups masked
   const int nss_full = g.K / kSuper, nss = (g.K + kSuper - 1) / kSuper;
-  const int S_begin = wk * nss / WK, S_end = (wk + 1) * nss / WK;
-  const int S_end_full = min(S_end, nss_full);
-  const bool has_tail = S_end > nss_full;
+  const int S_begin = 0, S_end_full = nss_full;
+  const bool has_tail = nss > nss_full;
   const int ngroups = g.K / 32;
   const int nmb = (nr + 15) / 16;
 
@@ -543,17 +552,12 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
       sc[b][1] = v[1];
     }
   };
-  // byte offset of the activation row of tile row m (m < nr)
-  auto a_off_of = [&](int m) __attribute__((always_inline)) -> uint32_t {
-    const int pos = pos0 + m;
-    if (GATEUP) {
-      const int slot = g.perm[pos];
-      if (slot < 0 || slot >= g.R) return kOob;
-      const int tok = slot < g.T ? slot / g.k : slot - g.T;
-      if (tok >= g.M) return kOob;
-      return (uint32_t)tok * (uint32_t)g.K * 2;
-    }
-    return (uint32_t)pos * (uint32_t)g.K * 2;
+  // token of tile row m (m < nr), from its sorted slot; -1 if the slot is
+  // not one of the call's
+  auto tok_of = [&](int slot) __attribute__((always_inline)) -> int {
+    if (slot < 0 || slot >= g.R) return -1;
+    const int tok = slot < g.T ? slot / g.k : slot - g.T;
+    return tok < g.M ? tok : -1;
   };
 
   // ---------------- prefill tiles: the activation tile of each sub-step
@@ -571,7 +575,6 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   // (kq + rr) mod 4 (4 conflict cycles per 8-cycle read): with the new slots
   // it measured up to 1% slower, so these reads do not bound it.  Wave w
   // loads block q = w mod 4 of every (WN/4)-th row block, starting at w / 4.
-  static_assert(WK == 1, "128-row tiles split N across waves, not K");
   constexpr int kBlkHalves = 520;  // 1040-byte LDS block
   // two buffers as separate arrays, so that the compiler can tell loads
   // into one from operand reads of the other
@@ -589,17 +592,23 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
     load_b(S_begin, 0, fb0, true);
     load_b(S_begin, 1, fb1, true);
   }
-  // per tile row: activation offset; down: also its slot and routing
-  // weight, read by the epilogue
+  // per tile row: activation offset and the token's scale, read by the
+  // epilogue (gate+up: 2^e, which takes x's scaling off g and u; down: its
+  // slot, and the routing weight times 2^2e, which takes h's scaling off)
   __shared__ uint32_t lds_row[MB * 16];
+  __shared__ float lds_sc[MB * 16];
   __shared__ int lds_slot[GATEUP ? 1 : MB * 16];
-  __shared__ float lds_w[GATEUP ? 1 : MB * 16];
   for (int m = tid; m < MB * 16; m += 64 * WN) {
-    lds_row[m] = m < nr ? a_off_of(m) : kOob;
-    if (!GATEUP) {
-      const int slot = m < nr ? g.perm[pos0 + m] : -1;
+    const int slot = m < nr ? g.perm[pos0 + m] : -1;
+    const int tok = tok_of(slot);
+    const int e = tok >= 0 ? g.xexp[tok] : 0;
+    if (GATEUP) {
+      lds_row[m] = tok >= 0 ? (uint32_t)tok * (uint32_t)g.K * 2 : kOob;
+      lds_sc[m] = pow2f(e);
+    } else {
+      lds_row[m] = m < nr ? (uint32_t)(pos0 + m) * (uint32_t)g.K * 2 : kOob;
       lds_slot[m] = slot;
-      lds_w[m] = (slot >= 0 && slot < g.T) ? g.wts[slot] : 1.0f;
+      lds_sc[m] = ((slot >= 0 && slot < g.T) ? g.wts[slot] : 1.0f) * pow2f(2 * e);
     }
   }
   __syncthreads();
@@ -871,15 +880,17 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
         if (row >= nr) continue;
         const int pos = pos0 + row;
         if (GATEUP) {
-          const float gt = acc[mb][2 * c][i], up = acc[mb][2 * c + 1][i];
-          // odd columns are stored divided by 16 (operand format)
-          const float hv = gt / (1.0f + __expf(-gt)) * up * ((col & 1) ? 0.0625f : 1.0f);
+          // g = acc * 2^e; h is stored times 2^-2e: SiLU(g) * (acc_up * 2^-e),
+          // odd columns divided by 16 (operand format)
+          const float sc = lds_sc[row];
+          const float gt = acc[mb][2 * c][i] * sc;
+          const float up = acc[mb][2 * c + 1][i] * inv_pow2f(sc) * ((col & 1) ? 0.0625f : 1.0f);
+          const float hv = gt / (1.0f + __expf(-gt)) * up;
           g.h_out[(size_t)pos * g.N + ((col & ~7) | inv_perm8(col & 7))] = (_Float16)hv;
         } else {
           const int slot = lds_slot[row];
           if (slot < 0 || slot >= g.R) continue;
-          const float wv = lds_w[row];
-          g.y_out[(size_t)slot * g.N + col] = (uint16_t)f32_to_bf16_rne(wv * acc[mb][c][i]);
+          g.y_out[(size_t)slot * g.N + col] = (uint16_t)f32_to_bf16_rne(lds_sc[row] * acc[mb][c][i]);
         }
       }
     }
@@ -934,15 +945,14 @@ constexpr int kGemvWPE = 2;
 // default policy on MI355X; it pays only while each expert's codes are read
 // once (about one routed row per expert or fewer).  Scales keep the default
 // policy (non-temporal scales measured slower at every M).
-template <int WN, int WK, bool GATEUP, bool NT>
+template <bool GATEUP, bool NT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kGemvWPE))) void gemv_kernel(
     GemmArgs g) {
-  static_assert(WN * WK == 4, "4 waves per block");
+  constexpr int WN = kThreads / 64;      // waves along N
   constexpr int NBB = 2;                 // weight blocks of 16 rows per wave
   constexpr int NBW = GATEUP ? 1 : 2;    // output column blocks per wave
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave % WN, wk = wave / WN;
+  const int wn = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 4, j = lane & 15;
 
   // consecutive blocks take consecutive column blocks of one item, so each
@@ -989,9 +999,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kGemvW
   }
 
   const int nss_full = g.K / kSuper, nss = (g.K + kSuper - 1) / kSuper;
-  const int S_begin = wk * nss / WK, S_end = (wk + 1) * nss / WK;
-  const int S_end_full = min(S_end, nss_full);
-  const bool has_tail = S_end > nss_full;
+  const int S_begin = 0, S_end_full = nss_full;
+  const bool has_tail = nss > nss_full;
   const int ngroups = g.K / 32;
 
   // one super-step of this lane's weights: group j of rows 4m + q of each
@@ -1019,18 +1028,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kGemvW
   // the first super-step's loads go out before the rows are staged
   Super fa, fb;
   if (S_end_full > S_begin) load_super(S_begin, fa, true);
-  // down: each row's slot and routing weight are read now, so their two
-  // dependent round trips overlap the weight stream instead of following it
-  int slot_of[kGemvRows];
-  float w_of[kGemvRows];
-  if (!GATEUP) {
+  // each row's slot, token and scale are read now, so their dependent round
+  // trips overlap the weight stream instead of following it.  Gate+up: 2^e
+  // (x rows are held times 2^-e); down: the routing weight times 2^2e (h
+  // rows are held times 2^-2e)
+  int slot_of[kGemvRows], tok_of[kGemvRows];
+  float sc_of[kGemvRows];
 #pragma unroll
-    for (int t = 0; t < kGemvRows; ++t) slot_of[t] = t < nr ? g.perm[pos0 + t] : -1;
+  for (int t = 0; t < kGemvRows; ++t) {
+    const int sl = t < nr ? g.perm[pos0 + t] : -1;
+    const int tok = (sl >= 0 && sl < g.R) ? (sl < g.T ? sl / g.k : sl - g.T) : -1;
+    slot_of[t] = sl;
+    tok_of[t] = tok < g.M ? tok : -1;
+  }
 #pragma unroll
-    for (int t = 0; t < kGemvRows; ++t) {
-      const int sl = slot_of[t];
-      w_of[t] = (sl >= 0 && sl < g.T) ? g.wts[sl] : 1.0f;
-    }
+  for (int t = 0; t < kGemvRows; ++t) {
+    const int e = tok_of[t] >= 0 ? g.xexp[tok_of[t]] : 0;
+    const int sl = slot_of[t];
+    sc_of[t] = GATEUP ? pow2f(e) : ((sl >= 0 && sl < g.T) ? g.wts[sl] : 1.0f) * pow2f(2 * e);
   }
 
   // ---- stage the item's activation rows (operand format) in LDS: group
@@ -1044,9 +1059,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kGemvW
   for (int t = 0; t < nr; ++t) {
     uint32_t off;
     if (GATEUP) {
-      const int slot = g.perm[pos0 + t];
-      const int tok = slot < g.T ? slot / g.k : slot - g.T;
-      off = (slot >= 0 && slot < g.R && tok < g.M) ? (uint32_t)tok * (uint32_t)g.K * 2 : kOob;
+      off = tok_of[t] >= 0 ? (uint32_t)tok_of[t] * (uint32_t)g.K * 2 : kOob;
     } else {
       off = (uint32_t)(pos0 + t) * (uint32_t)g.K * 2;
     }
@@ -1175,28 +1188,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kGemvW
       res[b][t] = j == 0 ? acc[b][0][t] : j == 1 ? acc[b][1][t] : j == 2 ? acc[b][2][t] : acc[b][3][t];
     }
   const int r = 4 * j + q;  // this lane's row in each block (lanes with j < 4)
-  // ---- then over the WK waves along K (fixed order: wave wk=0 adds 1, 2, 3)
-  if constexpr (WK > 1) {
-    float* red = reinterpret_cast<float*>(gemv_lds);  // the staged rows are dead by now
-    constexpr int kVals = NBB * kGemvRows;
-    __syncthreads();
-    if (wk > 0 && j < 4) {
-#pragma unroll
-      for (int b = 0; b < NBB; ++b)
-#pragma unroll
-        for (int t = 0; t < kGemvRows; ++t)
-          red[(((wk - 1) * WN + wn) * kVals + b * kGemvRows + t) * 16 + r] = res[b][t];
-    }
-    __syncthreads();
-    if (wk > 0) return;
-#pragma unroll
-    for (int w = 1; w < WK; ++w)
-#pragma unroll
-      for (int b = 0; b < NBB; ++b)
-#pragma unroll
-        for (int t = 0; t < kGemvRows; ++t)
-          if (j < 4) res[b][t] += red[(((w - 1) * WN + wn) * kVals + b * kGemvRows + t) * 16 + r];
-  }
   if (j >= 4) return;
 
   // ---- epilogue: lane (q, j) holds weight row r = 4j + q of each block
@@ -1207,14 +1198,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kGemvW
     if (GATEUP) {
       if (col0[0] >= g.N) continue;
       const int col = col0[0] + r;
-      const float gt = res[0][t], up = res[1][t];
-      // odd columns are stored divided by 16 (operand format)
-      const float hv = gt / (1.0f + __expf(-gt)) * up * ((col & 1) ? 0.0625f : 1.0f);
+      // g = res * 2^e; h is stored times 2^-2e, odd columns divided by 16
+      const float gt = res[0][t] * sc_of[t];
+      const float up = res[1][t] * inv_pow2f(sc_of[t]) * ((col & 1) ? 0.0625f : 1.0f);
+      const float hv = gt / (1.0f + __expf(-gt)) * up;
       g.h_out[(size_t)pos * g.N + ((col & ~7) | inv_perm8(col & 7))] = (_Float16)hv;
     } else {
       const int slot = slot_of[t];
       if (slot < 0 || slot >= g.R) continue;
-      const float wv = w_of[t];
+      const float wv = sc_of[t];
 #pragma unroll
       for (int c = 0; c < NBW; ++c) {
         if (col0[c] >= g.N) continue;
@@ -1283,16 +1275,20 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t* w, co
   for (int p = 0; p < 8; ++p) out[(size_t)n * K + d * 8 + perm8(p)] = h[p];
 }
 
-__global__ __launch_bounds__(kThreads) void read_h_kernel(const _Float16* h, const int* inv_perm, int T,
-                                                           long long R, int I, float* out) {
+// h rows are held in sorted order, times 2^-2e of their token, odd columns
+// divided by 16; out: slot order, true scale.
+__global__ __launch_bounds__(kThreads) void read_h_kernel(const _Float16* h, const int* inv_perm,
+                                                           const int* xexp, int T, int k, long long R, int I,
+                                                           float* out) {
   const long long q = (long long)blockIdx.x * kThreads + threadIdx.x;
   if (q >= R * I) return;
   const long long f = q / I;
   const int col = (int)(q % I);
   long long pos = f < T ? inv_perm[f] : f;
   if (pos < 0 || pos >= R) pos = f;
-  const float v = (float)h[pos * I + ((col & ~7) | inv_perm8(col & 7))];
-  out[q] = (col & 1) ? v * 16.0f : v;  // odd columns are stored divided by 16
+  const long long tok = f < T ? f / k : f - T;
+  const float v = (float)h[pos * I + ((col & ~7) | inv_perm8(col & 7))] * pow2f(2 * xexp[tok]);
+  out[q] = (col & 1) ? v * 16.0f : v;
 }
 
 __global__ __launch_bounds__(kThreads) void read_y_kernel(const uint16_t* y, long long n, float* out) {
@@ -1325,7 +1321,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
   int64_t T, S, R, C, max_items_all;
-  size_t ctrl, ids, wts, counts, offsets, cmask, pbase, perm, inv_perm, items, xa, h, y, total;
+  size_t ctrl, ids, wts, counts, offsets, cmask, pbase, perm, inv_perm, items, xexp, xa, h, y, total;
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -1342,7 +1338,6 @@ struct qmoe_layer {
   bool shared = false;
   std::atomic<uint64_t> forward_calls{0}, route_calls{0}, gemm_launches{0}, launches{0}, inits{0},
       ws_last{0}, ws_peak{0}, prefill_tiles{0}, gemv_tiles{0}, gemv_nt{0};
-  int split_k = 1;  // GEMV K split (1, 2 or 4 waves along K)
 };
 
 namespace {
@@ -1371,6 +1366,7 @@ Layout make_layout(const qmoe_layer* L, int64_t M) {
   l.perm = take(l.R * 4);
   l.inv_perm = take(l.T * 4);
   l.items = take(l.max_items_all * 16);
+  l.xexp = take(M * 4);
   l.xa = take(M * H * 2);
   l.h = take(l.R * I * 2);
   l.y = take(l.R * H * 2);
@@ -1466,6 +1462,7 @@ int do_route(qmoe_layer* L, const void* x, const float* logits, int64_t M, void*
   a.inv_perm = at<int>(ws, lay.inv_perm);
   a.items = at<int4>(ws, lay.items);
   a.xa = at<uint4>(ws, lay.xa);
+  a.xexp = at<int>(ws, lay.xexp);
   a.subs = (lay.C > 1 && lay.C <= kMaxSplitChunks) ? kSubs : 1;
   a.nrb = (int)lay.C * a.subs;
   if (lay.C > 1) {
@@ -1478,8 +1475,8 @@ int do_route(qmoe_layer* L, const void* x, const float* logits, int64_t M, void*
     const int rc = check_launch(L, "ticket and mask clear");
     if (rc != QMOE_OK) return rc;
   }
-  // routing blocks, then the blocks that convert x
-  const int64_t xblocks = ceil_div(M * (L->d.H / 8), (int64_t)kXRuns);
+  // routing blocks, then the blocks that convert x (one wave per token row)
+  const int64_t xblocks = ceil_div(M, (int64_t)kRouteWaves);
   const dim3 grid((unsigned)(a.nrb + xblocks));
   const int epl = (L->d.E + 63) / 64;
   if (epl <= 1) route_kernel<1><<<grid, kRouteThreads, 0, st>>>(a);
@@ -1504,6 +1501,7 @@ void fill_gemm_args(const qmoe_layer* L, int64_t M, void* ws, const Layout& lay,
   g.items = at<int4>(ws, lay.items);
   g.perm = at<int>(ws, lay.perm);
   g.wts = at<float>(ws, lay.wts);
+  g.xexp = at<int>(ws, lay.xexp);
   if (GATEUP) {
     g.w = L->d.w13;
     g.s = L->d.s13;
@@ -1546,9 +1544,9 @@ int launch_gemm(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream
   return check_launch(L, GATEUP ? "gate_up gemm" : "down gemm");
 }
 
-template <int WN, bool GATEUP>
+template <bool GATEUP>
 int launch_gemv(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t st) {
-  constexpr int WK = 4 / WN;
+  constexpr int WN = kThreads / 64;
   GemmArgs g;
   fill_gemm_args<GATEUP>(L, M, ws, lay, g);
   g.max_items = (int)max_items_for(lay.T, M, lay.S, L->d.E, kGemvRows);
@@ -1556,40 +1554,31 @@ int launch_gemv(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream
   g.nblk = (int)ceil_div(g.N, WN * cols);
   const int64_t blocks = (int64_t)g.nblk * g.max_items;
   if (blocks > 0x7FFFFFFF) return fail(QMOE_ERR_UNSUPPORTED, "grid too large");
-  const size_t lds = std::max<size_t>(gemv_lds_bytes(g.K), (size_t)(WK - 1) * WN * 2 * kGemvRows * 16 * 4);
+  const size_t lds = gemv_lds_bytes(g.K);
   // non-temporal code reads while each expert's codes are read about once:
   // at most one routed row per expert on average and no shared expert (whose
   // codes every item of the call reads)
   const bool nt = M * L->d.top_k <= L->d.E && L->d.shared_w13 == nullptr;
   if (nt) {
-    gemv_kernel<WN, WK, GATEUP, true><<<dim3((unsigned)blocks), kThreads, lds, st>>>(g);
+    gemv_kernel<GATEUP, true><<<dim3((unsigned)blocks), kThreads, lds, st>>>(g);
     L->gemv_nt++;
   } else
-    gemv_kernel<WN, WK, GATEUP, false><<<dim3((unsigned)blocks), kThreads, lds, st>>>(g);
+    gemv_kernel<GATEUP, false><<<dim3((unsigned)blocks), kThreads, lds, st>>>(g);
   L->gemm_launches++;
   return check_launch(L, GATEUP ? "gate_up gemv" : "down gemv");
-}
-
-// GEMV shape: 4 waves along N, or K split over 2 or 4 of them (the split
-// each layer was created with; see qmoe_layer_create)
-template <bool GATEUP>
-int launch_gemv_split(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t st) {
-  if (L->split_k == 4) return launch_gemv<1, GATEUP>(L, M, ws, lay, st);
-  if (L->split_k == 2) return launch_gemv<2, GATEUP>(L, M, ws, lay, st);
-  return launch_gemv<4, GATEUP>(L, M, ws, lay, st);
 }
 
 int do_gate_up(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t st) {
   if (regime_of(L, M) == kGemv) {
     L->gemv_tiles++;
-    return launch_gemv_split<true>(L, M, ws, lay, st);
+    return launch_gemv<true>(L, M, ws, lay, st);
   }
   L->prefill_tiles++;
   return launch_gemm<kTileMB, kGuWN, kGuNBW, true>(L, M, ws, lay, st);
 }
 
 int do_down(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t st) {
-  if (regime_of(L, M) == kGemv) return launch_gemv_split<false>(L, M, ws, lay, st);
+  if (regime_of(L, M) == kGemv) return launch_gemv<false>(L, M, ws, lay, st);
   return launch_gemm<kTileMB, kDnWN, kDnNBW, false>(L, M, ws, lay, st);
 }
 
@@ -1638,11 +1627,6 @@ int qmoe_layer_create(const qmoe_layer_desc* d, qmoe_layer** out) {
   if (nsh != 0 && nsh != 4) return fail(QMOE_ERR_ARG, "shared expert: set all four pointers or none");
   if (!aligned16(d->w13) || !aligned16(d->w2) || (nsh && (!aligned16(d->shared_w13) || !aligned16(d->shared_w2))))
     return fail(QMOE_ERR_ARG, "weight code arrays must be 16-byte aligned");
-  int split_k = 1;
-  if (const char* v = std::getenv("QMOE_SPLIT_K")) {
-    split_k = std::atoi(v);
-    if (split_k != 1 && split_k != 2 && split_k != 4) return fail(QMOE_ERR_ARG, "QMOE_SPLIT_K must be 1, 2 or 4");
-  }
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return fail(QMOE_ERR_DEVICE, "no HIP device (hipGetDevice failed)");
   hipDeviceProp_t prop;
@@ -1653,7 +1637,6 @@ int qmoe_layer_create(const qmoe_layer_desc* d, qmoe_layer** out) {
   L->d = *d;
   L->device = dev;
   L->shared = nsh == 4;
-  L->split_k = split_k;
   *out = L;
   return QMOE_OK;
 }
@@ -1754,7 +1737,8 @@ int qmoe_read_intermediate(qmoe_layer* L, int64_t M, const void* ws, size_t ws_b
   if (which == 0) {
     const int64_t n = lay.R * L->d.I;
     read_h_kernel<<<dim3((unsigned)ceil_div(n, kThreads)), kThreads, 0, st>>>(
-        at<_Float16>(w, lay.h), at<int>(w, lay.inv_perm), (int)lay.T, lay.R, L->d.I, out_f32);
+        at<_Float16>(w, lay.h), at<int>(w, lay.inv_perm), at<int>(w, lay.xexp), (int)lay.T, L->d.top_k, lay.R,
+        L->d.I, out_f32);
     return check_launch(L, "read_h_kernel");
   }
   if (which == 1) {

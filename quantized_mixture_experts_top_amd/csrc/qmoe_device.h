@@ -1,7 +1,9 @@
 // Device-side building blocks of the fused int4 MoE layer for gfx950.
 //
 // Operand format ("A-format"): activations that feed the MFMA contraction are
-// stored as fp16, and inside every run of 8 consecutive inputs the values are
+// stored as fp16 scaled per token by a power of two (each token's hidden row
+// times 2^-e so that its largest |value| lies in [1, 2); its h row times
+// 2^-2e), and inside every run of 8 consecutive inputs the values are
 // kept in the order of input offsets {0,4,1,5,2,6,3,7}, with the values at
 // odd offsets divided by 16 (exact for normal fp16 values).  That matches
 // dq8() below, which produces decoded weights from one 32-bit word of packed
@@ -82,15 +84,49 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
-// 8 bf16 (natural order) -> 8 fp16 in A-format order.  bf16 -> fp32 is
-// exact, the odd offsets are divided by 16 (exact), and fp32 -> fp16 is exact
-// for values inside the fp16 normal range.
-__device__ __forceinline__ uint4 bf16x8_to_aformat(uint4 in) {
+// 2^n as a float, for n in [-126, 127] (built from the exponent field).
+__device__ __forceinline__ float pow2f(int n) { return __int_as_float((n + 127) << 23); }
+// 1/p for p = 2^n, n in [-126, 126] (exact; no division).
+__device__ __forceinline__ float inv_pow2f(float p) { return __int_as_float(0x7F000000 - __float_as_int(p)); }
+
+// Largest |value| of 8 bf16 (one 16-byte run) as a magnitude bit pattern:
+// for finite values the order of the 15-bit patterns is the order of the
+// magnitudes.
+__device__ __forceinline__ uint32_t absmax_bf16x8(uint4 in) {
+  uint32_t m = 0;
+  const uint32_t w[4] = {in.x, in.y, in.z, in.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
+    m = lo > m ? lo : m;
+    m = hi > m ? hi : m;
+  }
+  return m;
+}
+
+// Exponent e of a token row whose largest |x| has the bf16 magnitude pattern
+// amax: 2^e <= amax < 2^(e+1), so the row times 2^-e has its largest value
+// in [1, 2).  A row of zeros gets e = 0; e is clamped to [-kExpClamp,
+// kExpClamp] so that 2^(+-2e) stays a normal float.
+constexpr int kExpClamp = 60;
+__device__ __forceinline__ int row_exponent(uint32_t amax) {
+  if (amax == 0) return 0;
+  const int field = (int)(amax >> 7);  // bf16 exponent field (8 bits)
+  const int e = field == 0 ? -127 : field - 127;
+  return e < -kExpClamp ? -kExpClamp : (e > kExpClamp ? kExpClamp : e);
+}
+
+// 8 bf16 (natural order) times sc (a power of two) -> 8 fp16 in A-format
+// order.  bf16 -> fp32 is exact, the scaling and the division of the odd
+// offsets by 16 are exact, and fp32 -> fp16 is exact for results inside the
+// fp16 normal range (rounded to nearest even below it).
+__device__ __forceinline__ uint4 bf16x8_to_aformat(uint4 in, float sc) {
+  const float so = sc * 0.0625f;
   float f[8];
-  f[0] = bf16_lo(in.x); f[1] = bf16_hi(in.x) * 0.0625f;
-  f[2] = bf16_lo(in.y); f[3] = bf16_hi(in.y) * 0.0625f;
-  f[4] = bf16_lo(in.z); f[5] = bf16_hi(in.z) * 0.0625f;
-  f[6] = bf16_lo(in.w); f[7] = bf16_hi(in.w) * 0.0625f;
+  f[0] = bf16_lo(in.x) * sc; f[1] = bf16_hi(in.x) * so;
+  f[2] = bf16_lo(in.y) * sc; f[3] = bf16_hi(in.y) * so;
+  f[4] = bf16_lo(in.z) * sc; f[5] = bf16_hi(in.z) * so;
+  f[6] = bf16_lo(in.w) * sc; f[7] = bf16_hi(in.w) * so;
   half2_t o0 = {(_Float16)f[0], (_Float16)f[4]};
   half2_t o1 = {(_Float16)f[1], (_Float16)f[5]};
   half2_t o2 = {(_Float16)f[2], (_Float16)f[6]};

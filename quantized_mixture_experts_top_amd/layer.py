@@ -52,7 +52,7 @@ class Layer:
         check(self.lib.qmoe_layer_create(ctypes.byref(desc), ctypes.byref(handle)))
         self.handle = handle
         self.device = w13.device
-        self._ws = None
+        self._ws = {}  # stream handle -> workspace used by calls on that stream
 
     def close(self):
         if getattr(self, "handle", None):
@@ -73,15 +73,24 @@ class Layer:
         return n.value
 
     def workspace(self, M: int, stream=None) -> torch.Tensor:
-        """A workspace large enough for M tokens, kept and grown as needed.
+        """The workspace of calls on `stream` (default: the current stream),
+        large enough for M tokens, kept and grown as needed.  Each stream has
+        its own (calls that overlap must not share one), allocated while that
+        stream is current, so the caching allocator does not hand its memory
+        to anyone else before the stream's queued kernels are done with it.
         A new allocation is initialised explicitly (its memory may have held
         other tensors)."""
+        s = torch.cuda.current_stream() if stream is None else stream
         need = self.workspace_bytes(M)
-        if self._ws is None or self._ws.numel() < need:
-            self._ws = None
-            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
-            check(self.lib.qmoe_workspace_init(self.handle, _ptr(self._ws), self._ws.numel(), _stream(stream)))
-        return self._ws
+        ws = self._ws.get(s.cuda_stream)
+        if ws is None or ws.numel() < need:
+            self._ws.pop(s.cuda_stream, None)
+            del ws
+            with torch.cuda.stream(s):
+                ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+            check(self.lib.qmoe_workspace_init(self.handle, _ptr(ws), ws.numel(), _stream(s)))
+            self._ws[s.cuda_stream] = ws
+        return ws
 
     def _args(self, M, stream):
         ws = self.workspace(M, stream)

@@ -67,12 +67,11 @@ def test_create_rejects_bad_fields(lib, field, value, needle):
     assert not h.value
 
 
-def test_create_rejects_bad_split_k(lib, monkeypatch):
-    monkeypatch.setenv("QMOE_SPLIT_K", "3")
-    h = ctypes.c_void_p()
-    assert lib.qmoe_layer_create(ctypes.byref(_desc()), ctypes.byref(h)) == B.QMOE_ERR_ARG
-    assert "QMOE_SPLIT_K" in lib.qmoe_last_error().decode()
-    assert not h.value
+def test_library_reads_no_environment():
+    """No kernel path is chosen from the environment: the library source
+    calls no getenv."""
+    src = open(os.path.join(ROOT, "quantized_mixture_experts_top_amd", "csrc", "qmoe.hip")).read()
+    assert "getenv" not in src
 
 
 def test_create_null_arguments(lib):

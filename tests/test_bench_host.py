@@ -27,7 +27,29 @@ def test_cpu_baseline_record():
     rec = bench.cpu_baseline(synth.TINY, 16, False)
     assert rec["kind"] == "oracle" and rec["unit"] == "tokens/s"
     assert rec["value"] > 0 and rec["cores"] >= 1
-    assert "routing for all 16" in rec["sample"]  # the sample says what was timed
+    assert "routing of all 16 tokens" in rec["sample"]  # the sample says what was timed
+    assert rec["cpu_model"] is not None and rec["blas"] and rec["host_cpus_visible"] >= 1
+
+
+def test_counter_summary(tmp_path):
+    """Gate+up bytes per launch from the two counter passes: per dispatch
+    the counter summed over its rows, averaged over the gate+up dispatches
+    only, scaled by the copy calibration, and stored with the source hash."""
+    def rows(*r):
+        return "Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n" + "".join(
+            f'{d},"void (anonymous namespace)::{k}(GemmArgs)",{c},{v}\n' for d, k, c, v in r)
+    f = tmp_path / "f.csv"
+    f.write_text(rows((1, "gemm_kernel<8, 4, 2, true>", "FETCH_SIZE", 100),
+                      (1, "gemm_kernel<8, 4, 2, true>", "FETCH_SIZE", 20),
+                      (2, "gemm_kernel<8, 4, 2, true>", "FETCH_SIZE", 140),
+                      (3, "gemm_kernel<8, 8, 1, false>", "FETCH_SIZE", 9999)))
+    w = tmp_path / "w.csv"
+    w.write_text(rows((5, "gemv_kernel<true, true>", "WRITE_SIZE", 3),
+                      (6, "gemv_kernel<false, true>", "WRITE_SIZE", 777)))
+    out = tmp_path / "traffic.json"
+    b = bench.summarize_counters("plateau:M=4096", str(f), str(w), str(out))
+    assert b == round(130 * 1024 * bench.FETCH_FACTOR + 3 * 1024 * bench.WRITE_FACTOR)
+    assert bench.stored_traffic("plateau", 4096, str(out)) == b
 
 
 @pytest.mark.parametrize("shape", [synth.TINY, synth.FULL])

@@ -149,6 +149,17 @@ FWD_CASES = [
     (16, 256, 1024, 2, 64, True),    # tiles: down items of <= 32 rows, 2 whole super-steps; shared expert
     (4, 256, 128, 1, 300, False),    # tiles: items of 4, 5 and 6 row blocks
     (4, 256, 128, 1, 400, False),    # tiles: items of 6 and 7 row blocks
+    # tiles with K >= 1536 in both products (3 whole super-steps: the
+    # pipelined K loops) and 65-128 routed rows per expert (items of 5-8 row
+    # blocks), every token compared; the shared expert adds items of 8 blocks
+    (4, 1536, 1536, 1, 300, False),
+    (4, 1536, 1536, 1, 300, True),
+    (4, 1536, 1536, 1, 360, False),
+    (4, 1536, 1536, 1, 360, True),
+    (4, 1536, 1536, 1, 400, False),
+    (4, 1536, 1536, 1, 400, True),
+    (4, 1536, 1536, 1, 500, False),
+    (4, 1536, 1536, 1, 500, True),
 ]
 
 
@@ -161,6 +172,16 @@ def _run_case(E, H, I, k, M, shared, seed=5):
     return layer, w, x, lg, ref
 
 
+def _item_blocks(counts, shared_rows):
+    """Row blocks of 16 of each 128-row MFMA work item (the K loop each
+    item runs through), over the routed experts and the shared expert."""
+    blocks = []
+    for c in list(counts) + ([shared_rows] if shared_rows else []):
+        for r0 in range(0, int(c), 128):
+            blocks.append((min(128, int(c) - r0) + 15) // 16)
+    return sorted(set(blocks))
+
+
 @pytest.mark.parametrize("E,H,I,k,M,shared", FWD_CASES)
 def test_forward_parity(E, H, I, k, M, shared):
     say(f"forward E={E} H={H} I={I} k={k} M={M} shared={shared}")
@@ -168,7 +189,10 @@ def test_forward_parity(E, H, I, k, M, shared):
     out = layer.forward(dev_bf16(x), dev(lg)).float().cpu().numpy()
     check_routing(layer, M, ref, E)
     err = rel_err(out, ref["out"])
-    say(f"  rel err out {err:.3e}")
+    tiles = layer.stats()["prefill_tiles"] > 0
+    where = (f"tiles, items of {_item_blocks(ref['counts'], M if shared else 0)} row blocks" if tiles
+             else "dot-product GEMV")
+    say(f"  all {M} tokens; {where}; rel err out {err:.3e}")
     assert err <= REL_TOL
 
 
@@ -200,23 +224,6 @@ def test_steps_match_oracle_intermediates(E, H, I, k, M, shared):
         assert rel_err(y[T:], ref_s) <= REL_TOL
     out = layer.combine(M).float().cpu().numpy()
     assert rel_err(out, ref["out"]) <= REL_TOL
-
-
-@pytest.mark.parametrize("split", ["2", "4"])
-@pytest.mark.parametrize("case", [(64, 1152, 640, 2, 20, False), (32, 2048, 1536, 4, 8, True),
-                                  (8, 512, 256, 2, 7, True)])
-def test_gemv_split_k_parity(monkeypatch, split, case):
-    """The GEMV with K split over 2 or 4 waves of a block (fixed-order LDS
-    reduction) against the oracle, and against the unsplit layer."""
-    import torch
-    monkeypatch.setenv("QMOE_SPLIT_K", split)
-    say(f"split-K {split} case {case}")
-    layer, w, x, lg, ref = _run_case(*case)
-    out = layer.forward(dev_bf16(x), dev(lg)).float().cpu().numpy()
-    assert layer.stats()["gemv_tiles"] == 1
-    err = rel_err(out, ref["out"])
-    say(f"  rel err out {err:.3e}")
-    assert err <= REL_TOL
 
 
 @pytest.mark.parametrize("M", [20, 2])  # 128-row tiles, dot-product items
@@ -328,6 +335,13 @@ def test_graph_capture_replays_match_eager(M):
     want = layer.forward(x, lg).clone()
     want2 = layer.forward(x2, lg2).clone()
     assert not torch.equal(want.view(torch.int16), want2.view(torch.int16))
+    # the eager result the replays must match is itself checked against the oracle
+    xn, ln = synth.hidden(4, M, shape.H), synth.logits(4, M, shape.E)
+    w = synth.all_experts(3, shape)
+    ref = oracle_moe.forward(xn, ln, shape.top_k, expert_getter(w), shape.I)
+    err = rel_err(want.float().cpu().numpy(), ref["out"])
+    say(f"graph M={M}: eager vs oracle rel err {err:.3e}")
+    assert err <= REL_TOL
     out = torch.empty_like(want)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -342,6 +356,59 @@ def test_graph_capture_replays_match_eager(M):
         got2 = layer.forward(x2, lg2)  # eager work in between, same workspace
         torch.cuda.synchronize()
         assert torch.equal(got2.view(torch.int16), want2.view(torch.int16))
+
+
+def _heavy_tailed(seed, M, H, frac=0.01, lo=100.0, hi=2000.0):
+    """N(0,1) hidden states with a fraction of entries replaced by
+    +-U(lo, hi) outliers, rounded to bf16."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, H)).astype(np.float32)
+    mask = rng.random((M, H)) < frac
+    x[mask] = (rng.uniform(lo, hi, int(mask.sum())) * rng.choice([-1.0, 1.0], int(mask.sum()))).astype(np.float32)
+    return synth.f32_to_bf16_bits(x)
+
+
+def _per_token_rel_err(got, ref):
+    scale = np.max(np.abs(ref), axis=1)
+    scale = np.where(scale > 0, scale, 1.0)
+    return float(np.max(np.max(np.abs(got.astype(np.float64) - ref), axis=1) / scale))
+
+
+# (E, H, I, k, M, shared): dot-product GEMV items and 128-row tiles
+RANGE_CASES = [(16, 1024, 512, 2, 4, False), (16, 1024, 512, 2, 96, True)]
+
+
+@pytest.mark.parametrize("case", RANGE_CASES)
+@pytest.mark.parametrize("kind", ["outliers", "x1e3", "x1e-4", "mixed"])
+def test_activation_range(case, kind):
+    """Hidden states outside N(0,1): 1% outliers of 100..2000 (the gate and
+    up products then reach ~1e6, past fp16), the whole input scaled by 1e3 or
+    1e-4, and rows of very different magnitudes in one call.  Each token's
+    row is scaled by its own power of two on the GPU, so every token must
+    match the oracle relative to its own largest output."""
+    E, H, I, k, M, shared = case
+    shape = synth.LayerShape(E=E, H=H, I=I, top_k=k, shared=shared)
+    layer, w = make_layer(shape, 11, M)
+    if kind == "outliers":
+        x = _heavy_tailed(12, M, H)
+    else:
+        xf = oracle_moe.decode_bf16(synth.hidden(12, M, H))
+        if kind == "x1e3":
+            xf = xf * 1e3
+        elif kind == "x1e-4":
+            xf = xf * 1e-4
+        else:  # token t scaled by 10^(t mod 9 - 4)
+            xf = xf * (10.0 ** (np.arange(M) % 9 - 4))[:, None]
+        x = synth.f32_to_bf16_bits(xf.astype(np.float32))
+    lg = synth.logits(13, M, E)
+    ref = oracle_moe.forward(x, lg, k, expert_getter(w), I, shared=shared_of(w))
+    out = layer.forward(dev_bf16(x), dev(lg)).float().cpu().numpy()
+    check_routing(layer, M, ref, E)
+    assert np.all(np.isfinite(out))
+    err, tok_err = rel_err(out, ref["out"]), _per_token_rel_err(out, ref["out"])
+    say(f"range {kind} case {case}: max|oracle| {np.max(np.abs(ref['out'])):.3e}, rel err {err:.3e}, "
+        f"worst per-token rel err {tok_err:.3e}")
+    assert err <= REL_TOL and tok_err <= REL_TOL
 
 
 def test_side_stream():
