@@ -143,6 +143,23 @@ int qmoe_workspace_init(qmoe_layer* layer, void* workspace, size_t ws_bytes, voi
 int qmoe_forward(qmoe_layer* layer, const void* x, const float* logits, int64_t M,
                  void* out, void* workspace, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+   capture, serving loops or harnesses that forbid allocation): the whole
+   layer exactly as qmoe_forward (same kernels, same results), with its
+   scratch in a device array the library holds for each GPU
+   (QMOE_STATIC_SCRATCH_BYTES, held until the process ends) instead of a
+   caller workspace.  Allocates nothing.  The caller still passes x, logits
+   and out.  A call whose workspace (qmoe_workspace_size) would exceed the
+   array returns QMOE_ERR_WORKSPACE without enqueueing anything (the
+   384-expert, H=7168, I=2048, top-8 layer fits up to about 190 tokens).
+   Every call on one GPU, from any layer, uses that GPU's one array: calls
+   that overlap on a GPU (different streams or threads) race, and the caller
+   must serialise them.  Routing and intermediates of such a call are not
+   readable through qmoe_read_routing / qmoe_read_intermediate. */
+#define QMOE_STATIC_SCRATCH_BYTES (32u << 20)
+int qmoe_forward_static(qmoe_layer* layer, const void* x, const float* logits, int64_t M, void* out,
+                        void* stream);
+
 /* The same four steps one at a time, on one workspace and in this order
    (each reads what the previous one left in the workspace).  They let a
    caller time or check each step alone.

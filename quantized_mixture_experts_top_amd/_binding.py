@@ -59,6 +59,7 @@ SIGNATURES = {
     "qmoe_workspace_size": (ctypes.c_int, [_VP, _I64, ctypes.POINTER(_SZ)]),
     "qmoe_workspace_init": (ctypes.c_int, [_VP, _VP, _SZ, _VP]),
     "qmoe_forward": (ctypes.c_int, [_VP, _VP, _VP, _I64, _VP, _VP, _SZ, _VP]),
+    "qmoe_forward_static": (ctypes.c_int, [_VP, _VP, _VP, _I64, _VP, _VP]),
     "qmoe_route": (ctypes.c_int, [_VP, _VP, _VP, _I64, _VP, _SZ, _VP]),
     "qmoe_gate_up": (ctypes.c_int, [_VP, _I64, _VP, _SZ, _VP]),
     "qmoe_down": (ctypes.c_int, [_VP, _I64, _VP, _SZ, _VP]),

@@ -23,6 +23,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstdio>
+#include <mutex>
 #include <cstdlib>
 #include <cstring>
 #include <string>
@@ -1332,10 +1333,39 @@ int64_t max_items_for(int64_t T, int64_t M, int64_t S, int64_t E, int64_t bmc) {
 
 }  // namespace
 
+// Scratch of qmoe_forward_static (callers that cannot allocate device
+// memory): one file-scope device array per GPU, used in place of a caller
+// workspace.  In host code `scratch` names a host-side stand-in; its device
+// address on each GPU comes from hipGetSymbolAddress, taken once per device
+// when the first layer on that device is created, and only that address is
+// ever passed to kernels.
+namespace {
+constexpr size_t kScratchBytes = (size_t)QMOE_STATIC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on device dev (the current device).
+hipError_t scratch_address(int dev, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
 struct qmoe_layer {
   qmoe_layer_desc d;
   int device = 0;
   bool shared = false;
+  void* scratch = nullptr;  // device address of this device's scratch array
   std::atomic<uint64_t> forward_calls{0}, route_calls{0}, gemm_launches{0}, launches{0}, inits{0},
       ws_last{0}, ws_peak{0}, prefill_tiles{0}, gemv_tiles{0}, gemv_nt{0};
 };
@@ -1633,10 +1663,15 @@ int qmoe_layer_create(const qmoe_layer_desc* d, qmoe_layer** out) {
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(QMOE_ERR_DEVICE, "hipGetDeviceProperties failed");
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(QMOE_ERR_UNSUPPORTED, std::string("device arch ") + prop.gcnArchName + " is not gfx950");
+  void* sp = nullptr;
+  const hipError_t se = scratch_address(dev, &sp);
+  if (se != hipSuccess)
+    return fail(QMOE_ERR_DEVICE, std::string("hipGetSymbolAddress of the static scratch failed: ") + hipGetErrorString(se));
   qmoe_layer* L = new qmoe_layer;
   L->d = *d;
   L->device = dev;
   L->shared = nsh == 4;
+  L->scratch = sp;
   *out = L;
   return QMOE_OK;
 }
@@ -1701,6 +1736,16 @@ int qmoe_forward(qmoe_layer* L, const void* x, const float* logits, int64_t M, v
   if ((rc = do_combine(L, M, out, ws, lay, st)) != QMOE_OK) return rc;
   L->forward_calls++;
   return QMOE_OK;
+}
+
+int qmoe_forward_static(qmoe_layer* L, const void* x, const float* logits, int64_t M, void* out, void* stream) {
+  if (!L) return fail(QMOE_ERR_ARG, "layer is NULL");
+  if (M < 0 || M > L->d.max_rows) return fail(QMOE_ERR_ARG, "M outside [0, max_rows]");
+  const size_t need = make_layout(L, M).total;
+  if (need > kScratchBytes)
+    return fail(QMOE_ERR_WORKSPACE, "M=" + std::to_string(M) + " needs " + std::to_string(need) +
+                                        " bytes of scratch, more than the static " + std::to_string(kScratchBytes));
+  return qmoe_forward(L, x, logits, M, out, L->scratch, kScratchBytes, stream);
 }
 
 int qmoe_read_routing(qmoe_layer* L, int64_t M, const void* ws, size_t ws_bytes, int32_t* ids, float* w,
