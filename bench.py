@@ -359,7 +359,8 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--only", default=None,
-                    help="time one configuration, as workload:M (e.g. plateau:4096); default: the whole sweep")
+                    help="time these configurations only, as workload:M[,workload:M...] (e.g. plateau:4096); "
+                         "the last one is the headline; default: the whole sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="also time the forward captured into one HIP graph per step and replayed back to back")
@@ -390,10 +391,12 @@ def main():
     from quantized_mixture_experts_top_amd import Layer
 
     if args.only:
-        wname, m = args.only.split(":")
-        configs = [(wname, int(m.replace("M=", "")))]
-        if wname not in synth.WORKLOADS:
-            raise SystemExit(f"unknown workload {wname}")
+        configs = []
+        for item in args.only.split(","):
+            wname, m = item.split(":")
+            if wname not in synth.WORKLOADS:
+                raise SystemExit(f"unknown workload {wname}")
+            configs.append((wname, int(m.replace("M=", ""))))
     else:
         configs = list(SWEEP)
     headline = configs[-1] if args.only else HEADLINE

@@ -128,15 +128,14 @@ void qmoe_layer_destroy(qmoe_layer* layer);
 /* Bytes of workspace a call with M tokens needs (0 <= M <= max_rows). */
 int qmoe_workspace_size(const qmoe_layer* layer, int64_t M, size_t* bytes);
 
-/* Enqueue a clear of a workspace's control words.  Optional: the calls do
-   not depend on what a workspace held before (a call that routes more than
-   64 tokens clears the routing ticket, and for up to 1024 tokens the
-   per-chunk token masks, itself: one extra small launch). */
+/* Enqueue a clear of a workspace's control words.  Optional: no call
+   depends on what a workspace held before. */
 int qmoe_workspace_init(qmoe_layer* layer, void* workspace, size_t ws_bytes, void* stream);
 
 /* The whole layer: route, gate+up, down, combine: four kernel launches,
-   five for calls of more than 64 tokens (a small kernel first clears the
-   routing ticket the routing blocks meet at).
+   five for calls of more than 64 tokens (their routing takes two: the top-k
+   of every token, then one block per 64-token chunk for the counts, the
+   scan, the sorted positions and the work list).
    x: bf16 [M,H] (any finite values; see the ranges above); logits: fp32
    [M,E], finite; out: bf16 [M,H] (device pointers, 16-byte aligned).
    M == 0 is a no-op.  Graph-capturable for a fixed M (no memset nodes). */

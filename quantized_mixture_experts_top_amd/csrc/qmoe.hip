@@ -1,10 +1,12 @@
 // Fused int4 group-32 Mixture-of-Experts layer for AMD Instinct MI355X
 // (gfx950): HIP kernels and the host side of the C ABI declared in qmoe.h.
 //
-// Steps of one call, one kernel each, all on the caller's stream:
-//   route_kernel    top-k routing, expert counts, their exclusive scan, the
-//                   stable sort of routed slots by expert, the flat list of
-//                   (expert, row tile) work items, x -> fp16 operand format
+// Steps of one call, all on the caller's stream:
+//   route_single_kernel (calls of at most 64 tokens), or route_topk_kernel
+//                   then route_finish_kernel: top-k routing, expert counts,
+//                   their exclusive scan, the stable sort of routed slots by
+//                   expert, the flat list of (expert, row tile) work items,
+//                   x -> fp16 operand format
 //   gemm_kernel<..., true>   stacked gate+up product with h = SiLU(g)*u
 //   gemm_kernel<..., false>  down product times the routing weight
 //                   (128-row MFMA tiles; calls averaging at most 1.75 routed
@@ -40,7 +42,7 @@ namespace {
 
 constexpr int kThreads = 256;   // every kernel: 4 waves of 64
 constexpr int kChunk = 64;      // tokens per routing chunk = bits of one mask word
-constexpr int kCtrlWords = 64;  // [0] route ticket, [1] number of work items
+constexpr int kCtrlWords = 64;  // [1] number of work items
 constexpr int kKStep = 128;     // inputs per K-step of a wave (4 lane groups x 32)
 
 // Shape of the 128-row MFMA tiles: MB row blocks of 16 per work item, NBW
@@ -67,15 +69,12 @@ struct RouteArgs {
   const float* logits;
   const uint4* x;  // bf16 [M, H] as 16-byte runs
   int M, E, H, k, S, C, bmc, max_items;
-  int subs;  // routing blocks per chunk (1, or kSubs for 2..kMaxSplitChunks chunks)
-  int nrb;   // routing blocks: C * subs
+  int nrb;  // blocks before the x-conversion blocks
   int* ctrl;
   int* ids;
   float* wts;
   int* counts;
   int* offsets;
-  unsigned long long* cmask;  // [C, E] token bitmask per chunk and expert
-  int* pbase;                 // [C, E] first sorted position of a chunk's tokens
   int* perm;
   int* inv_perm;
   int4* items;
@@ -83,23 +82,21 @@ struct RouteArgs {
   int* xexp;   // [M] per-token exponent
 };
 
-constexpr int kRouteThreads = 1024;  // routing blocks: 16 waves
+constexpr int kRouteThreads = 1024;  // routing blocks: up to 16 waves
 constexpr int kRouteWaves = kRouteThreads / 64;  // also token rows per conversion block
-constexpr int kSubs = 4;                   // routing blocks per chunk for calls of 2..kMaxSplitChunks chunks
-constexpr int kMaxSplitChunks = 16;         // beyond, one block per chunk: the per-block fences dominate
 
 // Counts, offsets and the flat work list from the per-expert row counts in
-// s_cnt[0..E) (the caller's threads wrote them before calling), all in LDS:
-// used when the whole call is one chunk (M <= 64) and by the multi-chunk
-// path's last block.  One wave does both exclusive scans (row offsets and
-// work-item offsets) over the E+1 entries at once: lane l sums its run of
-// ceil((E+1)/64) consecutive experts, a 6-step shuffle scan combines the
-// 64 lane totals, and each lane walks its run again to write offsets and
-// items.  This replaces a serial loop over the expert counts, and needs no
-// block barrier between the two scans.  The shared expert (entry E, a row
-// per token) gets the first items: its tiles are the longest of a call and
-// should not be the last to start.
-__device__ void route_items(const RouteArgs& a, int* s_cnt, int* s_off) {
+// s_cnt[0..E) (the caller's threads wrote them before calling), all in LDS.
+// One wave does both exclusive scans (row offsets and work-item offsets)
+// over the E+1 entries at once: lane l sums its run of ceil((E+1)/64)
+// consecutive experts, a 6-step shuffle scan combines the 64 lane totals,
+// and each lane walks its run again to write offsets and, when `write` is
+// set, the counts, offsets and items to the workspace.  This replaces a
+// serial loop over the expert counts, and needs no block barrier between
+// the two scans.  The shared expert (entry E, a row per token) gets the
+// first items: its tiles are the longest of a call and should not be the
+// last to start.
+__device__ void route_items(const RouteArgs& a, int* s_cnt, int* s_off, bool write) {
   const int tid = threadIdx.x, E = a.E, n = E + 1, bmc = a.bmc;
   if (tid == 0) s_cnt[E] = a.S;  // the shared expert takes every token
   __syncthreads();
@@ -130,33 +127,137 @@ __device__ void route_items(const RouteArgs& a, int* s_cnt, int* s_off) {
       if (e >= n) break;
       const int c = s_cnt[e], ni = (c + bmc - 1) / bmc;
       s_off[e] = c_run;
-      a.counts[e] = c;
-      a.offsets[e] = c_run;
-      const int base = e == E ? 0 : i_run + nsh;
-      for (int i = 0; i < ni; ++i) {
-        const int r0 = i * bmc;
-        if (base + i < a.max_items) a.items[base + i] = make_int4(e, r0, min(bmc, c - r0), c_run + r0);
+      if (write) {
+        a.counts[e] = c;
+        a.offsets[e] = c_run;
+        const int base = e == E ? 0 : i_run + nsh;
+        for (int i = 0; i < ni; ++i) {
+          const int r0 = i * bmc;
+          if (base + i < a.max_items) a.items[base + i] = make_int4(e, r0, min(bmc, c - r0), c_run + r0);
+        }
       }
       c_run += c;
       i_run += ni;
     }
     if (lane == 63) {
       s_off[n] = c_run;
-      a.offsets[n] = c_run;
-      a.ctrl[1] = min(i_run, a.max_items);
+      if (write) {
+        a.offsets[n] = c_run;
+        a.ctrl[1] = min(i_run, a.max_items);
+      }
     }
   }
   __syncthreads();
 }
 
-__device__ void route_finish_single(const RouteArgs& a, const uint32_t (*cm)[2], const int* s_ids, int* s_cnt,
-                                    int* s_off) {
-  const int tid = threadIdx.x, E = a.E, k = a.k;
-  for (int e = tid; e < E; e += kRouteThreads) s_cnt[e] = __popc(cm[e][0]) + __popc(cm[e][1]);
-  route_items(a, s_cnt, s_off);
+// The top_k experts of token t (one wave): order-preserving keys of the
+// logits; each of k rounds takes the largest key and, among experts holding
+// it, the lowest index.  Lane j < k returns the j-th selection and its
+// renormalised weight.  EPL = logits per lane (E <= 64 * EPL).
+template <int EPL>
+__device__ __forceinline__ void wave_topk(const RouteArgs& a, int t, int lane, int& my_e, float& my_w) {
+  const int E = a.E, k = a.k;
+  const float* row = a.logits + (size_t)t * E;
+  // (loads clamped into the row rather than predicated, so they all issue
+  // before the first wait; absent and taken experts have key 0, below every
+  // finite logit's)
+  float lv[EPL];
+#pragma unroll
+  for (int s = 0; s < EPL; ++s) lv[s] = row[min(s * 64 + lane, E - 1)];
+  uint32_t key[EPL];
+#pragma unroll
+  for (int s = 0; s < EPL; ++s) key[s] = (s * 64 + lane < E) ? ordered_key(lv[s]) : 0u;
+  my_e = 0;
+  float my_l = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    uint32_t best = 0;
+#pragma unroll
+    for (int s = 0; s < EPL; ++s) best = key[s] > best ? key[s] : best;
+    best = wave_max_u32(best);
+    int e_sel = -1;
+#pragma unroll
+    for (int s = 0; s < EPL; ++s) {
+      const uint64_t m = __ballot(key[s] == best);
+      if (e_sel < 0 && m != 0) e_sel = s * 64 + __ffsll((long long)m) - 1;
+    }
+#pragma unroll
+    for (int s = 0; s < EPL; ++s)
+      if (s * 64 + lane == e_sel) key[s] = 0;
+    if (lane == j) {
+      my_e = e_sel;
+      my_l = from_ordered_key(best);
+    }
+  }
+  // renormalised softmax over the selected logits: the full-softmax
+  // denominator cancels, so w_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0)
+  const float lj = (lane < k) ? my_l : 0.0f;
+  const float l0 = __shfl(lj, 0, 64);
+  const float ex = (lane < k) ? expf(lj - l0) : 0.0f;
+  float sum = ex;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
+  my_w = ex / sum;
+}
+
+// x -> fp16 operand format, one wave per token row: the row's largest |x|
+// sets its exponent e, and the row is stored times 2^-e (exact), so any
+// finite bf16 row fits fp16.
+__device__ __forceinline__ void convert_x_row(const RouteArgs& a, int t, int lane) {
+  const int runs = a.H / 8;
+  const uint4* __restrict__ row = a.x + (size_t)t * runs;
+  uint32_t amax = 0;
+  int v = lane;
+  for (; v + 3 * 64 < runs; v += 4 * 64) {  // four loads in flight per lane
+    uint4 r[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) r[u] = row[v + u * 64];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) amax = max(amax, absmax_bf16x8(r[u]));
+  }
+  for (; v < runs; v += 64) amax = max(amax, absmax_bf16x8(row[v]));
+  const int e = row_exponent(wave_max_u32(amax));
+  const float sc = pow2f(-e);
+  uint4* __restrict__ dst = a.xa + (size_t)t * runs;
+  for (v = lane; v < runs; v += 64) dst[v] = bf16x8_to_aformat(row[v], sc);  // the row again, from cache
+  if (lane == 0) a.xexp[t] = e;
+}
+
+// A call of at most 64 tokens is routed by one block of one wave per token
+// (blockDim.x = 64 * min(M, 16)), which finishes in LDS: per-expert 64-bit
+// masks of the tokens that chose it give each routed slot's rank inside its
+// expert (popcount of the lower bits).  The blocks after it convert x.
+template <int EPL>
+__global__ __launch_bounds__(kRouteThreads) void route_single_kernel(RouteArgs a) {
+  __shared__ uint32_t cm[QMOE_MAX_EXPERTS][2];
+  __shared__ int s_cnt[QMOE_MAX_EXPERTS + 2];
+  __shared__ int s_off[QMOE_MAX_EXPERTS + 2];
+  __shared__ int s_ids[kChunk * QMOE_MAX_TOPK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nthr = blockDim.x, nw = nthr / 64;
+  const int E = a.E, k = a.k;
+  if (blockIdx.x >= 1) {
+    const int t = ((int)blockIdx.x - 1) * nw + wave;
+    if (t < a.M) convert_x_row(a, t, lane);
+    return;
+  }
+  for (int e = tid; e < E; e += nthr) cm[e][0] = cm[e][1] = 0u;
+  __syncthreads();
+  for (int t = wave; t < a.M; t += nw) {
+    int my_e;
+    float my_w;
+    wave_topk<EPL>(a, t, lane, my_e, my_w);
+    if (lane < k) {
+      a.ids[(size_t)t * k + lane] = my_e;
+      a.wts[(size_t)t * k + lane] = my_w;
+      s_ids[t * k + lane] = my_e;
+      atomicOr(&cm[my_e][t >> 5], 1u << (t & 31));
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += nthr) s_cnt[e] = __popc(cm[e][0]) + __popc(cm[e][1]);
+  route_items(a, s_cnt, s_off, true);
   // slot (t, j): its expert's offset plus the number of lower tokens routed
   // to that expert (each token selects an expert at most once)
-  for (int f = tid; f < a.M * k; f += kRouteThreads) {
+  for (int f = tid; f < a.M * k; f += nthr) {
     const int t = f / k, e = s_ids[f];
     const unsigned long long m = (unsigned long long)cm[e][0] | ((unsigned long long)cm[e][1] << 32);
     const int pos = s_off[e] + __popcll(m & ((1ull << t) - 1ull));
@@ -164,201 +265,84 @@ __device__ void route_finish_single(const RouteArgs& a, const uint32_t (*cm)[2],
     a.inv_perm[f] = pos;
   }
   const int T = a.M * k;
-  for (int t = tid; t < a.S; t += kRouteThreads) a.perm[T + t] = T + t;
+  for (int t = tid; t < a.S; t += nthr) a.perm[T + t] = T + t;
 }
 
-// A call of at most 64 tokens (one chunk) is routed by one block, which
-// finishes in LDS.  With several chunks, each chunk of 64 tokens gets one
-// block, or, for up to kMaxSplitChunks chunks, kSubs blocks of 16 tokens
-// (one per wave: the top-k is compute bound inside a CU) that OR their
-// tokens' bits into the chunk's masks in global memory; the last block to
-// finish (atomic ticket, no waiting) turns the masks into counts, offsets,
-// positions and work items.  The blocks after the routing blocks convert x
-// to the fp16 operand format in slices (they take no part in the ticket).
-// EPL = logits per lane (E <= 64 * EPL).
+// Calls of more than 64 tokens, first of two kernels: one wave per token
+// selects its top_k experts and weights (blocks of 16 tokens, spread over
+// the GPU); the blocks after the routing blocks convert x.
 template <int EPL>
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
+__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(RouteArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if ((int)blockIdx.x >= a.nrb) {
+    const int t = ((int)blockIdx.x - a.nrb) * kRouteWaves + wave;
+    if (t < a.M) convert_x_row(a, t, lane);
+    return;
+  }
+  const int t = (int)blockIdx.x * kRouteWaves + wave;
+  if (t >= a.M) return;
+  int my_e;
+  float my_w;
+  wave_topk<EPL>(a, t, lane, my_e, my_w);
+  if (lane < a.k) {
+    a.ids[(size_t)t * a.k + lane] = my_e;
+    a.wts[(size_t)t * a.k + lane] = my_w;
+  }
+}
+
+// Second kernel: one block per chunk of 64 tokens.  Every block histograms
+// all routed slots (the expert counts) and, separately, those of the tokens
+// before its chunk; the counts' exclusive scan (route_items) plus the
+// earlier tokens' count gives the first sorted position of the chunk's
+// tokens in each expert, and the chunk's own per-expert token masks give
+// each slot's rank after them.  So no block waits for another, and no
+// global atomics or cleared memory are needed.  Block 0 also writes the
+// counts, offsets and work items.
+__global__ __launch_bounds__(kRouteThreads) void route_finish_kernel(RouteArgs a) {
   __shared__ uint32_t cm[QMOE_MAX_EXPERTS][2];
   __shared__ int s_cnt[QMOE_MAX_EXPERTS + 2];
   __shared__ int s_off[QMOE_MAX_EXPERTS + 2];
-  __shared__ int s_last;
-  __shared__ int s_ids[kChunk * QMOE_MAX_TOPK];  // the chunk's selected experts
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int E = a.E, k = a.k;
-  const int c = blockIdx.x / a.subs;                // chunk
-  const int rows = min(kChunk, a.M - c * kChunk);    // the chunk's tokens
-  // this block's tokens of the chunk: [t_lo, t_hi)
-  const int t_lo = (blockIdx.x % a.subs) * (kChunk / a.subs);
-  const int t_hi = min(rows, t_lo + kChunk / a.subs);
-
-  // blocks past the routing blocks convert x to the fp16 operand format, one
-  // wave per token row: the row's largest |x| sets its exponent e, and the
-  // row is stored times 2^-e (exact), so any finite bf16 row fits fp16
-  if ((int)blockIdx.x >= a.nrb) {
-    const int t = ((int)blockIdx.x - a.nrb) * kRouteWaves + wave;
-    if (t >= a.M) return;
-    const int runs = a.H / 8;
-    const uint4* __restrict__ row = a.x + (size_t)t * runs;
-    uint32_t amax = 0;
-    int v = lane;
-    for (; v + 3 * 64 < runs; v += 4 * 64) {  // four loads in flight per lane
-      uint4 r[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) r[u] = row[v + u * 64];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) amax = max(amax, absmax_bf16x8(r[u]));
-    }
-    for (; v < runs; v += 64) amax = max(amax, absmax_bf16x8(row[v]));
-    const int e = row_exponent(wave_max_u32(amax));
-    const float sc = pow2f(-e);
-    uint4* __restrict__ dst = a.xa + (size_t)t * runs;
-    for (v = lane; v < runs; v += 64) dst[v] = bf16x8_to_aformat(row[v], sc);  // the row again, from cache
-    if (lane == 0) a.xexp[t] = e;
-    return;
-  }
-
-  for (int e = tid; e < E; e += kRouteThreads) cm[e][0] = cm[e][1] = 0u;
-  __syncthreads();
-
-  // ---- phase 1a: top-k of each token, one wave per token
-  for (int tl = t_lo + wave; tl < t_hi; tl += kRouteWaves) {
-    const int t = c * kChunk + tl;
-    const float* row = a.logits + (size_t)t * E;
-    // key = order-preserving bits of the logit (every finite logit maps
-    // above 0; absent and taken experts are 0).  Each round takes the
-    // largest key and, among experts holding it, the lowest index: the
-    // first slot s with a lane holding it, lowest lane first.
-    // (loads clamped into the row rather than predicated, so they all
-    // issue before the first wait)
-    float lv[EPL];
-#pragma unroll
-    for (int s = 0; s < EPL; ++s) lv[s] = row[min(s * 64 + lane, E - 1)];
-    uint32_t key[EPL];
-#pragma unroll
-    for (int s = 0; s < EPL; ++s) key[s] = (s * 64 + lane < E) ? ordered_key(lv[s]) : 0u;
-    int my_e = 0;
-    float my_l = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      uint32_t best = 0;
-#pragma unroll
-      for (int s = 0; s < EPL; ++s) best = key[s] > best ? key[s] : best;
-      best = wave_max_u32(best);
-      int e_sel = -1;
-#pragma unroll
-      for (int s = 0; s < EPL; ++s) {
-        const uint64_t m = __ballot(key[s] == best);
-        if (e_sel < 0 && m != 0) e_sel = s * 64 + __ffsll((long long)m) - 1;
-      }
-#pragma unroll
-      for (int s = 0; s < EPL; ++s)
-        if (s * 64 + lane == e_sel) key[s] = 0;
-      if (lane == j) {
-        my_e = e_sel;
-        my_l = from_ordered_key(best);
-      }
-    }
-    // renormalised softmax over the selected logits: the full-softmax
-    // denominator cancels, so w_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0)
-    const float lj = (lane < k) ? my_l : 0.0f;
-    const float l0 = __shfl(lj, 0, 64);
-    const float ex = (lane < k) ? expf(lj - l0) : 0.0f;
-    float sum = ex;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
-    if (lane < k) {
-      a.ids[(size_t)t * k + lane] = my_e;
-      s_ids[tl * k + lane] = my_e;
-      a.wts[(size_t)t * k + lane] = ex / sum;
-      atomicOr(&cm[my_e][tl >> 5], 1u << (tl & 31));
-    }
-  }
-
-  __syncthreads();
-  if (a.C == 1) {
-    route_finish_single(a, cm, s_ids, s_cnt, s_off);
-    return;
-  }
-  // this block's token bits into the chunk's masks: stored by the chunk's
-  // only block, or OR-ed into masks zeroed before the call
+  __shared__ int s_before[QMOE_MAX_EXPERTS];
+  const int tid = threadIdx.x, E = a.E, k = a.k, c = blockIdx.x;
+  const int t0 = c * kChunk, rows = min(kChunk, a.M - t0);
   for (int e = tid; e < E; e += kRouteThreads) {
+    s_cnt[e] = 0;
+    s_before[e] = 0;
+    cm[e][0] = cm[e][1] = 0u;
+  }
+  __syncthreads();
+  const int T = a.M * k, before = t0 * k;
+  const int* __restrict__ ids = a.ids;
+  for (int f0 = 0; f0 < T; f0 += 4 * kRouteThreads) {  // four loads in flight per thread
+    int e[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int f = f0 + u * kRouteThreads + tid;
+      e[u] = f < T ? ids[f] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int f = f0 + u * kRouteThreads + tid;
+      if (e[u] < 0 || e[u] >= E) continue;  // ids come from the workspace: skip any out of range
+      atomicAdd(&s_cnt[e[u]], 1);
+      if (f < before) atomicAdd(&s_before[e[u]], 1);
+      else if (f < before + rows * k) {
+        const int tl = f / k - t0;
+        atomicOr(&cm[e[u]][tl >> 5], 1u << (tl & 31));
+      }
+    }
+  }
+  __syncthreads();
+  route_items(a, s_cnt, s_off, c == 0);
+  for (int f = before + tid; f < before + rows * k; f += kRouteThreads) {
+    const int tl = f / k - t0, e = ids[f];
+    if (e < 0 || e >= E) continue;
     const unsigned long long m = (unsigned long long)cm[e][0] | ((unsigned long long)cm[e][1] << 32);
-    if (a.subs == 1) a.cmask[(size_t)c * E + e] = m;
-    else if (m != 0ull) atomicOr(&a.cmask[(size_t)c * E + e], m);
+    const int pos = s_off[e] + s_before[e] + __popcll(m & ((1ull << tl) - 1ull));
+    a.perm[pos] = f;
+    a.inv_perm[f] = pos;
   }
-  // the last routing block to arrive (device-scope ticket) finishes
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(a.ctrl, 1) == a.nrb - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
-  // ---- phase 2 (last block only)
-  // per expert (one thread each), walk the chunks in order: the count, and
-  // each chunk's first rank within the expert; loads are batched by 8
-  {
-    const unsigned long long* __restrict__ cmask = a.cmask;
-    int* __restrict__ pbase = a.pbase;
-    for (int e = tid; e < E; e += kRouteThreads) {
-      int run = 0, cc = 0;
-      for (; cc + 8 <= a.C; cc += 8) {
-        int v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = __popcll(cmask[(size_t)(cc + u) * E + e]);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          pbase[(size_t)(cc + u) * E + e] = run;
-          run += v[u];
-        }
-      }
-      for (; cc < a.C; ++cc) {
-        const int v = __popcll(cmask[(size_t)cc * E + e]);
-        pbase[(size_t)cc * E + e] = run;
-        run += v;
-      }
-      s_cnt[e] = run;
-    }
-  }
-  route_items(a, s_cnt, s_off);
-  __threadfence();
-  __syncthreads();
-  // sorted position of every routed slot: expert offset + rank of the
-  // token's chunk + rank inside the chunk (popcount of the lower mask bits)
-  {
-    const int* __restrict__ ids = a.ids;
-    const unsigned long long* __restrict__ cmask = a.cmask;
-    const int* __restrict__ pbase = a.pbase;
-    int* __restrict__ perm = a.perm;
-    int* __restrict__ inv_perm = a.inv_perm;
-    for (int t = tid; t < a.M; t += kRouteThreads) {
-      const int cc = t / kChunk, tl = t % kChunk;
-      const unsigned long long below = (1ull << tl) - 1ull;
-      for (int j0 = 0; j0 < k; j0 += 8) {
-        const int nj = min(8, k - j0);
-        int e[8], pb[8];
-        unsigned long long mk[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) e[u] = u < nj ? ids[t * k + j0 + u] : 0;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const size_t ce = (size_t)cc * E + e[u];
-          pb[u] = u < nj ? pbase[ce] : 0;
-          mk[u] = u < nj ? cmask[ce] : 0ull;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (u < nj) {
-            const int f = t * k + j0 + u;
-            const int pos = s_off[e[u]] + pb[u] + __popcll(mk[u] & below);
-            perm[pos] = f;
-            inv_perm[f] = pos;
-          }
-        }
-      }
-    }
-  }
-  const int T = a.M * k;
-  for (int t = tid; t < a.S; t += kRouteThreads) a.perm[T + t] = T + t;
+  for (int t = t0 + tid; t < t0 + rows && t < a.S; t += kRouteThreads) a.perm[T + t] = T + t;
 }
 
 // ------------------------------------------------------------------ GEMMs
@@ -588,7 +572,10 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   // so the round trips of the lookups (sorted slot, routing weight) overlap
   // theirs instead of preceding them.  (Gate+up issues them after: its
   // 128 accumulators leave no room to hold them across the lookups.)
-  if (!GATEUP && S_end_full > S_begin) {
+  // (down tiles of one 16-column block per wave only: wider waves have no
+  // registers to hold these fragments across the lookups)
+  constexpr bool kEarlyB = !GATEUP && NBW == 1;
+  if (kEarlyB && S_end_full > S_begin) {
     load_sc(S_begin, sc_nxt, true);
     load_b(S_begin, 0, fb0, true);
     load_b(S_begin, 1, fb1, true);
@@ -725,7 +712,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
     constexpr int NMBC = decltype(nmbc_tag)::value;
     const int n = S_end_full - S_begin;
     if (n > 0) {
-      if (GATEUP) {
+      if (!kEarlyB) {
         load_sc(S_begin, sc_nxt, true);
         load_b(S_begin, 0, fb0, true);
         QMOE_LOAD_A_TILE(S_begin, 0, true, 0);
@@ -851,7 +838,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
     }
   };
   if (nmb <= 2) {
-    if constexpr (!GATEUP && MB >= 8) kloop_ss();
+    if constexpr (kEarlyB && MB >= 8) kloop_ss();
     else kloop(std::integral_constant<int, (MB < 2 ? MB : 2)>{});
   } else if (nmb <= 4) kloop(std::integral_constant<int, (MB < 4 ? MB : 4)>{});
   else if (GATEUP && MB == 8 && nmb == 5) kloop(std::integral_constant<int, 5>{});
@@ -1301,14 +1288,6 @@ __global__ void init_ctrl_kernel(int* ctrl) {
   if (threadIdx.x < kCtrlWords) ctrl[threadIdx.x] = 0;
 }
 
-// Clears the routing ticket and the n per-chunk token masks of a call with
-// several chunks (the routing blocks OR their tokens' bits into them).
-__global__ __launch_bounds__(kThreads) void init_route_kernel(int* ctrl, unsigned long long* cmask, long long n) {
-  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
-  if (blockIdx.x == 0 && threadIdx.x < kCtrlWords) ctrl[threadIdx.x] = 0;
-  if (i < n) cmask[i] = 0ull;
-}
-
 // ============================================================= host side
 
 thread_local std::string g_err;
@@ -1322,7 +1301,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
   int64_t T, S, R, C, max_items_all;
-  size_t ctrl, ids, wts, counts, offsets, cmask, pbase, perm, inv_perm, items, xexp, xa, h, y, total;
+  size_t ctrl, ids, wts, counts, offsets, perm, inv_perm, items, xexp, xa, h, y, total;
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -1391,8 +1370,6 @@ Layout make_layout(const qmoe_layer* L, int64_t M) {
   l.wts = take(l.T * 4);
   l.counts = take((E + 1) * 4);
   l.offsets = take((E + 2) * 4);
-  l.cmask = take(l.C * E * 8);
-  l.pbase = take(l.C * E * 4);
   l.perm = take(l.R * 4);
   l.inv_perm = take(l.T * 4);
   l.items = take(l.max_items_all * 16);
@@ -1486,37 +1463,41 @@ int do_route(qmoe_layer* L, const void* x, const float* logits, int64_t M, void*
   a.wts = at<float>(ws, lay.wts);
   a.counts = at<int>(ws, lay.counts);
   a.offsets = at<int>(ws, lay.offsets);
-  a.cmask = at<unsigned long long>(ws, lay.cmask);
-  a.pbase = at<int>(ws, lay.pbase);
   a.perm = at<int>(ws, lay.perm);
   a.inv_perm = at<int>(ws, lay.inv_perm);
   a.items = at<int4>(ws, lay.items);
   a.xa = at<uint4>(ws, lay.xa);
   a.xexp = at<int>(ws, lay.xexp);
-  a.subs = (lay.C > 1 && lay.C <= kMaxSplitChunks) ? kSubs : 1;
-  a.nrb = (int)lay.C * a.subs;
-  if (lay.C > 1) {
-    // several routing blocks meet at a ticket (and, when chunks are split,
-    // OR into the chunk masks): clear them first (the call then does not
-    // depend on what the workspace held before)
-    const long long n = a.subs > 1 ? lay.C * (long long)L->d.E : 0;
-    init_route_kernel<<<dim3((unsigned)std::max<long long>(1, ceil_div(n, kThreads))), kThreads, 0, st>>>(
-        a.ctrl, a.cmask, n);
-    const int rc = check_launch(L, "ticket and mask clear");
-    if (rc != QMOE_OK) return rc;
-  }
-  // routing blocks, then the blocks that convert x (one wave per token row)
-  const int64_t xblocks = ceil_div(M, (int64_t)kRouteWaves);
-  const dim3 grid((unsigned)(a.nrb + xblocks));
   const int epl = (L->d.E + 63) / 64;
-  if (epl <= 1) route_kernel<1><<<grid, kRouteThreads, 0, st>>>(a);
-  else if (epl <= 2) route_kernel<2><<<grid, kRouteThreads, 0, st>>>(a);
-  else if (epl <= 4) route_kernel<4><<<grid, kRouteThreads, 0, st>>>(a);
-  else if (epl <= 6) route_kernel<6><<<grid, kRouteThreads, 0, st>>>(a);  // 257-384 experts
-  else if (epl <= 8) route_kernel<8><<<grid, kRouteThreads, 0, st>>>(a);
-  else route_kernel<16><<<grid, kRouteThreads, 0, st>>>(a);
   L->route_calls++;
-  return check_launch(L, "route_kernel");
+  if (lay.C == 1) {
+    // one routing block of one wave per token, then x-conversion blocks
+    // of as many waves
+    const int nw = (int)std::min<int64_t>(M, kRouteWaves);
+    a.nrb = 1;
+    const dim3 grid((unsigned)(1 + ceil_div(M, nw))), block((unsigned)(64 * nw));
+    if (epl <= 1) route_single_kernel<1><<<grid, block, 0, st>>>(a);
+    else if (epl <= 2) route_single_kernel<2><<<grid, block, 0, st>>>(a);
+    else if (epl <= 4) route_single_kernel<4><<<grid, block, 0, st>>>(a);
+    else if (epl <= 6) route_single_kernel<6><<<grid, block, 0, st>>>(a);  // 257-384 experts
+    else if (epl <= 8) route_single_kernel<8><<<grid, block, 0, st>>>(a);
+    else route_single_kernel<16><<<grid, block, 0, st>>>(a);
+    return check_launch(L, "route_single_kernel");
+  }
+  // top-k blocks of 16 tokens, then as many x-conversion blocks; then one
+  // finishing block per 64-token chunk
+  a.nrb = (int)ceil_div(M, kRouteWaves);
+  const dim3 grid((unsigned)(2 * a.nrb));
+  if (epl <= 1) route_topk_kernel<1><<<grid, kRouteThreads, 0, st>>>(a);
+  else if (epl <= 2) route_topk_kernel<2><<<grid, kRouteThreads, 0, st>>>(a);
+  else if (epl <= 4) route_topk_kernel<4><<<grid, kRouteThreads, 0, st>>>(a);
+  else if (epl <= 6) route_topk_kernel<6><<<grid, kRouteThreads, 0, st>>>(a);
+  else if (epl <= 8) route_topk_kernel<8><<<grid, kRouteThreads, 0, st>>>(a);
+  else route_topk_kernel<16><<<grid, kRouteThreads, 0, st>>>(a);
+  int rc = check_launch(L, "route_topk_kernel");
+  if (rc != QMOE_OK) return rc;
+  route_finish_kernel<<<dim3((unsigned)lay.C), kRouteThreads, 0, st>>>(a);
+  return check_launch(L, "route_finish_kernel");
 }
 
 template <bool GATEUP>
