@@ -302,6 +302,8 @@ def time_config(layer, shape, wl, M, steps, warmup, graph=False):
         graph_res = {"us_per_call": gv0.elapsed_time(gv1) / steps * 1e3,
                      "matches_eager": bool(torch.equal(outs[n - 1].view(torch.int16), eager_last.view(torch.int16)))}
         del graphs, outs
+    receipt = layer.receipt()
+    receipt["items_built"] = layer.item_count(M)  # the last step's routing
     del xs, ls
     b13, b2 = bytes_per_expert(shape)
     f13, f2 = flops_per_row(shape)
@@ -333,6 +335,8 @@ def time_config(layer, shape, wl, M, steps, warmup, graph=False):
         "gate_up_flops_per_launch": rows * f13,
         "gate_up_us": float(st_ms[1] * 1e3),
         "bracketed_call_us_p10_p50_p90": [float(np.percentile(per_call_us, q)) for q in (10, 50, 90)],
+        "receipt": {k: receipt[k] for k in ("regime", "rows_per_item", "nt_codes", "launches", "max_items",
+                                             "items_built", "gate_up_blocks", "down_blocks", "workspace_bytes")},
     }
     if graph_res is not None:
         res["graph_us_per_call"] = graph_res["us_per_call"]

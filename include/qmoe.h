@@ -79,7 +79,7 @@
 extern "C" {
 #endif
 
-#define QMOE_VERSION 2
+#define QMOE_VERSION 3
 
 enum qmoe_status {
   QMOE_OK = 0,
@@ -220,6 +220,44 @@ typedef struct {
 
 int qmoe_get_stats(const qmoe_layer* layer, qmoe_stats* out);
 int qmoe_reset_stats(qmoe_layer* layer);
+
+/* Per-call engagement receipt: what the last completed forward call on the
+   handle (qmoe_forward or qmoe_forward_static) enqueued, recorded on the
+   host as it enqueued it (no device readback), so a caller can prove which
+   kernels ran and that nothing fell back.  The counterpart of the per-call
+   tier and engagement counters in "perf(exl3): accelerate fat-expert
+   prefill", sections "Summary" and "Engagement and fallback proof". */
+#define QMOE_REGIME_GEMV 1   /* dot-product GEMV on work items of <= 2 routed rows */
+#define QMOE_REGIME_TILES 2  /* 128-row MFMA tiles */
+typedef struct {
+  uint64_t seq;             /* 1-based number of the forward call on this handle */
+  int64_t M;
+  int32_t regime;           /* QMOE_REGIME_GEMV or QMOE_REGIME_TILES */
+  int32_t rows_per_item;    /* routed rows per work item: 2 or 128 */
+  int32_t nt_codes;         /* 1: the GEMV read weight codes non-temporal */
+  int32_t shared_expert;    /* 1: a shared expert was applied */
+  int32_t launches;         /* kernel launches the call enqueued */
+  int32_t route_kernels;    /* 1 (calls of <= 64 tokens) or 2 */
+  int64_t max_items;        /* work items the GEMM grids were sized for (an upper
+                               bound of the items routing builds) */
+  int64_t gate_up_blocks;   /* grid sizes of the launches */
+  int64_t down_blocks;
+  int64_t combine_blocks;
+  uint64_t workspace_bytes; /* workspace bytes the call used */
+  int32_t static_scratch;   /* 1: qmoe_forward_static (library scratch) */
+  int32_t reserved;
+} qmoe_receipt;
+
+/* Copy the receipt of the last completed forward call (QMOE_ERR_ARG if none
+   has completed). */
+int qmoe_last_receipt(const qmoe_layer* layer, qmoe_receipt* out);
+
+/* Enqueue a device-to-device copy of the number of work items the last
+   routing on this workspace built (int32, device memory): the items the GEMM
+   grids actually processed, sum over experts of ceil(count / rows_per_item)
+   plus the shared expert's. */
+int qmoe_read_item_count(qmoe_layer* layer, int64_t M, const void* workspace, size_t ws_bytes,
+                         int32_t* n_items, void* stream);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* qmoe_last_error(void);

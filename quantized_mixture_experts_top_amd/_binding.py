@@ -48,6 +48,20 @@ class Stats(ctypes.Structure):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}
 
 
+class Receipt(ctypes.Structure):
+    _fields_ = [("seq", ctypes.c_uint64), ("M", ctypes.c_int64), ("regime", ctypes.c_int32),
+                ("rows_per_item", ctypes.c_int32), ("nt_codes", ctypes.c_int32), ("shared_expert", ctypes.c_int32),
+                ("launches", ctypes.c_int32), ("route_kernels", ctypes.c_int32), ("max_items", ctypes.c_int64),
+                ("gate_up_blocks", ctypes.c_int64), ("down_blocks", ctypes.c_int64),
+                ("combine_blocks", ctypes.c_int64), ("workspace_bytes", ctypes.c_uint64),
+                ("static_scratch", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+    def as_dict(self) -> dict:
+        d = {n: int(getattr(self, n)) for n, _ in self._fields_ if n != "reserved"}
+        d["regime"] = {1: "gemv", 2: "tiles"}.get(d["regime"], d["regime"])
+        return d
+
+
 _VP, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 
 # name -> (restype, argtypes); mirrors include/qmoe.h
@@ -69,9 +83,11 @@ SIGNATURES = {
     "qmoe_dequant_debug": (ctypes.c_int, [_VP, _I32, _I32, _VP, _VP]),
     "qmoe_get_stats": (ctypes.c_int, [_VP, ctypes.POINTER(Stats)]),
     "qmoe_reset_stats": (ctypes.c_int, [_VP]),
+    "qmoe_last_receipt": (ctypes.c_int, [_VP, ctypes.POINTER(Receipt)]),
+    "qmoe_read_item_count": (ctypes.c_int, [_VP, _I64, _VP, _SZ, _VP, _VP]),
 }
 
-ABI_VERSION = 2  # QMOE_VERSION of include/qmoe.h
+ABI_VERSION = 3  # QMOE_VERSION of include/qmoe.h
 _lib = None
 
 

@@ -627,12 +627,12 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
     for (int b = 0; b < NBB; ++b) transpose_scales(sc_nxt[b][0], sc_nxt[b][1], sc_cur[b]);
   };
   // this wave's blocks of sub-step U of super-step S into buffer BUF, for
-  // the NMBC row blocks in use (NMBC is a multiple of WN/4); lanes whose
-  // group is past K (OK false) read zeros
+  // the NMBC row blocks in use (row block amb0 + MBS*t; a wave-uniform
+  // test); lanes whose group is past K (OK false) read zeros
 #define QMOE_LOAD_A_TILE_AT(S, U, OK, BUF, SLOT0)                                                \
   do {                                                                                           \
     _Pragma("unroll") for (int t = 0; t < NA; ++t) {                                             \
-      if (t < NMBC / MBS)                                                                        \
+      if (MBS == 1 ? t < NMBC : amb0 + MBS * t < NMBC)                                           \
         load_lds16(rA, &QMOE_LDS_A(BUF)[(((SLOT0) + amb0 + MBS * t) * 4 + aq) * kBlkHalves],      \
                    (OK) ? aoffs[t] : kOob, (S) * (kSuper * 2) + 256 * (U));                      \
     }                                                                                            \
@@ -704,8 +704,8 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
     __syncthreads();                                                                             \
   } while (0)
   // The row blocks that hold routed rows are computed without a branch per
-  // block: the loop is instantiated for 2, 4, 6 and 8 blocks (gate+up also
-  // 5 and 7: about 85 rows per expert at 4096 tokens) and the item's count
+  // block: the loop is instantiated for 2, 4, 5, 6, 7 and 8 blocks (about
+  // 85 rows per expert at 4096 tokens: 5-7 blocks) and the item's count
   // rounds up to the next of these (blocks past the item's rows multiply
   // zero rows, which are never stored).
   auto kloop = [&](auto nmbc_tag) __attribute__((always_inline)) {
@@ -841,9 +841,9 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
     if constexpr (kEarlyB && MB >= 8) kloop_ss();
     else kloop(std::integral_constant<int, (MB < 2 ? MB : 2)>{});
   } else if (nmb <= 4) kloop(std::integral_constant<int, (MB < 4 ? MB : 4)>{});
-  else if (GATEUP && MB == 8 && nmb == 5) kloop(std::integral_constant<int, 5>{});
+  else if (MB == 8 && nmb == 5) kloop(std::integral_constant<int, 5>{});
   else if (nmb <= 6) kloop(std::integral_constant<int, (MB < 6 ? MB : 6)>{});
-  else if (GATEUP && MB == 8 && nmb == 7) kloop(std::integral_constant<int, 7>{});
+  else if (MB == 8 && nmb == 7) kloop(std::integral_constant<int, 7>{});
   else kloop(std::integral_constant<int, MB>{});
 #undef QMOE_SUBSTEP
 #undef QMOE_SUBSTEP_PAIR
@@ -1291,6 +1291,8 @@ __global__ void init_ctrl_kernel(int* ctrl) {
 // ============================================================= host side
 
 thread_local std::string g_err;
+// receipt of the forward call being enqueued on this thread (null outside one)
+thread_local qmoe_receipt* t_rc = nullptr;
 
 int fail(int code, const std::string& msg) {
   g_err = msg;
@@ -1345,6 +1347,10 @@ struct qmoe_layer {
   int device = 0;
   bool shared = false;
   void* scratch = nullptr;  // device address of this device's scratch array
+  std::mutex receipt_mu;
+  qmoe_receipt last{};      // receipt of the last completed forward call
+  bool has_receipt = false;
+  std::atomic<uint64_t> receipt_seq{0};  // forward calls since creation (not reset by qmoe_reset_stats)
   std::atomic<uint64_t> forward_calls{0}, route_calls{0}, gemm_launches{0}, launches{0}, inits{0},
       ws_last{0}, ws_peak{0}, prefill_tiles{0}, gemv_tiles{0}, gemv_nt{0};
 };
@@ -1404,6 +1410,7 @@ T* at(void* ws, size_t off) {
 
 int check_launch(qmoe_layer* L, const char* what) {
   L->launches++;
+  if (t_rc) t_rc->launches++;
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(QMOE_ERR_LAUNCH, std::string(what) + ": " + hipGetErrorString(e));
   return QMOE_OK;
@@ -1552,6 +1559,10 @@ int launch_gemm(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream
   if (blocks > 0x7FFFFFFF) return fail(QMOE_ERR_UNSUPPORTED, "grid too large");
   gemm_kernel<MB, WN, NBW, GATEUP><<<dim3((unsigned)blocks), 64 * WN, 0, st>>>(g);
   L->gemm_launches++;
+  if (t_rc) {
+    t_rc->max_items = g.max_items;
+    (GATEUP ? t_rc->gate_up_blocks : t_rc->down_blocks) = blocks;
+  }
   return check_launch(L, GATEUP ? "gate_up gemm" : "down gemm");
 }
 
@@ -1576,6 +1587,11 @@ int launch_gemv(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream
   } else
     gemv_kernel<GATEUP, false><<<dim3((unsigned)blocks), kThreads, lds, st>>>(g);
   L->gemm_launches++;
+  if (t_rc) {
+    t_rc->max_items = g.max_items;
+    t_rc->nt_codes = nt ? 1 : 0;
+    (GATEUP ? t_rc->gate_up_blocks : t_rc->down_blocks) = blocks;
+  }
   return check_launch(L, GATEUP ? "gate_up gemv" : "down gemv");
 }
 
@@ -1597,6 +1613,7 @@ int do_combine(qmoe_layer* L, int64_t M, void* out, void* ws, const Layout& lay,
   if (!out) return fail(QMOE_ERR_ARG, "out is NULL");
   if (!aligned16(out)) return fail(QMOE_ERR_ARG, "out must be 16-byte aligned");
   const int64_t n = M * (L->d.H / 4);
+  if (t_rc) t_rc->combine_blocks = ceil_div(n, kThreads);
   combine_kernel<<<dim3((unsigned)ceil_div(n, kThreads)), kThreads, 0, st>>>(
       at<uint2>(ws, lay.y), static_cast<uint2*>(out), (int)M, L->d.H, L->d.top_k, (int)lay.T, (int)lay.S);
   return check_launch(L, "combine_kernel");
@@ -1704,18 +1721,59 @@ int qmoe_combine(qmoe_layer* L, int64_t M, void* out, void* ws, size_t ws_bytes,
   return do_combine(L, M, out, ws, lay, static_cast<hipStream_t>(stream));
 }
 
-int qmoe_forward(qmoe_layer* L, const void* x, const float* logits, int64_t M, void* out, void* ws,
-                 size_t ws_bytes, void* stream) {
+namespace {
+int forward_impl(qmoe_layer* L, const void* x, const float* logits, int64_t M, void* out, void* ws,
+                 size_t ws_bytes, hipStream_t st, bool from_scratch) {
   Layout lay;
   int rc = check_call(L, M, ws, ws_bytes, &lay);
   if (rc != QMOE_OK || M == 0) return rc;
   if (!out) return fail(QMOE_ERR_ARG, "out is NULL");
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  if ((rc = do_route(L, x, logits, M, ws, lay, st)) != QMOE_OK) return rc;
-  if ((rc = do_gate_up(L, M, ws, lay, st)) != QMOE_OK) return rc;
-  if ((rc = do_down(L, M, ws, lay, st)) != QMOE_OK) return rc;
-  if ((rc = do_combine(L, M, out, ws, lay, st)) != QMOE_OK) return rc;
+  qmoe_receipt r{};
+  r.M = M;
+  const Regime rg = regime_of(L, M);
+  r.regime = rg == kGemv ? QMOE_REGIME_GEMV : QMOE_REGIME_TILES;
+  r.rows_per_item = rows_per_item(rg);
+  r.shared_expert = L->shared ? 1 : 0;
+  r.route_kernels = lay.C == 1 ? 1 : 2;
+  r.workspace_bytes = lay.total;
+  r.static_scratch = from_scratch ? 1 : 0;
+  t_rc = &r;
+  if ((rc = do_route(L, x, logits, M, ws, lay, st)) == QMOE_OK && (rc = do_gate_up(L, M, ws, lay, st)) == QMOE_OK &&
+      (rc = do_down(L, M, ws, lay, st)) == QMOE_OK)
+    rc = do_combine(L, M, out, ws, lay, st);
+  t_rc = nullptr;
+  if (rc != QMOE_OK) return rc;
   L->forward_calls++;
+  r.seq = ++L->receipt_seq;
+  std::lock_guard<std::mutex> lock(L->receipt_mu);
+  L->last = r;
+  L->has_receipt = true;
+  return QMOE_OK;
+}
+}  // namespace
+
+int qmoe_forward(qmoe_layer* L, const void* x, const float* logits, int64_t M, void* out, void* ws,
+                 size_t ws_bytes, void* stream) {
+  return forward_impl(L, x, logits, M, out, ws, ws_bytes, static_cast<hipStream_t>(stream), false);
+}
+
+int qmoe_last_receipt(const qmoe_layer* L, qmoe_receipt* out) {
+  if (!L || !out) return fail(QMOE_ERR_ARG, "layer or receipt is NULL");
+  std::lock_guard<std::mutex> lock(const_cast<qmoe_layer*>(L)->receipt_mu);
+  if (!L->has_receipt) return fail(QMOE_ERR_ARG, "no forward call has completed on this layer");
+  *out = L->last;
+  return QMOE_OK;
+}
+
+int qmoe_read_item_count(qmoe_layer* L, int64_t M, const void* ws, size_t ws_bytes, int32_t* n_items, void* stream) {
+  Layout lay;
+  int rc = check_call(L, M, ws, ws_bytes, &lay);
+  if (rc != QMOE_OK) return rc;
+  if (!n_items) return fail(QMOE_ERR_ARG, "n_items is NULL");
+  if (M == 0) return fail(QMOE_ERR_ARG, "M=0 builds no work list");
+  if (hipMemcpyAsync(n_items, static_cast<const char*>(ws) + lay.ctrl + 4, 4, hipMemcpyDeviceToDevice,
+                     static_cast<hipStream_t>(stream)) != hipSuccess)
+    return fail(QMOE_ERR_LAUNCH, "hipMemcpyAsync of the item count failed");
   return QMOE_OK;
 }
 
@@ -1726,7 +1784,7 @@ int qmoe_forward_static(qmoe_layer* L, const void* x, const float* logits, int64
   if (need > kScratchBytes)
     return fail(QMOE_ERR_WORKSPACE, "M=" + std::to_string(M) + " needs " + std::to_string(need) +
                                         " bytes of scratch, more than the static " + std::to_string(kScratchBytes));
-  return qmoe_forward(L, x, logits, M, out, L->scratch, kScratchBytes, stream);
+  return forward_impl(L, x, logits, M, out, L->scratch, kScratchBytes, static_cast<hipStream_t>(stream), true);
 }
 
 int qmoe_read_routing(qmoe_layer* L, int64_t M, const void* ws, size_t ws_bytes, int32_t* ids, float* w,

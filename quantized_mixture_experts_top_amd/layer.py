@@ -10,7 +10,7 @@ import ctypes
 import numpy as np
 import torch
 
-from ._binding import LayerDesc, Stats, check, load_library
+from ._binding import LayerDesc, Receipt, Stats, check, load_library
 
 GROUP = 32
 
@@ -168,6 +168,19 @@ class Layer:
         s = Stats()
         check(self.lib.qmoe_get_stats(self.handle, ctypes.byref(s)))
         return s.as_dict()
+
+    def receipt(self) -> dict:
+        """The engagement receipt of the last completed forward call."""
+        r = Receipt()
+        check(self.lib.qmoe_last_receipt(self.handle, ctypes.byref(r)))
+        return r.as_dict()
+
+    def item_count(self, M, stream=None) -> int:
+        """Work items the last routing on this stream's workspace built (read back from the device)."""
+        n = torch.zeros(1, dtype=torch.int32, device=self.device)
+        ws, nb, st = self._args(M, stream)
+        check(self.lib.qmoe_read_item_count(self.handle, M, ws, nb, _ptr(n), st))
+        return int(n.item())
 
     def reset_stats(self):
         check(self.lib.qmoe_reset_stats(self.handle))

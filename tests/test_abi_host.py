@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert lib.qmoe_version() == 2
+    assert lib.qmoe_version() == B.ABI_VERSION == 3
 
 
 def _desc(**kw):
@@ -104,6 +104,10 @@ def test_calls_on_null_layer(lib):
     s = B.Stats()
     assert lib.qmoe_get_stats(None, ctypes.byref(s)) == B.QMOE_ERR_ARG
     assert lib.qmoe_workspace_init(None, None, 0, None) == B.QMOE_ERR_ARG
+    r = B.Receipt()
+    assert lib.qmoe_last_receipt(None, ctypes.byref(r)) == B.QMOE_ERR_ARG
+    assert lib.qmoe_read_item_count(None, 1, None, 0, None, None) == B.QMOE_ERR_ARG
+    assert lib.qmoe_forward_static(None, None, None, 1, None, None) == B.QMOE_ERR_ARG
     lib.qmoe_layer_destroy(None)  # no-op
 
 

@@ -470,3 +470,45 @@ def test_errors_from_the_library():
     assert "needs" in layer.lib.qmoe_last_error().decode()
     with pytest.raises(QmoeError):
         check(layer.lib.qmoe_dequant_debug(layer.handle, shape.E, 0, None, None))
+
+
+@pytest.mark.parametrize("E,H,I,k,M,shared", [
+    (64, 1024, 512, 4, 9, False),    # GEMV, codes non-temporal (M*k <= E, no shared expert)
+    (64, 1024, 512, 4, 20, True),    # GEMV with a shared expert (default cache policy)
+    (64, 1024, 512, 4, 130, True),   # tiles; routing in two kernels (more than 64 tokens)
+    (8, 256, 128, 2, 16, False),     # tiles; one routing kernel
+])
+def test_receipt_exact_counts(E, H, I, k, M, shared):
+    """The per-call receipt names the regime, cache policy, launches, grid
+    sizes and workspace bytes the call used, and the device's work-item count
+    equals the count the oracle's routing implies exactly."""
+    import math
+    shape = synth.LayerShape(E=E, H=H, I=I, top_k=k, shared=shared)
+    layer, w = make_layer(shape, 41, M)
+    x, lg = synth.hidden(42, M, H), synth.logits(43, M, E)
+    layer.forward(dev_bf16(x), dev(lg))
+    layer.forward(dev_bf16(x), dev(lg))
+    r = layer.receipt()
+    counts = oracle_moe.route(lg, k)["counts"]
+    gemv = 4 * M * k <= 7 * E
+    rpi = 2 if gemv else 128
+    items = sum(math.ceil(int(c) / rpi) for c in counts) + (math.ceil(M / rpi) if shared else 0)
+    T = M * k
+    max_items = T // rpi + min(E, T) + (math.ceil(M / rpi) if shared else 0)
+    say(f"receipt E={E} M={M} shared={shared}: {r}; device items {layer.item_count(M)} (expected {items})")
+    assert layer.item_count(M) == items
+    assert r["seq"] == 2 and r["M"] == M
+    assert r["regime"] == ("gemv" if gemv else "tiles") and r["rows_per_item"] == rpi
+    assert r["nt_codes"] == int(gemv and T <= E and not shared)
+    assert r["shared_expert"] == int(shared) and r["static_scratch"] == 0
+    assert r["route_kernels"] == (1 if M <= 64 else 2)
+    assert r["launches"] == 3 + r["route_kernels"]
+    assert r["max_items"] == max_items >= items
+    if gemv:
+        assert r["gate_up_blocks"] == max_items * math.ceil(I / 64)
+        assert r["down_blocks"] == max_items * math.ceil(H / 128)
+    else:
+        assert r["gate_up_blocks"] == 8 * math.ceil(I / 128) * math.ceil(max_items / 8)
+        assert r["down_blocks"] == 8 * math.ceil(H / 128) * math.ceil(max_items / 8)
+    assert r["combine_blocks"] == math.ceil(M * H / 4 / 256)
+    assert r["workspace_bytes"] == layer.workspace_bytes(M)

@@ -40,6 +40,7 @@ def test_forward_static_matches_forward():
         assert rc == 0, layer.lib.qmoe_last_error().decode()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), want.view(torch.int16))
+        assert layer.receipt()["static_scratch"] == 1
         ref = oracle_moe.forward(x, lg, shape.top_k, expert_getter(w), shape.I, shared=shared_of(w))
         err = rel_err(out.float().cpu().numpy(), ref["out"])
         say(f"  bit-equal to qmoe_forward; rel err vs oracle {err:.3e}")
