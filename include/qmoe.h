@@ -159,6 +159,24 @@ int qmoe_forward(qmoe_layer* layer, const void* x, const float* logits, int64_t 
 int qmoe_forward_static(qmoe_layer* layer, const void* x, const float* logits, int64_t M, void* out,
                         void* stream);
 
+/* The router in front of the layer ("The MoE Throughput Lever: Quantifying
+   the INT4 Marlin GEMM on Blackwell PRO 6000", section "The Context: Why
+   This Measurement Matters" states top-8 routing over 384 experts, not how
+   the scores are made; this build reads it as a linear map):
+     logits[t, e] = sum_k x[t, k] * w_router[e, k]
+   x: bf16 [M,H]; w_router: bf16 [E,H], row-major (device pointers, 16-byte
+   aligned); logits: fp32 [M,E] (device).  Products of two bf16 values are
+   exact in fp32; the sum is accumulated in fp32 (bf16 MFMA above 16 tokens,
+   fp32 FMAs below).  One kernel launch; M == 0 is a no-op. */
+int qmoe_router_logits(qmoe_layer* layer, const void* x, const void* w_router, int64_t M, float* logits,
+                       void* stream);
+
+/* The router and the whole layer in one call: qmoe_router_logits into the
+   workspace (its size already covers the M*E logits), then qmoe_forward on
+   them.  Same arguments as qmoe_forward with w_router in place of logits. */
+int qmoe_forward_router(qmoe_layer* layer, const void* x, const void* w_router, int64_t M, void* out,
+                        void* workspace, size_t ws_bytes, void* stream);
+
 /* The same four steps one at a time, on one workspace and in this order
    (each reads what the previous one left in the workspace).  They let a
    caller time or check each step alone.
@@ -245,7 +263,7 @@ typedef struct {
   int64_t combine_blocks;
   uint64_t workspace_bytes; /* workspace bytes the call used */
   int32_t static_scratch;   /* 1: qmoe_forward_static (library scratch) */
-  int32_t reserved;
+  int32_t router;           /* 1: qmoe_forward_router (logits computed in the call) */
 } qmoe_receipt;
 
 /* Copy the receipt of the last completed forward call (QMOE_ERR_ARG if none

@@ -99,3 +99,21 @@ def layer(x_bits, logits, k, experts, H, I, shared=None):
         all_ids.append(ids)
         all_w.append([mask[e] for e in ids])
     return out, all_ids, all_w
+
+
+def router_logits(x_bits, wr_bits):
+    """Router logits by explicit loops: logits[t][e] = sum over k of
+    x[t][k] * W_r[e][k], each bf16 decoded from its bit pattern, summed in
+    Python floats."""
+    M, H = len(x_bits), len(x_bits[0])
+    out = []
+    for t in range(M):
+        xs = [_bf16(x_bits[t][kk]) for kk in range(H)]
+        row = []
+        for wr in wr_bits:
+            acc = 0.0
+            for kk in range(H):
+                acc += xs[kk] * _bf16(wr[kk])
+            row.append(acc)
+        out.append(row)
+    return out

@@ -88,6 +88,18 @@ def dequant(packed: np.ndarray, scales_bits: np.ndarray) -> np.ndarray:
 # ----------------------------------------------------------------- routing
 
 
+def router_logits(x_bits: np.ndarray, wr_bits: np.ndarray) -> np.ndarray:
+    """The router in front of the layer: logits[t, e] = sum_k x[t, k] *
+    W_r[e, k], a plain product of the bf16 hidden states [M, H] with the bf16
+    router weights [E, H], in float64 (exact products of two bf16 values).
+    The pages state top-8 routing over 384 experts but neither the router
+    nor its scoring ("The MoE Throughput Lever ...", section "The Context:
+    Why This Measurement Matters"); this is the plainest reading: a linear
+    map to one logit per expert, whose scores the softmax-then-top-k routing
+    below consumes."""
+    return decode_bf16(x_bits) @ decode_bf16(wr_bits).T
+
+
 def select_topk(logits: np.ndarray, k: int) -> np.ndarray:
     """Per token, the k experts with the largest logit, ties to the lower
     expert index, in that order.  [M, E] -> int32 [M, k]."""

@@ -54,10 +54,10 @@ class Receipt(ctypes.Structure):
                 ("launches", ctypes.c_int32), ("route_kernels", ctypes.c_int32), ("max_items", ctypes.c_int64),
                 ("gate_up_blocks", ctypes.c_int64), ("down_blocks", ctypes.c_int64),
                 ("combine_blocks", ctypes.c_int64), ("workspace_bytes", ctypes.c_uint64),
-                ("static_scratch", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("static_scratch", ctypes.c_int32), ("router", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
-        d = {n: int(getattr(self, n)) for n, _ in self._fields_ if n != "reserved"}
+        d = {n: int(getattr(self, n)) for n, _ in self._fields_}
         d["regime"] = {1: "gemv", 2: "tiles"}.get(d["regime"], d["regime"])
         return d
 
@@ -74,6 +74,8 @@ SIGNATURES = {
     "qmoe_workspace_init": (ctypes.c_int, [_VP, _VP, _SZ, _VP]),
     "qmoe_forward": (ctypes.c_int, [_VP, _VP, _VP, _I64, _VP, _VP, _SZ, _VP]),
     "qmoe_forward_static": (ctypes.c_int, [_VP, _VP, _VP, _I64, _VP, _VP]),
+    "qmoe_router_logits": (ctypes.c_int, [_VP, _VP, _VP, _I64, _VP, _VP]),
+    "qmoe_forward_router": (ctypes.c_int, [_VP, _VP, _VP, _I64, _VP, _VP, _SZ, _VP]),
     "qmoe_route": (ctypes.c_int, [_VP, _VP, _VP, _I64, _VP, _SZ, _VP]),
     "qmoe_gate_up": (ctypes.c_int, [_VP, _I64, _VP, _SZ, _VP]),
     "qmoe_down": (ctypes.c_int, [_VP, _I64, _VP, _SZ, _VP]),

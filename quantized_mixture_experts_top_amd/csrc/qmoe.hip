@@ -1245,6 +1245,157 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint2* y, uint2
   out[q] = o;
 }
 
+// ----------------------------------------------------------------- router
+
+// The router in front of the layer: logits[t, e] = sum_k x[t, k] * W_r[e, k]
+// with bf16 x [M, H] and bf16 W_r [E, H], accumulated in fp32 (products of
+// two bf16 values are exact in fp32).  The pages state top-8 routing over
+// 384 experts but not the router ("The MoE Throughput Lever: Quantifying the
+// INT4 Marlin GEMM on Blackwell PRO 6000", section "The Context: Why This
+// Measurement Matters"): a linear map to one logit per expert is the
+// plainest reading.
+
+struct RouterArgs {
+  const uint4* x;   // bf16 [M, H] as 16-byte runs
+  const uint4* wr;  // bf16 [E, H]
+  float* logits;    // fp32 [M, E]
+  int M, E, H;
+};
+
+constexpr int kRouterGemvTokens = 4;   // tokens per wave of the GEMV
+constexpr int kRouterGemvMaxM = 16;    // the GEMV up to this many tokens, tiles above
+
+// bf16 pair (one dword) dotted with another, accumulated by two fp32 FMAs
+__device__ __forceinline__ float dot_bf16x2(uint32_t a, uint32_t b, float acc) {
+  acc = fmaf(bf16_lo(a), bf16_lo(b), acc);
+  return fmaf(bf16_hi(a), bf16_hi(b), acc);
+}
+
+// Small M: one wave per (expert, group of up to 4 tokens); each lane takes
+// 8 consecutive inputs of every 512, the 64 lanes' partial sums are added by
+// a butterfly.  The router row is read once per token group, x from cache.
+__global__ __launch_bounds__(kThreads) void router_gemv_kernel(RouterArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wid = (int)blockIdx.x * (kThreads / 64) + (int)(threadIdx.x >> 6);
+  const int e = wid % a.E, tg = wid / a.E;
+  const int t0 = tg * kRouterGemvTokens;
+  if (t0 >= a.M) return;
+  const int runs = a.H / 8;
+  const uint4* wrow = a.wr + (size_t)e * runs;
+  const uint4* xrow[kRouterGemvTokens];
+#pragma unroll
+  for (int u = 0; u < kRouterGemvTokens; ++u) xrow[u] = a.x + (size_t)min(t0 + u, a.M - 1) * runs;  // clamped
+  float acc[kRouterGemvTokens] = {};
+  for (int v = lane; v < runs; v += 64) {
+    const uint4 w = wrow[v];
+#pragma unroll
+    for (int u = 0; u < kRouterGemvTokens; ++u) {
+      const uint4 xv = xrow[u][v];
+      acc[u] = dot_bf16x2(w.x, xv.x, acc[u]);
+      acc[u] = dot_bf16x2(w.y, xv.y, acc[u]);
+      acc[u] = dot_bf16x2(w.z, xv.z, acc[u]);
+      acc[u] = dot_bf16x2(w.w, xv.w, acc[u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kRouterGemvTokens; ++u) {
+    float v = acc[u];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    if (lane == 0 && t0 + u < a.M) a.logits[(size_t)(t0 + u) * a.E + e] = v;
+  }
+}
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+constexpr int kRouterTile = 64;   // tokens and experts per block
+constexpr int kRouterKC = 64;     // inputs per K chunk (two MFMA k-slices)
+
+// Larger M: 64-token x 64-expert tiles, 4 waves of 16 tokens each; bf16
+// MFMA 16x16x32 with fp32 accumulators.  Each K chunk of the block's router
+// rows (64 rows x 128 bytes) goes from memory straight into LDS (lane l of a
+// load instruction fills bytes 16l..16l+15 of its 1 KiB), double-buffered;
+// the 16-byte piece p of row n sits at slot p ^ ((n >> 1) & 7), so the 16
+// rows an MFMA operand read touches fall in distinct banks.  Each wave's
+// token fragments come from memory into registers, one chunk ahead.
+__global__ __launch_bounds__(kThreads) void router_tile_kernel(RouterArgs a) {
+  __shared__ __attribute__((aligned(16))) _Float16 lds_b0[kRouterTile * kRouterKC];
+  __shared__ __attribute__((aligned(16))) _Float16 lds_b1[kRouterTile * kRouterKC];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, kq = lane >> 4;
+  const int ntt = (a.M + kRouterTile - 1) / kRouterTile;
+  const int t0 = ((int)blockIdx.x % ntt) * kRouterTile, e0 = ((int)blockIdx.x / ntt) * kRouterTile;
+  const uint32_t row_bytes = (uint32_t)a.H * 2;
+  const __amdgpu_buffer_rsrc_t rX = buffer_rsrc(a.x, (uint32_t)a.M * row_bytes);
+  const __amdgpu_buffer_rsrc_t rW = buffer_rsrc(a.wr, (uint32_t)a.E * row_bytes);
+  // this lane's token row (rows past M read zeros)
+  const int trow = t0 + 16 * wave + r;
+  const uint32_t xoff = trow < a.M ? (uint32_t)trow * row_bytes + 16 * kq : kOob;
+  // router-row loads: instruction j of this wave fills rows 8(2*wave + j) ..
+  // +7 of the chunk; lane l: row + l/8, LDS slot l%8 holds piece
+  // (l%8) ^ ((row >> 1) & 7)
+  uint32_t woff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = 8 * (2 * wave + j) + (lane >> 3);
+    const int piece = (lane & 7) ^ ((n >> 1) & 7);
+    woff[j] = e0 + n < a.E ? (uint32_t)(e0 + n) * row_bytes + 16 * piece : kOob;
+  }
+  const int nchunks = a.H / kRouterKC;
+  auto load_w = [&](int c, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      load_lds16(rW, (buf ? lds_b1 : lds_b0) + (8 * (2 * wave + j)) * kRouterKC, woff[j], c * kRouterKC * 2);
+  };
+  auto load_x = [&](int c, u32x4_t (&xf)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      xf[s] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rX, xoff, c * kRouterKC * 2 + 64 * s, 0));
+  };
+  float4_t acc[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) acc[cb] = float4_t{0.f, 0.f, 0.f, 0.f};
+  u32x4_t xa[2], xb[2];
+  load_w(0, 0);
+  load_x(0, xa);
+  wait_vmcnt<0>();
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    const int buf = c & 1;
+    const bool more = c + 1 < nchunks;
+    if (more) {
+      load_w(c + 1, buf ^ 1);
+      load_x(c + 1, xb);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const _Float16* lb = buf ? lds_b1 : lds_b0;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, xa[s]);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int n = 16 * cb + r, piece = 4 * s + kq;
+        const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(lb + n * kRouterKC + 8 * (piece ^ ((n >> 1) & 7)));
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bv), acc[cb], 0, 0, 0);
+      }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    xa[0] = xb[0];
+    xa[1] = xb[1];
+  }
+  // lane (r, kq) holds tokens 4kq..4kq+3 of its wave's 16, expert column r
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int e = e0 + 16 * cb + r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 16 * wave + 4 * kq + i;
+      if (t < a.M && e < a.E) a.logits[(size_t)t * a.E + e] = acc[cb][i];
+    }
+  }
+}
+
 // ------------------------------------------------------------- inspection
 
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t* w, const uint16_t* s, int N,
@@ -1303,7 +1454,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
   int64_t T, S, R, C, max_items_all;
-  size_t ctrl, ids, wts, counts, offsets, perm, inv_perm, items, xexp, xa, h, y, total;
+  size_t ctrl, ids, wts, counts, offsets, perm, inv_perm, items, xexp, logits, xa, h, y, total;
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -1380,6 +1531,7 @@ Layout make_layout(const qmoe_layer* L, int64_t M) {
   l.inv_perm = take(l.T * 4);
   l.items = take(l.max_items_all * 16);
   l.xexp = take(M * 4);
+  l.logits = take(M * E * 4);  // router logits of qmoe_forward_router
   l.xa = take(M * H * 2);
   l.h = take(l.R * I * 2);
   l.y = take(l.R * H * 2);
@@ -1619,6 +1771,27 @@ int do_combine(qmoe_layer* L, int64_t M, void* out, void* ws, const Layout& lay,
   return check_launch(L, "combine_kernel");
 }
 
+int do_router(qmoe_layer* L, const void* x, const void* w_router, int64_t M, float* logits, hipStream_t st) {
+  if (!x || !w_router || !logits) return fail(QMOE_ERR_ARG, "x, w_router or logits is NULL");
+  if (!aligned16(x) || !aligned16(w_router)) return fail(QMOE_ERR_ARG, "x and w_router must be 16-byte aligned");
+  if ((int64_t)L->d.E * L->d.H * 2 >= (1LL << 31)) return fail(QMOE_ERR_UNSUPPORTED, "router weights too large");
+  RouterArgs a;
+  a.x = static_cast<const uint4*>(x);
+  a.wr = static_cast<const uint4*>(w_router);
+  a.logits = logits;
+  a.M = (int)M;
+  a.E = L->d.E;
+  a.H = L->d.H;
+  if (M <= kRouterGemvMaxM) {
+    const int64_t waves = (int64_t)L->d.E * ceil_div(M, kRouterGemvTokens);
+    router_gemv_kernel<<<dim3((unsigned)ceil_div(waves, kThreads / 64)), kThreads, 0, st>>>(a);
+    return check_launch(L, "router_gemv_kernel");
+  }
+  const int64_t blocks = ceil_div(M, kRouterTile) * ceil_div(L->d.E, kRouterTile);
+  router_tile_kernel<<<dim3((unsigned)blocks), kThreads, 0, st>>>(a);
+  return check_launch(L, "router_tile_kernel");
+}
+
 }  // namespace
 
 // ================================================================ C ABI
@@ -1755,6 +1928,36 @@ int forward_impl(qmoe_layer* L, const void* x, const float* logits, int64_t M, v
 int qmoe_forward(qmoe_layer* L, const void* x, const float* logits, int64_t M, void* out, void* ws,
                  size_t ws_bytes, void* stream) {
   return forward_impl(L, x, logits, M, out, ws, ws_bytes, static_cast<hipStream_t>(stream), false);
+}
+
+int qmoe_router_logits(qmoe_layer* L, const void* x, const void* w_router, int64_t M, float* logits,
+                       void* stream) {
+  if (!L) return fail(QMOE_ERR_ARG, "layer is NULL");
+  if (M < 0 || M > L->d.max_rows) return fail(QMOE_ERR_ARG, "M outside [0, max_rows]");
+  if (M == 0) return QMOE_OK;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != L->device) return fail(QMOE_ERR_DEVICE, "not the layer's device");
+  return do_router(L, x, w_router, M, logits, static_cast<hipStream_t>(stream));
+}
+
+int qmoe_forward_router(qmoe_layer* L, const void* x, const void* w_router, int64_t M, void* out, void* ws,
+                        size_t ws_bytes, void* stream) {
+  Layout lay;
+  int rc = check_call(L, M, ws, ws_bytes, &lay);
+  if (rc != QMOE_OK || M == 0) return rc;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  float* logits = at<float>(ws, lay.logits);
+  qmoe_receipt r0{};
+  t_rc = &r0;  // the router launch counts toward the call's receipt
+  rc = do_router(L, x, w_router, M, logits, st);
+  t_rc = nullptr;
+  if (rc != QMOE_OK) return rc;
+  rc = forward_impl(L, x, logits, M, out, ws, ws_bytes, st, false);
+  if (rc != QMOE_OK) return rc;
+  std::lock_guard<std::mutex> lock(L->receipt_mu);
+  L->last.launches += r0.launches;
+  L->last.router = 1;
+  return QMOE_OK;
 }
 
 int qmoe_last_receipt(const qmoe_layer* L, qmoe_receipt* out) {

@@ -116,6 +116,30 @@ class Layer:
 
     __call__ = forward
 
+    def router_logits(self, x, w_router, stream=None):
+        """fp32 [M, E] logits of bf16 x [M, H] through bf16 router weights [E, H]."""
+        M = x.shape[0]
+        if x.dtype != torch.bfloat16 or tuple(x.shape) != (M, self.H):
+            raise ValueError(f"x must be bf16 [M, {self.H}]")
+        if w_router.dtype != torch.bfloat16 or tuple(w_router.shape) != (self.E, self.H):
+            raise ValueError(f"w_router must be bf16 [{self.E}, {self.H}]")
+        out = torch.empty((M, self.E), dtype=torch.float32, device=self.device)
+        check(self.lib.qmoe_router_logits(self.handle, _ptr(x), _ptr(w_router), M, _ptr(out), _stream(stream)))
+        return out
+
+    def forward_router(self, x, w_router, out=None, stream=None):
+        """The router and the whole layer in one call."""
+        M = x.shape[0]
+        if x.dtype != torch.bfloat16 or tuple(x.shape) != (M, self.H):
+            raise ValueError(f"x must be bf16 [M, {self.H}]")
+        if w_router.dtype != torch.bfloat16 or tuple(w_router.shape) != (self.E, self.H):
+            raise ValueError(f"w_router must be bf16 [{self.E}, {self.H}]")
+        if out is None:
+            out = torch.empty((M, self.H), dtype=torch.bfloat16, device=self.device)
+        ws, nb, st = self._args(M, stream)
+        check(self.lib.qmoe_forward_router(self.handle, _ptr(x), _ptr(w_router), M, _ptr(out), ws, nb, st))
+        return out
+
     def route(self, x, logits, stream=None):
         M = self._check_inputs(x, logits)
         ws, nb, st = self._args(M, stream)

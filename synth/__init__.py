@@ -19,6 +19,7 @@ SeedSequence([seed, tag, index]) so that one expert can be regenerated alone:
   tag 2  gate+up codes  (per expert) tag 3  gate+up scales (per expert)
   tag 4  down codes     (per expert) tag 5  down scales    (per expert)
   tag 6..9  the shared expert's gate+up codes, scales, down codes, scales
+  tag 10  router weights (bf16 [E, H])
 
 Packed code bytes are the little-endian bytes of PCG64's raw 64-bit outputs;
 each byte is uniform on 0..255, so both of its nibbles are uniform on 0..15.
@@ -36,6 +37,7 @@ ZIPF_S = 1.2
 TAG_X, TAG_LOGITS = 0, 1
 TAG_W13, TAG_S13, TAG_W2, TAG_S2 = 2, 3, 4, 5
 TAG_SHARED_W13, TAG_SHARED_S13, TAG_SHARED_W2, TAG_SHARED_S2 = 6, 7, 8, 9
+TAG_ROUTER = 10
 
 SCALE_LO, SCALE_HI = 0.002, 0.02
 
@@ -118,6 +120,13 @@ def logits(seed: int, M: int, E: int, skew: bool = False) -> np.ndarray:
     return z
 
 
+def router_weights(seed: int, E: int, H: int) -> np.ndarray:
+    """Router weights W_r: N(0, 1/H) float32 rounded to bf16, [E, H] (so that
+    the logits of N(0,1) hidden states are about N(0,1)); uint16 patterns."""
+    w = _rng(seed, TAG_ROUTER).standard_normal((E, H), dtype=np.float32) * np.float32(1.0 / np.sqrt(H))
+    return f32_to_bf16_bits(w)
+
+
 def _scales(seed: int, tag: int, index: int, rows: int, groups: int) -> np.ndarray:
     s = _rng(seed, tag, index).uniform(SCALE_LO, SCALE_HI, size=(rows, groups))
     return s.astype(np.float32).astype(np.float16).view(np.uint16)
@@ -185,5 +194,5 @@ def inputs(seed: int, shape: LayerShape, M: int, skew: bool = False, logits_seed
 __all__ = [
     "GROUP", "LayerShape", "Workload", "WORKLOADS", "TINY", "FULL", "FULL_SHARED", "TP8_SLICE",
     "f32_to_bf16_bits", "hidden", "logits", "zipf_bias", "expert", "all_experts",
-    "inputs", "expected_touched",
+    "inputs", "expected_touched", "router_weights",
 ]

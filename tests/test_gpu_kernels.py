@@ -512,3 +512,61 @@ def test_receipt_exact_counts(E, H, I, k, M, shared):
         assert r["down_blocks"] == 8 * math.ceil(H / 128) * math.ceil(max_items / 8)
     assert r["combine_blocks"] == math.ceil(M * H / 4 / 256)
     assert r["workspace_bytes"] == layer.workspace_bytes(M)
+
+
+# ------------------------------------------------------------ router GEMM
+
+
+def _router_only_layer(E, H, max_rows):
+    """A layer handle for router calls only: the router kernels read no
+    expert weights, so tiny placeholder tensors stand in for them."""
+    import torch
+    from quantized_mixture_experts_top_amd import Layer
+    ph = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    ps = torch.zeros(128, dtype=torch.int16, device="cuda")
+    return Layer(E=E, H=H, I=128, top_k=min(8, E), max_rows=max_rows, w13=ph, s13=ps, w2=ph, s2=ps)
+
+
+@pytest.mark.parametrize("E,H,M", [
+    (384, 7168, 1), (384, 7168, 9), (384, 7168, 16),   # GEMV (one wave per expert and 4 tokens)
+    (384, 7168, 17), (384, 7168, 300),                 # 64x64 MFMA tiles, ragged token tile
+    (100, 1024, 70), (8, 256, 16), (1000, 128, 65),    # experts not a multiple of 64; K of 2 chunks
+])
+def test_router_logits_parity(E, H, M):
+    """logits = x @ W_r^T (bf16 inputs, fp32 accumulation) against the
+    float64 oracle: each entry within 4e-5 of sum_k |x_k w_k| (fp32 rounding
+    of a K-term sum), plus the routing the GPU logits give bit-exact."""
+    x, wr = synth.hidden(51, M, H), synth.router_weights(52, E, H)
+    layer = _router_only_layer(E, H, M)
+    got = layer.router_logits(dev_bf16(x), dev_bf16(wr)).cpu().numpy().astype(np.float64)
+    ref = oracle_moe.router_logits(x, wr)
+    bound = 4e-5 * (np.abs(oracle_moe.decode_bf16(x)) @ np.abs(oracle_moe.decode_bf16(wr)).T) + 1e-30
+    worst = float(np.max(np.abs(got - ref) / bound))
+    say(f"router E={E} H={H} M={M}: worst |gpu-oracle| / bound = {worst:.3f}; max|logit| {np.max(np.abs(ref)):.3f}")
+    assert worst <= 1.0
+
+
+@pytest.mark.parametrize("M", [9, 130])
+def test_forward_router(M):
+    """The router and the layer in one call: bit-equal to the two-step path
+    (router logits, then forward), routing bit-exact against the oracle on
+    those logits, output within the bar of the oracle's."""
+    import torch
+    shape = synth.LayerShape(E=64, H=1024, I=512, top_k=4, shared=True)
+    layer, w = make_layer(shape, 61, M)
+    x, wr = synth.hidden(62, M, shape.H), synth.router_weights(63, shape.E, shape.H)
+    xd, wrd = dev_bf16(x), dev_bf16(wr)
+    lg = layer.router_logits(xd, wrd)
+    two_step = layer.forward(xd, lg).clone()
+    base_launches = layer.receipt()["launches"]
+    fused = layer.forward_router(xd, wrd)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int16), two_step.view(torch.int16))
+    r = layer.receipt()
+    assert r["router"] == 1 and r["launches"] == base_launches + 1
+    lgn = lg.cpu().numpy()
+    ref = oracle_moe.forward(x, lgn, shape.top_k, expert_getter(w), shape.I, shared=shared_of(w))
+    check_routing(layer, M, ref, shape.E)
+    err = rel_err(fused.float().cpu().numpy(), ref["out"])
+    say(f"forward_router M={M}: rel err {err:.3e}")
+    assert err <= REL_TOL

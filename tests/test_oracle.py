@@ -305,3 +305,42 @@ def test_empty_call():
     ex, _ = _tiny_experts(1, 4, 32, 32)
     r = moe.forward(np.zeros((0, 32), np.uint16), np.zeros((0, 4), np.float32), 2, lambda e: ex[e], 32)
     assert r["out"].shape == (0, 32) and r["perm"].size == 0 and r["counts"].sum() == 0
+
+
+# ------------------------------------------------------------ router GEMM
+
+
+def test_router_logits_against_loops():
+    """The oracle's router product against explicit Python loops (another
+    code path: element-by-element bf16 decode, no matrix product)."""
+    x = synth.hidden(5, 3, 64)
+    wr = synth.router_weights(6, 5, 64)
+    got = moe.router_logits(x, wr)
+    want = np.array(brute.router_logits(x.tolist(), wr.tolist()))
+    assert got.shape == (3, 5)
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_router_logits_closed_forms():
+    """One-hot router rows pick hidden columns exactly (a transposed operand
+    would pick rows); all-ones rows give the row sums."""
+    M, H, E = 4, 32, 6
+    x = synth.hidden(7, M, H)
+    xf = moe.decode_bf16(x)
+    one = np.zeros((E, H), np.float32)
+    cols = [0, 5, 31, 7, 7, 12]
+    for e, c in enumerate(cols):
+        one[e, c] = 1.0
+    got = moe.router_logits(x, synth.f32_to_bf16_bits(one))
+    assert np.array_equal(got, xf[:, cols])
+    ones = synth.f32_to_bf16_bits(np.ones((2, H), np.float32))
+    assert np.allclose(moe.router_logits(x, ones), xf.sum(axis=1, keepdims=True) * np.ones((1, 2)), atol=1e-12)
+
+
+def test_router_weights_give_unit_scale_logits():
+    """The synthetic router (N(0, 1/H) entries) on N(0,1) hidden states gives
+    logits of about unit variance, like the direct logits recipe."""
+    x = synth.hidden(8, 64, 1024)
+    wr = synth.router_weights(9, 128, 1024)
+    lg = moe.router_logits(x, wr)
+    assert 0.85 < lg.std() < 1.15
