@@ -304,6 +304,19 @@ def time_config(layer, shape, wl, M, steps, warmup, graph=False):
         del graphs, outs
     receipt = layer.receipt()
     receipt["items_built"] = layer.item_count(M)  # the last step's routing
+    # the router in front of the layer (an adjacent step, not part of the
+    # timed call): logits of each step's hidden states, bracketed by events
+    wr = torch.from_numpy(synth.router_weights(0, shape.E, shape.H).view(np.int16)).cuda().view(torch.bfloat16)
+    for s in range(min(warmup, 3)):
+        layer.router_logits(xs[s], wr)
+    rv0, rv1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rv0.record(stream)
+    for s in range(warmup, n):
+        layer.router_logits(xs[s], wr)
+    rv1.record(stream)
+    torch.cuda.synchronize()
+    router_us = rv0.elapsed_time(rv1) / steps * 1e3
+    del wr
     del xs, ls
     b13, b2 = bytes_per_expert(shape)
     f13, f2 = flops_per_row(shape)
@@ -335,6 +348,7 @@ def time_config(layer, shape, wl, M, steps, warmup, graph=False):
         "gate_up_flops_per_launch": rows * f13,
         "gate_up_us": float(st_ms[1] * 1e3),
         "bracketed_call_us_p10_p50_p90": [float(np.percentile(per_call_us, q)) for q in (10, 50, 90)],
+        "router_us": router_us,
         "receipt": {k: receipt[k] for k in ("regime", "rows_per_item", "nt_codes", "launches", "max_items",
                                              "items_built", "gate_up_blocks", "down_blocks", "workspace_bytes")},
     }

@@ -665,9 +665,42 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
       if (NBB >= 4) __builtin_amdgcn_sched_barrier(0);                                           \
     }                                                                                            \
   } while (0)
+  // The same compute with the weights of the sub-step after next issued one
+  // 16-row block per k-slice (block b before slice b mod 4) instead of all
+  // before the compute: a wave whose load waits for room in the address
+  // unit's queue then still has MFMAs of the slices before it issued (gate+up
+  // at 4096 tokens 3% faster on MI355X).
+#define QMOE_COMPUTE_IL(F, SC, U, BUF, SB, UB, FNN)                                               \
+  do {                                                                                           \
+    uint32_t s2_[NBB];                                                                           \
+    _Pragma("unroll") for (int b = 0; b < NBB; ++b) s2_[b] = (SC)[b][(U)];                       \
+    half8_t bfa_[NBB], bfb_[NBB];                                                                \
+    _Pragma("unroll") for (int b = 0; b < NBB; ++b) bfa_[b] = dq8p(word((F).b[b], 0), s2_[b]);   \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                              \
+      _Pragma("unroll") for (int b = 0; b < NBB; ++b) {                                          \
+        if (b % 4 == i)                                                                          \
+          (FNN).b[b] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(        \
+              rB, bl + 64 * (UB), (SB) * (kSuper / 2) + brow[b] * K2, 0));                       \
+      }                                                                                          \
+      half8_t* cur_ = (i & 1) ? bfb_ : bfa_;                                                     \
+      half8_t* nxt_ = (i & 1) ? bfa_ : bfb_;                                                     \
+      _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                                        \
+        if (mb < NMBC) {                                                                         \
+          const half8_t av =                                                                     \
+              *reinterpret_cast<const half8_t*>(&QMOE_LDS_A(BUF)[mb * 4 * kBlkHalves + rd_half + 8 * i]); \
+          _Pragma("unroll") for (int b = 0; b < NBB; ++b) acc[mb][b] = mfma16x16x32(av, cur_[b], acc[mb][b]); \
+        }                                                                                        \
+      }                                                                                          \
+      if (i < 3) {                                                                               \
+        _Pragma("unroll") for (int b = 0; b < NBB; ++b) nxt_[b] = dq8p(word((F).b[b], i + 1), s2_[b]); \
+      }                                                                                          \
+      __builtin_amdgcn_sched_barrier(0);                                                         \
+    }                                                                                            \
+  } while (0)
   // One sub-step with one barrier: start the next sub-step's activation
-  // tile (into the other buffer) and then the weights of the sub-step after
-  // next (into FNN), compute this sub-step from fragment set FCUR and
+  // tile (into the other buffer) and, spread over the k-slices, the weights
+  // of the sub-step after next (into FNN), compute this sub-step from
+  // fragment set FCUR and
   // buffer BUF, then wait until at most the NBB weight loads just issued
   // are outstanding (loads complete in order, so the tile, written straight
   // into LDS, and the next sub-step's weights are in) and meet the barrier
@@ -676,9 +709,8 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
 #define QMOE_SUBSTEP(U, FCUR, SA, UA, SB, UB, FNN, BUF)                                         \
   do {                                                                                           \
     QMOE_LOAD_A_TILE((SA), (UA), true, (BUF) ^ 1);                                               \
-    load_b((SB), (UB), FNN, true);                                                               \
-    __builtin_amdgcn_sched_barrier(0); /* keep the loads ahead of the compute */                 \
-    QMOE_COMPUTE(FCUR, sc_cur, (U), (BUF));                                                      \
+    __builtin_amdgcn_sched_barrier(0); /* keep the tile loads ahead of the compute */            \
+    QMOE_COMPUTE_IL(FCUR, sc_cur, (U), (BUF), (SB), (UB), FNN);                                  \
     wait_vmcnt<NBB>();                                                                           \
     __syncthreads();                                                                             \
   } while (0)
@@ -767,7 +799,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   // and meets one barrier per super-step instead of one per sub-step.  With
   // so few rows a sub-step is only 8 MFMAs per wave, far shorter than a trip
   // to memory; this doubles the bytes each wave keeps in flight.
-  auto kloop_ss = [&]() __attribute__((always_inline)) {
+  auto kloop_ss = [&](auto) __attribute__((always_inline)) {  // (generic: instantiated only where used)
     constexpr int NMBC = 2;
     static_assert(MB >= 4 * NMBC, "a super-step of 2-block tiles fits one buffer");
     Frag<NBB> fc0, fc1, fc2, fc3;  // the other super-step's weights
@@ -838,7 +870,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
     }
   };
   if (nmb <= 2) {
-    if constexpr (kEarlyB && MB >= 8) kloop_ss();
+    if constexpr (kEarlyB && MB >= 8) kloop_ss(0);
     else kloop(std::integral_constant<int, (MB < 2 ? MB : 2)>{});
   } else if (nmb <= 4) kloop(std::integral_constant<int, (MB < 4 ? MB : 4)>{});
   else if (MB == 8 && nmb == 5) kloop(std::integral_constant<int, 5>{});
@@ -846,6 +878,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   else if (MB == 8 && nmb == 7) kloop(std::integral_constant<int, 7>{});
   else kloop(std::integral_constant<int, MB>{});
 #undef QMOE_SUBSTEP
+#undef QMOE_COMPUTE_IL
 #undef QMOE_SUBSTEP_PAIR
 #undef QMOE_SUBSTEP_NOB
 #undef QMOE_COMPUTE
