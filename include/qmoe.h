@@ -43,13 +43,17 @@
  *   <= 1.75   dot-product GEMV on items of <= 2 rows: per 32-input group,
  *             sum(x*c) in fp32 (exact products) minus 8*sum(x), times the
  *             group's scale in fp32 (an all-8 group is zero only up to
- *             fp32 cancellation);
+ *             fp32 cancellation); a launch of fewer than 128 blocks splits
+ *             K over up to one block per 512 inputs, and the last block of
+ *             each split set adds the fp32 partial sums in split order;
  *   > 1.75    128-row MFMA tiles: codes decoded to fp16 operands
  *             ((c-8)*scale rounded to nearest even), products accumulated
  *             in fp32 by MFMA.
  * The weighted per-slot results are rounded to bf16 (nearest even) in the
  * workspace, summed per token in fp32 in slot order, and out is rounded to
- * bf16 (nearest even).  Results are deterministic for a given M.
+ * bf16 (nearest even).  Results are deterministic for a given M (the regime,
+ * the work items and the K splits depend on M, so a token's result may
+ * differ in its last bits between calls of different M).
  *
  * Ownership: the caller owns every buffer.  The layer handle borrows the
  * weight pointers for its lifetime and copies nothing.  The library never
@@ -234,6 +238,7 @@ typedef struct {
   uint64_t gemv_nt_launches;  /* dot-product launches (gate+up and down) reading the
                                  weight codes with the non-temporal cache policy:
                                  calls with M*top_k <= E and no shared expert */
+  uint64_t splitk_launches;   /* dot-product launches with K split over blocks */
 } qmoe_stats;
 
 int qmoe_get_stats(const qmoe_layer* layer, qmoe_stats* out);
@@ -264,6 +269,8 @@ typedef struct {
   uint64_t workspace_bytes; /* workspace bytes the call used */
   int32_t static_scratch;   /* 1: qmoe_forward_static (library scratch) */
   int32_t router;           /* 1: qmoe_forward_router (logits computed in the call) */
+  int32_t splits_gate_up;   /* K splits of the dot-product launches (1 = none) */
+  int32_t splits_down;
 } qmoe_receipt;
 
 /* Copy the receipt of the last completed forward call (QMOE_ERR_ARG if none

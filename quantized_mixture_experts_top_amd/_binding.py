@@ -42,7 +42,7 @@ class Stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "forward_calls", "route_calls", "gemm_launches", "launches", "workspace_inits",
         "workspace_bytes_last", "workspace_bytes_peak", "prefill_tiles", "gemv_tiles",
-        "gemv_nt_launches")]
+        "gemv_nt_launches", "splitk_launches")]
 
     def as_dict(self) -> dict:
         return {n: int(getattr(self, n)) for n, _ in self._fields_}
@@ -54,7 +54,8 @@ class Receipt(ctypes.Structure):
                 ("launches", ctypes.c_int32), ("route_kernels", ctypes.c_int32), ("max_items", ctypes.c_int64),
                 ("gate_up_blocks", ctypes.c_int64), ("down_blocks", ctypes.c_int64),
                 ("combine_blocks", ctypes.c_int64), ("workspace_bytes", ctypes.c_uint64),
-                ("static_scratch", ctypes.c_int32), ("router", ctypes.c_int32)]
+                ("static_scratch", ctypes.c_int32), ("router", ctypes.c_int32),
+                ("splits_gate_up", ctypes.c_int32), ("splits_down", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         d = {n: int(getattr(self, n)) for n, _ in self._fields_}

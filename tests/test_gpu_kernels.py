@@ -276,8 +276,10 @@ def test_repeat_runs_bitwise_identical(case):
 
 
 @pytest.mark.parametrize("E,H,I,k,M,m,path", [
-    # GEMV both times: 8 tokens alone read the codes non-temporal, 40 do not
-    (64, 1152, 640, 2, 40, 8, "gemv_tiles"),
+    # GEMV both times: 30 tokens alone read the codes non-temporal, 40 do
+    # not; neither call splits K (a split call adds its K shares in another
+    # order, so its bits may differ from an unsplit one)
+    (64, 1152, 640, 2, 40, 30, "gemv_tiles"),
     # tiles both times: 60 tokens alone take the 2-row-block K loops (paired
     # weight loads), all 400 the 6- and 7-block loops
     (4, 256, 128, 1, 400, 60, "prefill_tiles"),
@@ -297,6 +299,7 @@ def test_token_results_do_not_depend_on_the_call(E, H, I, k, M, m, path):
     # the GEMV's m tokens alone read the codes non-temporal (gate+up and
     # down), all M with the default policy; the tiles never do
     assert s["gemv_nt_launches"] == (2 if path == "gemv_tiles" else 0)
+    assert s["splitk_launches"] == 0
     assert torch.equal(full[:m].view(torch.int16), part.view(torch.int16))
 
 
@@ -505,9 +508,16 @@ def test_receipt_exact_counts(E, H, I, k, M, shared):
     assert r["launches"] == 3 + r["route_kernels"]
     assert r["max_items"] == max_items >= items
     if gemv:
-        assert r["gate_up_blocks"] == max_items * math.ceil(I / 64)
-        assert r["down_blocks"] == max_items * math.ceil(H / 128)
+        # a launch of fewer than 128 blocks splits K (about 512 blocks in all,
+        # up to one split per 512 inputs)
+        def splits(tiles, K):
+            return 1 if tiles >= 128 or K // 512 < 2 else min(K // 512, math.ceil(512 / tiles))
+        sg, sd = splits(max_items * math.ceil(I / 64), H), splits(max_items * math.ceil(H / 128), I)
+        assert (r["splits_gate_up"], r["splits_down"]) == (sg, sd)
+        assert r["gate_up_blocks"] == max_items * math.ceil(I / 64) * sg
+        assert r["down_blocks"] == max_items * math.ceil(H / 128) * sd
     else:
+        assert r["splits_gate_up"] == r["splits_down"] == 1
         assert r["gate_up_blocks"] == 8 * math.ceil(I / 128) * math.ceil(max_items / 8)
         assert r["down_blocks"] == 8 * math.ceil(H / 128) * math.ceil(max_items / 8)
     assert r["combine_blocks"] == math.ceil(M * H / 4 / 256)
@@ -570,3 +580,49 @@ def test_forward_router(M):
     err = rel_err(fused.float().cpu().numpy(), ref["out"])
     say(f"forward_router M={M}: rel err {err:.3e}")
     assert err <= REL_TOL
+
+
+# ------------------------------------------------------------ GEMV split-K
+
+SPLITK_CASES = [
+    # E, H, I, k, M, shared: GEMV launches of fewer than 128 blocks split K
+    (8, 4096, 256, 2, 1, False),     # gate+up in 8 splits; down K=256 unsplit
+    (16, 2048, 1024, 2, 2, False),   # gate+up in 4 splits, down in 2
+    (4, 2048, 1536, 1, 1, True),     # shared expert: gate+up 4 splits, down 3
+    (4, 4352, 640, 2, 3, False),     # 8 whole super-steps over 8 splits, a partial one in the last
+]
+
+
+@pytest.mark.parametrize("E,H,I,k,M,shared", SPLITK_CASES)
+def test_gemv_split_k(E, H, I, k, M, shared):
+    """K split over blocks, partial sums added by the last block to arrive
+    in split order: parity with the oracle, bit-identical repeats (the sum
+    does not depend on which block arrives last), the receipt and counter
+    name the split, and a captured graph replays to the eager result."""
+    import torch
+    layer, w, x, lg, ref = _run_case(E, H, I, k, M, shared)
+    xs, ls = dev_bf16(x), dev(lg)
+    layer.reset_stats()
+    out = layer.forward(xs, ls).clone()
+    r = layer.receipt()
+    say(f"split-K E={E} H={H} I={I} M={M} shared={shared}: splits gate+up {r['splits_gate_up']}, "
+        f"down {r['splits_down']}, blocks {r['gate_up_blocks']}/{r['down_blocks']}")
+    assert r["regime"] == "gemv" and r["splits_gate_up"] > 1
+    assert layer.stats()["splitk_launches"] == (r["splits_gate_up"] > 1) + (r["splits_down"] > 1)
+    check_routing(layer, M, ref, E)
+    err = rel_err(out.float().cpu().numpy(), ref["out"])
+    say(f"  rel err out {err:.3e}")
+    assert err <= REL_TOL
+    for _ in range(3):
+        again = layer.forward(xs, ls)
+        assert torch.equal(again.view(torch.int16), out.view(torch.int16))
+    g_out = torch.empty_like(out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(xs, ls, out=g_out)
+    for rep in range(3):
+        g_out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(g_out.view(torch.int16), out.view(torch.int16)), f"replay {rep}"
