@@ -71,7 +71,9 @@ def key_of(workload: str, M: int) -> str:
 
 def upload_weights(seed, shape, threads=16, chunk=32):
     import torch
-    E, H, I = shape.E, shape.H, shape.I
+    H, I = shape.H, shape.I
+    experts = list(shape.local_experts())  # an expert-parallel shard holds its own only
+    E = len(experts)
     out = {
         "w13": torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device="cuda"),
         "s13": torch.empty((E, 2 * I, H // 32), dtype=torch.int16, device="cuda"),
@@ -80,7 +82,7 @@ def upload_weights(seed, shape, threads=16, chunk=32):
     }
     with ThreadPoolExecutor(threads) as ex:
         for e0 in range(0, E, chunk):
-            es = list(range(e0, min(E, e0 + chunk)))
+            es = [experts[i] for i in range(e0, min(E, e0 + chunk))]
             ws = list(ex.map(lambda e: synth.expert(seed, shape, e), es))
             for key in out:
                 a = np.stack([w[key] for w in ws])
@@ -244,11 +246,12 @@ def time_config(layer, shape, wl, M, steps, warmup, graph=False):
     out = torch.empty((M, shape.H), dtype=torch.bfloat16, device="cuda")
     layer.workspace(M)
     # experts touched by each step, from the layer's own routing
-    touched = []
+    touched, local_rows = [], []
     for s in range(n):
         layer.route(xs[s], ls[s])
-        c = layer.read_routing(M)["counts"]
+        c = layer.read_routing(M)["counts"]  # per local expert (all E unless a shard)
         touched.append(int((c > 0).sum().item()) + (1 if shape.shared else 0))
+        local_rows.append(int(c.sum().item()) + (M if shape.shared else 0))
     torch.cuda.synchronize()
     # ---- whole-layer throughput: back-to-back calls
     for s in range(warmup):
@@ -322,7 +325,8 @@ def time_config(layer, shape, wl, M, steps, warmup, graph=False):
     f13, f2 = flops_per_row(shape)
     st_ms = stage.mean(axis=0)
     tt = np.array(touched[warmup:], dtype=np.float64)
-    rows = M * shape.top_k + (M if shape.shared else 0)
+    # routed rows computed here (an expert-parallel shard computes only its own)
+    rows = float(np.mean(local_rows[warmup:]))
     alg_bytes = tt * (b13 + b2) + M * shape.H * 2 + M * shape.E * 4 + M * shape.H * 2
     gu_bytes = tt * b13 + M * shape.H * 2
     dn_bytes = tt * b2 + M * shape.H * 2
@@ -426,10 +430,12 @@ def main():
     max_rows = max(m for _, m in configs)
     layers = {}
     for shp in shapes:
-        assert (shp.E, shp.H, shp.I, shp.top_k) == (base.E, base.H, base.I, base.top_k)
+        assert (shp.E, shp.H, shp.I, shp.top_k, shp.local_first, shp.local_count) == \
+            (base.E, base.H, base.I, base.top_k, base.local_first, base.local_count)
         layers[shp.shared] = Layer(E=shp.E, H=shp.H, I=shp.I, top_k=shp.top_k, max_rows=max_rows,
                                    w13=w["w13"], s13=w["s13"], w2=w["w2"], s2=w["s2"],
-                                   shared=shared if shp.shared else None)
+                                   shared=shared if shp.shared else None, local_first=shp.local_first,
+                                   local_count=shp.local_count)
     # warm the GPU up to its steady clocks before anything is timed: a few
     # calls of the largest configuration
     wl0, m0 = max(configs, key=lambda c: c[1])

@@ -116,6 +116,17 @@ typedef struct {
   const uint16_t* shared_s13;
   const uint8_t* shared_w2;
   const uint16_t* shared_s2;
+  /* Expert-parallel shard ("The MoE Throughput Lever ...", section "The
+     Architectural Implication: Refining the Engine Design": experts sharded
+     over GPUs): the handle holds and computes only experts local_first ..
+     local_first + local_count - 1 of the E it routes over; w13/s13/w2/s2
+     then hold local_count experts (local expert 0 = expert local_first).
+     Routing ranks all E logits; slots routed to other experts are skipped,
+     so out is this shard's partial sum over the token's local slots (plus
+     the shared expert, if configured); the shards' outputs add up to the
+     whole layer's.  local_count = 0: all E experts are local. */
+  int32_t local_first;
+  int32_t local_count;
 } qmoe_layer_desc;
 
 typedef struct qmoe_layer qmoe_layer;
@@ -202,9 +213,11 @@ int qmoe_combine(qmoe_layer* layer, int64_t M, void* out, void* workspace, size_
 
 /* Copy the routing results of the last qmoe_route/qmoe_forward on this
    workspace into caller buffers (device pointers; any may be NULL):
-   ids int32 [M,k], w fp32 [M,k], counts int32 [E], offsets int32 [E+1],
+   ids int32 [M,k], w fp32 [M,k], counts int32 [L], offsets int32 [L+1],
    perm int32 [M*k] (perm[pos] = t*k+j, experts in order, tokens ascending
-   within an expert). */
+   within an expert), L = the local experts (E unless the layer is an
+   expert-parallel shard; then only the first offsets[L] entries of perm are
+   this shard's). */
 int qmoe_read_routing(qmoe_layer* layer, int64_t M, const void* workspace, size_t ws_bytes,
                       int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
                       int32_t* perm, void* stream);

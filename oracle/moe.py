@@ -203,7 +203,7 @@ def combine(w_row: np.ndarray, y_rows, shared_row=None) -> np.ndarray:
 
 
 def forward(x_bits: np.ndarray, logits: np.ndarray, k: int, get_expert, I: int,
-            shared=None, tokens=None, return_h: bool = False) -> dict:
+            shared=None, tokens=None, return_h: bool = False, local=None) -> dict:
     """The layer: out[t] = sum_j w[t,j] * MLP_{ids[t,j]}(x[t]) (+ shared
     expert), float64.
 
@@ -212,7 +212,13 @@ def forward(x_bits: np.ndarray, logits: np.ndarray, k: int, get_expert, I: int,
     the output only for `tokens` (default: all), which is exact because each
     output row depends only on its own token.  With return_h, h is returned
     per routed slot of the computed tokens (dict slot -> h row) for
-    debugging."""
+    debugging.
+
+    local = (first, count): one expert-parallel shard ("The MoE Throughput
+    Lever ...", section "The Architectural Implication: Refining the Engine
+    Design"): routing over all experts as above, but the sum takes only the
+    slots routed to experts first .. first + count - 1 (the shard's partial
+    output; the shards' outputs add up to the whole layer's)."""
     xf = decode_bf16(x_bits)
     M, H = xf.shape
     r = route(logits, k)
@@ -221,10 +227,13 @@ def forward(x_bits: np.ndarray, logits: np.ndarray, k: int, get_expert, I: int,
     Y = {}  # (t, j) -> y row
     Hs = {}
     # group the requested pairs by expert so each expert is decoded once
+    lo, hi = (0, logits.shape[1]) if local is None else (local[0], local[0] + local[1])
+    mine = lambda e: lo <= e < hi
     by_e = {}
     for t in sel:
         for j in range(k):
-            by_e.setdefault(int(ids[t, j]), []).append((int(t), j))
+            if mine(int(ids[t, j])):
+                by_e.setdefault(int(ids[t, j]), []).append((int(t), j))
     for e in sorted(by_e):
         pairs = by_e[e]
         X = xf[[t for t, _ in pairs]]
@@ -237,7 +246,11 @@ def forward(x_bits: np.ndarray, logits: np.ndarray, k: int, get_expert, I: int,
     Ys = expert_mlp(xf[sel], shared, I) if shared is not None and sel.size else None
     res = np.zeros((sel.size, H), dtype=np.float64)
     for n, t in enumerate(sel):
-        res[n] = combine(w[t], [Y[(int(t), j)] for j in range(k)], None if Ys is None else Ys[n])
+        js = [j for j in range(k) if mine(int(ids[t, j]))]
+        if js:
+            res[n] = combine(w[t][js], [Y[(int(t), j)] for j in js], None if Ys is None else Ys[n])
+        elif Ys is not None:
+            res[n] = Ys[n]
     r.update({"out": res, "tokens": sel})
     if return_h:
         r["h"] = Hs

@@ -35,6 +35,7 @@ class LayerDesc(ctypes.Structure):
         ("w2", ctypes.c_void_p), ("s2", ctypes.c_void_p),
         ("shared_w13", ctypes.c_void_p), ("shared_s13", ctypes.c_void_p),
         ("shared_w2", ctypes.c_void_p), ("shared_s2", ctypes.c_void_p),
+        ("local_first", ctypes.c_int32), ("local_count", ctypes.c_int32),
     ]
 
 

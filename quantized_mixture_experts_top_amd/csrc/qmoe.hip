@@ -82,6 +82,7 @@ struct RouteArgs {
   int* xexp;   // [M] per-token exponent
   int* tickets;    // the GEMV split-K tickets, cleared here for the call
   int n_tickets;
+  int lo, nloc;    // local experts [lo, lo + nloc) (an expert-parallel shard; else 0, E)
 };
 
 constexpr int kRouteThreads = 1024;  // routing blocks: up to 16 waves
@@ -99,7 +100,7 @@ constexpr int kRouteWaves = kRouteThreads / 64;  // also token rows per conversi
 // first items: its tiles are the longest of a call and should not be the
 // last to start.
 __device__ void route_items(const RouteArgs& a, int* s_cnt, int* s_off, bool write) {
-  const int tid = threadIdx.x, E = a.E, n = E + 1, bmc = a.bmc;
+  const int tid = threadIdx.x, E = a.nloc, n = E + 1, bmc = a.bmc;  // over the local experts
   if (tid == 0) s_cnt[E] = a.S;  // the shared expert takes every token
   __syncthreads();
   if (tid < 64) {
@@ -256,19 +257,25 @@ __global__ __launch_bounds__(kRouteThreads) void route_single_kernel(RouteArgs a
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += nthr) s_cnt[e] = __popc(cm[e][0]) + __popc(cm[e][1]);
+  for (int le = tid; le < a.nloc; le += nthr) s_cnt[le] = __popc(cm[a.lo + le][0]) + __popc(cm[a.lo + le][1]);
   route_items(a, s_cnt, s_off, true);
   // slot (t, j): its expert's offset plus the number of lower tokens routed
-  // to that expert (each token selects an expert at most once)
+  // to that expert (each token selects an expert at most once); slots of
+  // experts that are not local get no position
   for (int f = tid; f < a.M * k; f += nthr) {
-    const int t = f / k, e = s_ids[f];
+    const int t = f / k, e = s_ids[f], le = e - a.lo;
+    if (le < 0 || le >= a.nloc) {
+      a.inv_perm[f] = -1;
+      continue;
+    }
     const unsigned long long m = (unsigned long long)cm[e][0] | ((unsigned long long)cm[e][1] << 32);
-    const int pos = s_off[e] + __popcll(m & ((1ull << t) - 1ull));
+    const int pos = s_off[le] + __popcll(m & ((1ull << t) - 1ull));
     a.perm[pos] = f;
     a.inv_perm[f] = pos;
   }
+  // the shared expert's rows follow the routed ones: slot T + t
   const int T = a.M * k;
-  for (int t = tid; t < a.S; t += nthr) a.perm[T + t] = T + t;
+  for (int t = tid; t < a.S; t += nthr) a.perm[s_off[a.nloc] + t] = T + t;
 }
 
 // Calls of more than 64 tokens, first of two kernels: one wave per token
@@ -309,7 +316,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_finish_kernel(RouteArgs a
   const int tid = threadIdx.x, E = a.E, k = a.k, c = blockIdx.x;
   const int t0 = c * kChunk, rows = min(kChunk, a.M - t0);
   for (int i = c * kRouteThreads + tid; i < a.n_tickets; i += (int)gridDim.x * kRouteThreads) a.tickets[i] = 0;
-  for (int e = tid; e < E; e += kRouteThreads) {
+  const int lo = a.lo, nloc = a.nloc;  // local experts (indices below are local)
+  for (int e = tid; e < nloc; e += kRouteThreads) {
     s_cnt[e] = 0;
     s_before[e] = 0;
     cm[e][0] = cm[e][1] = 0u;
@@ -327,26 +335,30 @@ __global__ __launch_bounds__(kRouteThreads) void route_finish_kernel(RouteArgs a
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int f = f0 + u * kRouteThreads + tid;
-      if (e[u] < 0 || e[u] >= E) continue;  // ids come from the workspace: skip any out of range
-      atomicAdd(&s_cnt[e[u]], 1);
-      if (f < before) atomicAdd(&s_before[e[u]], 1);
+      const int le = e[u] - lo;
+      if (e[u] < 0 || e[u] >= E || le < 0 || le >= nloc) continue;  // not local (or out of range)
+      atomicAdd(&s_cnt[le], 1);
+      if (f < before) atomicAdd(&s_before[le], 1);
       else if (f < before + rows * k) {
         const int tl = f / k - t0;
-        atomicOr(&cm[e[u]][tl >> 5], 1u << (tl & 31));
+        atomicOr(&cm[le][tl >> 5], 1u << (tl & 31));
       }
     }
   }
   __syncthreads();
   route_items(a, s_cnt, s_off, c == 0);
   for (int f = before + tid; f < before + rows * k; f += kRouteThreads) {
-    const int tl = f / k - t0, e = ids[f];
-    if (e < 0 || e >= E) continue;
-    const unsigned long long m = (unsigned long long)cm[e][0] | ((unsigned long long)cm[e][1] << 32);
-    const int pos = s_off[e] + s_before[e] + __popcll(m & ((1ull << tl) - 1ull));
+    const int tl = f / k - t0, le = ids[f] - lo;
+    if (le < 0 || le >= nloc) {
+      a.inv_perm[f] = -1;
+      continue;
+    }
+    const unsigned long long m = (unsigned long long)cm[le][0] | ((unsigned long long)cm[le][1] << 32);
+    const int pos = s_off[le] + s_before[le] + __popcll(m & ((1ull << tl) - 1ull));
     a.perm[pos] = f;
     a.inv_perm[f] = pos;
   }
-  for (int t = t0 + tid; t < t0 + rows && t < a.S; t += kRouteThreads) a.perm[T + t] = T + t;
+  for (int t = t0 + tid; t < t0 + rows && t < a.S; t += kRouteThreads) a.perm[s_off[nloc] + t] = T + t;
 }
 
 // ------------------------------------------------------------------ GEMMs
@@ -1300,9 +1312,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kGemvW
 // summed in fp32 from the bf16 slot rows and rounded to bf16.  One thread
 // per 4 consecutive columns; the k slots are loaded in batches of 8 before
 // they are summed, so a thread waits for one round trip per batch rather
-// than one per slot.
-__global__ __launch_bounds__(kThreads) void combine_kernel(const uint2* y, uint2* out, int M, int H,
-                                                            int k, int T, int S) {
+// than one per slot.  SHARD: an expert-parallel shard, whose slots routed
+// to experts outside [lo, lo + nloc) have no rows and are skipped.
+template <bool SHARD>
+__global__ __launch_bounds__(kThreads) void combine_kernel(const uint2* y, uint2* out, int M, int H, int k,
+                                                            int T, int S, const int* ids, int lo, int nloc) {
   const long long q = (long long)blockIdx.x * kThreads + threadIdx.x;
   const int per_row = H / 4;
   if (q >= (long long)M * per_row) return;
@@ -1313,15 +1327,21 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint2* y, uint2
   const int n = k + (S ? 1 : 0);  // slot rows to add, the shared expert last
   for (int j0 = 0; j0 < n; j0 += 8) {
     uint2 v[8];
+    bool use[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int j = j0 + u;
+      use[u] = j < n;
+      if (SHARD && j < k) {
+        const int le = ids[(size_t)t * k + j] - lo;
+        use[u] = le >= 0 && le < nloc;
+      }
       const size_t r = j < k ? (size_t)t * k + j : (size_t)T + t;
-      v[u] = j < n ? base[r * row4] : make_uint2(0u, 0u);
+      v[u] = use[u] ? base[r * row4] : make_uint2(0u, 0u);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      if (j0 + u < n) {
+      if (use[u]) {
         acc.x += __uint_as_float(v[u].x << 16);
         acc.y += __uint_as_float(v[u].x & 0xFFFF0000u);
         acc.z += __uint_as_float(v[u].y << 16);
@@ -1589,6 +1609,7 @@ struct qmoe_layer {
   qmoe_layer_desc d;
   int device = 0;
   bool shared = false;
+  int lo = 0, nloc = 0;     // local experts [lo, lo + nloc) (all E unless a shard)
   void* scratch = nullptr;  // device address of this device's scratch array
   std::mutex receipt_mu;
   qmoe_receipt last{};      // receipt of the last completed forward call
@@ -1611,7 +1632,7 @@ Layout make_layout(const qmoe_layer* L, int64_t M) {
   l.S = L->shared ? M : 0;
   l.R = l.T + l.S;
   l.C = ceil_div(M, kChunk);
-  l.max_items_all = max_items_for(l.T, M, l.S, E, kGemvRows);  // the smallest row tile bounds all
+  l.max_items_all = max_items_for(l.T, M, l.S, L->nloc, kGemvRows);  // the smallest row tile bounds all
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -1621,8 +1642,8 @@ Layout make_layout(const qmoe_layer* L, int64_t M) {
   l.ctrl = take(kCtrlWords * 4);
   l.ids = take(l.T * 4);
   l.wts = take(l.T * 4);
-  l.counts = take((E + 1) * 4);
-  l.offsets = take((E + 2) * 4);
+  l.counts = take((L->nloc + 1) * 4);
+  l.offsets = take((L->nloc + 2) * 4);
   l.perm = take(l.R * 4);
   l.inv_perm = take(l.T * 4);
   l.items = take(l.max_items_all * 16);
@@ -1676,7 +1697,7 @@ constexpr int kSplitMaxTiles = 128;
 constexpr int kSplitTargetBlocks = 512;
 int gemv_splits(const qmoe_layer* L, int64_t M, bool gateup, int64_t* tiles) {
   const int64_t T = M * L->d.top_k, S = L->shared ? M : 0;
-  const int64_t max_items = max_items_for(T, M, S, L->d.E, kGemvRows);
+  const int64_t max_items = max_items_for(T, M, S, L->nloc, kGemvRows);
   const int64_t N = gateup ? L->d.I : L->d.H;
   const int64_t nblk = ceil_div(N, (kThreads / 64) * (gateup ? 16 : 32));
   *tiles = max_items * nblk;
@@ -1746,7 +1767,9 @@ int do_route(qmoe_layer* L, const void* x, const float* logits, int64_t M, void*
   a.S = (int)lay.S;
   a.C = (int)lay.C;
   a.bmc = bmc;
-  a.max_items = (int)max_items_for(lay.T, M, lay.S, L->d.E, bmc);
+  a.max_items = (int)max_items_for(lay.T, M, lay.S, L->nloc, bmc);
+  a.lo = L->lo;
+  a.nloc = L->nloc;
   a.ctrl = at<int>(ws, lay.ctrl);
   a.ids = at<int>(ws, lay.ids);
   a.wts = at<float>(ws, lay.wts);
@@ -1793,8 +1816,8 @@ int do_route(qmoe_layer* L, const void* x, const float* logits, int64_t M, void*
 
 template <bool GATEUP>
 void fill_gemm_args(const qmoe_layer* L, int64_t M, void* ws, const Layout& lay, GemmArgs& g) {
-  const int E = L->d.E, H = L->d.H, I = L->d.I;
-  g.E = E;
+  const int H = L->d.H, I = L->d.I;
+  g.E = L->nloc;  // the weights hold the local experts
   g.T = (int)lay.T;
   g.M = (int)M;
   g.R = (int)lay.R;
@@ -1838,9 +1861,8 @@ template <int MB, int WN, int NBW, bool GATEUP>
 int launch_gemm(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t st) {
   GemmArgs g;
   fill_gemm_args<GATEUP>(L, M, ws, lay, g);
-  const int E = L->d.E;
   const int bmc = MB * 16;
-  g.max_items = (int)max_items_for(lay.T, M, lay.S, E, bmc);
+  g.max_items = (int)max_items_for(lay.T, M, lay.S, L->nloc, bmc);
   g.nblk = (int)ceil_div(g.N, WN * NBW * 16);
   const int64_t blocks = 8 * (int64_t)g.nblk * ceil_div(g.max_items, 8);
   if (blocks > 0x7FFFFFFF) return fail(QMOE_ERR_UNSUPPORTED, "grid too large");
@@ -1858,7 +1880,7 @@ int launch_gemv(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream
   constexpr int WN = kThreads / 64;
   GemmArgs g;
   fill_gemm_args<GATEUP>(L, M, ws, lay, g);
-  g.max_items = (int)max_items_for(lay.T, M, lay.S, L->d.E, kGemvRows);
+  g.max_items = (int)max_items_for(lay.T, M, lay.S, L->nloc, kGemvRows);
   const int cols = GATEUP ? 16 : 32;  // output columns per wave
   g.nblk = (int)ceil_div(g.N, WN * cols);
   g.splits = GATEUP ? lay.splits_gu : lay.splits_dn;
@@ -1904,8 +1926,14 @@ int do_combine(qmoe_layer* L, int64_t M, void* out, void* ws, const Layout& lay,
   if (!aligned16(out)) return fail(QMOE_ERR_ARG, "out must be 16-byte aligned");
   const int64_t n = M * (L->d.H / 4);
   if (t_rc) t_rc->combine_blocks = ceil_div(n, kThreads);
-  combine_kernel<<<dim3((unsigned)ceil_div(n, kThreads)), kThreads, 0, st>>>(
-      at<uint2>(ws, lay.y), static_cast<uint2*>(out), (int)M, L->d.H, L->d.top_k, (int)lay.T, (int)lay.S);
+  const dim3 grid((unsigned)ceil_div(n, kThreads));
+  if (L->nloc < L->d.E)
+    combine_kernel<true><<<grid, kThreads, 0, st>>>(at<uint2>(ws, lay.y), static_cast<uint2*>(out), (int)M, L->d.H,
+                                                    L->d.top_k, (int)lay.T, (int)lay.S, at<int>(ws, lay.ids), L->lo,
+                                                    L->nloc);
+  else
+    combine_kernel<false><<<grid, kThreads, 0, st>>>(at<uint2>(ws, lay.y), static_cast<uint2*>(out), (int)M, L->d.H,
+                                                     L->d.top_k, (int)lay.T, (int)lay.S, nullptr, 0, L->nloc);
   return check_launch(L, "combine_kernel");
 }
 
@@ -1966,6 +1994,9 @@ int qmoe_layer_create(const qmoe_layer_desc* d, qmoe_layer** out) {
   if (nsh != 0 && nsh != 4) return fail(QMOE_ERR_ARG, "shared expert: set all four pointers or none");
   if (!aligned16(d->w13) || !aligned16(d->w2) || (nsh && (!aligned16(d->shared_w13) || !aligned16(d->shared_w2))))
     return fail(QMOE_ERR_ARG, "weight code arrays must be 16-byte aligned");
+  if (d->local_count < 0 || d->local_count > d->E || d->local_first < 0 ||
+      (d->local_count > 0 && d->local_first > d->E - d->local_count))
+    return fail(QMOE_ERR_ARG, "local experts [local_first, local_first + local_count) must lie in [0, E)");
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return fail(QMOE_ERR_DEVICE, "no HIP device (hipGetDevice failed)");
   hipDeviceProp_t prop;
@@ -1981,6 +2012,8 @@ int qmoe_layer_create(const qmoe_layer_desc* d, qmoe_layer** out) {
   L->device = dev;
   L->shared = nsh == 4;
   L->scratch = sp;
+  L->lo = d->local_count ? d->local_first : 0;
+  L->nloc = d->local_count ? d->local_count : d->E;
   *out = L;
   return QMOE_OK;
 }
@@ -2141,8 +2174,8 @@ int qmoe_read_routing(qmoe_layer* L, int64_t M, const void* ws, size_t ws_bytes,
     size_t off, bytes;
   } cps[] = {{ids, lay.ids, (size_t)lay.T * 4},
              {w, lay.wts, (size_t)lay.T * 4},
-             {counts, lay.counts, (size_t)L->d.E * 4},
-             {offsets, lay.offsets, (size_t)(L->d.E + 1) * 4},
+             {counts, lay.counts, (size_t)L->nloc * 4},
+             {offsets, lay.offsets, (size_t)(L->nloc + 1) * 4},
              {perm, lay.perm, (size_t)lay.T * 4}};
   for (const Cp& c : cps) {
     if (!c.dst) continue;
@@ -2178,7 +2211,7 @@ int qmoe_read_intermediate(qmoe_layer* L, int64_t M, const void* ws, size_t ws_b
 int qmoe_dequant_debug(qmoe_layer* L, int32_t expert, int32_t which, uint16_t* out, void* stream) {
   if (!L) return fail(QMOE_ERR_ARG, "layer is NULL");
   if (!out) return fail(QMOE_ERR_ARG, "out is NULL");
-  if (expert < 0 || expert > L->d.E || (expert == L->d.E && !L->shared))
+  if (expert < 0 || expert > L->nloc || (expert == L->nloc && !L->shared))
     return fail(QMOE_ERR_ARG, "expert out of range");
   if (which != 0 && which != 1) return fail(QMOE_ERR_ARG, "which must be 0 (w13) or 1 (w2)");
   const int64_t H = L->d.H, I = L->d.I;
@@ -2186,7 +2219,7 @@ int qmoe_dequant_debug(qmoe_layer* L, int32_t expert, int32_t which, uint16_t* o
   const int K = which == 0 ? (int)H : (int)I;
   const uint8_t* w;
   const uint16_t* s;
-  if (expert < L->d.E) {
+  if (expert < L->nloc) {
     w = (which == 0 ? L->d.w13 : L->d.w2) + (size_t)expert * N * (K / 2);
     s = (which == 0 ? L->d.s13 : L->d.s2) + (size_t)expert * N * (K / 32);
   } else {

@@ -35,10 +35,14 @@ class Layer:
 
     w13 uint8 [E,2I,H/2], s13 fp16-bits (int16/uint16/float16) [E,2I,H/32],
     w2 uint8 [E,H,I/2], s2 [E,H,I/32]; `shared` an optional dict with the
-    same four keys for one always-selected shared expert.  The layer keeps
+    same four keys for one always-selected shared expert.  An expert-parallel
+    shard routes over E experts but holds and computes only experts
+    local_first .. local_first + local_count - 1 (the weight tensors then
+    have local_count experts) and returns its partial sum.  The layer keeps
     references to the tensors (the library borrows their memory)."""
 
-    def __init__(self, *, E, H, I, top_k, max_rows, w13, s13, w2, s2, shared=None):
+    def __init__(self, *, E, H, I, top_k, max_rows, w13, s13, w2, s2, shared=None, local_first=0,
+                 local_count=0):
         self.lib = load_library()
         self.E, self.H, self.I, self.top_k, self.max_rows = E, H, I, top_k, max_rows
         self._keep = [w13, s13, w2, s2]
@@ -47,7 +51,9 @@ class Layer:
             self._keep += [sh["w13"], sh["s13"], sh["w2"], sh["s2"]]
         self.has_shared = bool(shared)
         desc = LayerDesc(E, H, I, top_k, GROUP, max_rows, _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2),
-                         _ptr(sh.get("w13")), _ptr(sh.get("s13")), _ptr(sh.get("w2")), _ptr(sh.get("s2")))
+                         _ptr(sh.get("w13")), _ptr(sh.get("s13")), _ptr(sh.get("w2")), _ptr(sh.get("s2")),
+                         local_first, local_count)
+        self.local_first, self.local_count = local_first, (local_count or E)
         handle = ctypes.c_void_p()
         check(self.lib.qmoe_layer_create(ctypes.byref(desc), ctypes.byref(handle)))
         self.handle = handle
@@ -165,8 +171,8 @@ class Layer:
         r = {
             "ids": torch.empty((M, k), dtype=torch.int32, device=dev),
             "w": torch.empty((M, k), dtype=torch.float32, device=dev),
-            "counts": torch.empty((E,), dtype=torch.int32, device=dev),
-            "offsets": torch.empty((E + 1,), dtype=torch.int32, device=dev),
+            "counts": torch.empty((self.local_count,), dtype=torch.int32, device=dev),
+            "offsets": torch.empty((self.local_count + 1,), dtype=torch.int32, device=dev),
             "perm": torch.empty((M * k,), dtype=torch.int32, device=dev),
         }
         ws, nb, st = self._args(M, stream)
@@ -210,7 +216,8 @@ class Layer:
         check(self.lib.qmoe_reset_stats(self.handle))
 
 
-def layer_from_numpy(weights: dict, *, E, H, I, top_k, max_rows, device="cuda") -> Layer:
+def layer_from_numpy(weights: dict, *, E, H, I, top_k, max_rows, device="cuda", local_first=0,
+                     local_count=0) -> Layer:
     """Copy numpy weights (as produced by the seeded generators) to the GPU
     and create a Layer over them."""
     def dev(a):
@@ -222,4 +229,5 @@ def layer_from_numpy(weights: dict, *, E, H, I, top_k, max_rows, device="cuda") 
         shared = {k: dev(weights["shared_" + k]) for k in ("w13", "s13", "w2", "s2")}
     return Layer(E=E, H=H, I=I, top_k=top_k, max_rows=max_rows,
                  w13=dev(weights["w13"]), s13=dev(weights["s13"]),
-                 w2=dev(weights["w2"]), s2=dev(weights["s2"]), shared=shared)
+                 w2=dev(weights["w2"]), s2=dev(weights["s2"]), shared=shared, local_first=local_first,
+                 local_count=local_count)

@@ -49,6 +49,13 @@ class LayerShape:
     I: int
     top_k: int
     shared: bool = False
+    # expert-parallel shard: local experts [local_first, local_first + local_count)
+    # of the E routed over (0 = all E)
+    local_first: int = 0
+    local_count: int = 0
+
+    def local_experts(self) -> range:
+        return range(self.local_first, self.local_first + (self.local_count or self.E))
 
     def expert_bytes(self) -> int:
         """Packed code bytes plus fp16 scale bytes of one expert."""
@@ -71,6 +78,9 @@ FULL_SHARED = LayerShape(E=384, H=7168, I=2048, top_k=8, shared=True)
 # one GPU's share of the same layer under 8-way tensor parallelism over I:
 # every expert, an eighth of its intermediate width
 TP8_SLICE = LayerShape(E=384, H=7168, I=256, top_k=8)
+# one GPU's share under 8-way expert parallelism: routes over all 384
+# experts, holds and computes experts 0..47
+EP48_SLICE = LayerShape(E=384, H=7168, I=2048, top_k=8, local_first=0, local_count=48)
 
 WORKLOADS = {
     "tiny": Workload("tiny", TINY, (16,)),
@@ -79,6 +89,7 @@ WORKLOADS = {
     "plateau": Workload("plateau", FULL, (1024, 4096)),
     "skew": Workload("skew", FULL_SHARED, (512,), skew=True),
     "tp8": Workload("tp8", TP8_SLICE, (1, 9, 256, 4096)),
+    "ep48": Workload("ep48", EP48_SLICE, (1, 9, 256, 4096)),
 }
 
 
@@ -192,7 +203,7 @@ def inputs(seed: int, shape: LayerShape, M: int, skew: bool = False, logits_seed
 
 
 __all__ = [
-    "GROUP", "LayerShape", "Workload", "WORKLOADS", "TINY", "FULL", "FULL_SHARED", "TP8_SLICE",
+    "GROUP", "LayerShape", "Workload", "WORKLOADS", "TINY", "FULL", "FULL_SHARED", "TP8_SLICE", "EP48_SLICE",
     "f32_to_bf16_bits", "hidden", "logits", "zipf_bias", "expert", "all_experts",
     "inputs", "expected_touched", "router_weights",
 ]

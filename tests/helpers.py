@@ -73,7 +73,9 @@ def upload_full(seed: int, shape: synth.LayerShape, threads: int = 16, chunk: in
     """Generate the full layer's weights straight into device tensors, a
     chunk of experts at a time (bounded host memory)."""
     import torch
-    E, H, I = shape.E, shape.H, shape.I
+    H, I = shape.H, shape.I
+    experts = list(shape.local_experts())  # an expert-parallel shard holds its own only
+    E = len(experts)
     out = {
         "w13": torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device="cuda"),
         "s13": torch.empty((E, 2 * I, H // 32), dtype=torch.int16, device="cuda"),
@@ -82,7 +84,7 @@ def upload_full(seed: int, shape: synth.LayerShape, threads: int = 16, chunk: in
     }
     with ThreadPoolExecutor(threads) as ex:
         for e0 in range(0, E, chunk):
-            es = list(range(e0, min(E, e0 + chunk)))
+            es = [experts[i] for i in range(e0, min(E, e0 + chunk))]
             ws = list(ex.map(lambda e: synth.expert(seed, shape, e), es))
             for key in out:
                 a = np.stack([w[key] for w in ws])

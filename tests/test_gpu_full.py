@@ -67,6 +67,8 @@ class _Reference:
 
     def __init__(self, shape, cases, salt, threads=16):
         self.shape, self.cases = shape, {}
+        local = set(shape.local_experts())  # an expert-parallel shard sums its own slots only
+        self.local = local
         k, I = shape.top_k, shape.I
         rows = {}  # expert -> list of (case key, token)
         for key, (wl_name, M, n) in cases.items():
@@ -78,7 +80,8 @@ class _Reference:
                                "xf": oracle_moe.decode_bf16(inp["x"])}
             for t in tokens:
                 for j in range(k):
-                    rows.setdefault(int(r["ids"][t, j]), []).append((key, int(t)))
+                    if int(r["ids"][t, j]) in local:
+                        rows.setdefault(int(r["ids"][t, j]), []).append((key, int(t)))
                 if wl.shape.shared:
                     rows.setdefault("shared", []).append((key, int(t)))
         say(f"oracle: {len(rows)} expert MLPs over {sum(len(v) for v in rows.values())} sampled rows")
@@ -102,9 +105,13 @@ class _Reference:
         r, k = c["route"], self.shape.top_k
         res = []
         for t in c["tokens"]:
-            ys = [self.y[(key, int(t), int(r["ids"][t, j]))] for j in range(k)]
+            js = [j for j in range(k) if int(r["ids"][t, j]) in self.local]
+            ys = [self.y[(key, int(t), int(r["ids"][t, j]))] for j in js]
             sh = self.y[(key, int(t), "shared")] if c["shared"] else None
-            res.append(oracle_moe.combine(r["w"][t], ys, sh))
+            if js:
+                res.append(oracle_moe.combine(r["w"][t][js], ys, sh))
+            else:
+                res.append(sh if sh is not None else np.zeros(self.shape.H))
         return np.stack(res)
 
 
@@ -182,4 +189,49 @@ def test_tp8_slice_parity(tp8, tp8_ref, M, nsample):
     tokens = c["tokens"]
     err = rel_err(out[tokens], tp8_ref.out(key))
     say(f"  {tokens.size} tokens; {_coverage(c['route'], tokens, shape.top_k, shape.E, M)}; rel err {err:.3e}")
+    assert err <= REL_TOL
+
+
+EP48_CASES = [(1, None), (9, None), (256, 64), (4096, 256)]
+
+
+@pytest.fixture(scope="module")
+def ep48():
+    """One GPU's share under 8-way expert parallelism: experts 0..47 of the
+    384 the layer routes over (synthetic weights, the same as the whole
+    layer's experts 0..47)."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from quantized_mixture_experts_top_amd import Layer
+    shape = synth.EP48_SLICE
+    say("uploading the expert-parallel shard (experts 0..47 of 384, seed 0)")
+    r = upload_full(SEED, shape)["routed"]
+    layer = Layer(E=shape.E, H=shape.H, I=shape.I, top_k=shape.top_k, max_rows=4096, w13=r["w13"], s13=r["s13"],
+                  w2=r["w2"], s2=r["s2"], local_first=shape.local_first, local_count=shape.local_count)
+    yield layer
+    layer.close()
+
+
+@pytest.fixture(scope="module")
+def ep48_ref():
+    return _Reference(synth.EP48_SLICE, {f"ep48:{M}": ("ep48", M, n) for M, n in EP48_CASES}, salt=3000)
+
+
+@pytest.mark.parametrize("M,nsample", EP48_CASES)
+def test_ep48_shard_parity(ep48, ep48_ref, M, nsample):
+    shape = synth.EP48_SLICE
+    key = f"ep48:{M}"
+    c = ep48_ref.cases[key]
+    say(f"ep48 shard M={M}")
+    out = ep48.forward(dev_bf16(c["inp"]["x"]), dev(c["inp"]["logits"])).float().cpu().numpy()
+    r = c["route"]
+    rt = ep48.read_routing(M)
+    assert np.array_equal(rt["ids"].cpu().numpy(), r["ids"])
+    assert np.array_equal(rt["counts"].cpu().numpy(), r["counts"][:48])
+    n_loc = int(r["counts"][:48].sum())
+    assert np.array_equal(rt["perm"].cpu().numpy()[:n_loc], r["perm"][:n_loc])
+    tokens = c["tokens"]
+    err = rel_err(out[tokens], ep48_ref.out(key))
+    say(f"  {tokens.size} tokens, {n_loc} of {M * 8} routed slots local; rel err {err:.3e}")
     assert err <= REL_TOL

@@ -626,3 +626,46 @@ def test_gemv_split_k(E, H, I, k, M, shared):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(g_out.view(torch.int16), out.view(torch.int16)), f"replay {rep}"
+
+
+# ------------------------------------------------------ expert-parallel shard
+
+
+@pytest.mark.parametrize("M", [3, 24, 130])  # GEMV items; tiles; tiles with two routing kernels
+@pytest.mark.parametrize("shared", [False, True])
+def test_expert_parallel_shards(M, shared):
+    """Four shards of four experts each route over all 16 experts and compute
+    their own: each shard's output, counts and offsets against the oracle's
+    shard, and the four outputs against the whole layer (the shared expert,
+    when there is one, held by shard 0 only, as it would be computed once)."""
+    import torch
+    E, H, I, k = 16, 512, 256, 4
+    shape = synth.LayerShape(E=E, H=H, I=I, top_k=k, shared=shared)
+    w = synth.all_experts(71, shape)
+    x, lg = synth.hidden(72, M, H), synth.logits(73, M, E)
+    get, sh = expert_getter(w), shared_of(w)
+    full = oracle_moe.forward(x, lg, k, get, I, shared=sh)
+    total = np.zeros_like(full["out"])
+    for g in range(4):
+        lo = 4 * g
+        part = {key: w[key][lo:lo + 4] for key in ("w13", "s13", "w2", "s2")}
+        if shared and g == 0:
+            part.update({"shared_" + key: w["shared_" + key] for key in ("w13", "s13", "w2", "s2")})
+        from quantized_mixture_experts_top_amd import layer_from_numpy
+        layer = layer_from_numpy(part, E=E, H=H, I=I, top_k=k, max_rows=M, local_first=lo, local_count=4)
+        out = layer.forward(dev_bf16(x), dev(lg)).float().cpu().numpy()
+        ref = oracle_moe.forward(x, lg, k, get, I, shared=sh if g == 0 else None, local=(lo, 4))
+        rt = layer.read_routing(M)
+        assert np.array_equal(rt["ids"].cpu().numpy(), full["ids"])
+        assert np.array_equal(rt["counts"].cpu().numpy(), full["counts"][lo:lo + 4])
+        assert np.array_equal(rt["offsets"].cpu().numpy(), full["offsets"][lo:lo + 5] - full["offsets"][lo])
+        n_loc = int(full["counts"][lo:lo + 4].sum())
+        assert np.array_equal(rt["perm"].cpu().numpy()[:n_loc], full["perm"][full["offsets"][lo]:full["offsets"][lo + 4]])
+        err = rel_err(out, ref["out"])
+        say(f"shard [{lo}, {lo + 4}) M={M} shared={shared}: {n_loc} local slots, rel err {err:.3e}")
+        assert err <= REL_TOL
+        total += out
+        layer.close()
+    err = rel_err(total, full["out"])
+    say(f"  shards summed vs the whole layer: rel err {err:.3e}")
+    assert err <= REL_TOL

@@ -344,3 +344,50 @@ def test_router_weights_give_unit_scale_logits():
     wr = synth.router_weights(9, 128, 1024)
     lg = moe.router_logits(x, wr)
     assert 0.85 < lg.std() < 1.15
+
+
+# ------------------------------------------------------ expert-parallel shard
+
+
+def _shard_case(shared):
+    shape = synth.LayerShape(E=8, H=64, I=64, top_k=3, shared=shared)
+    w = synth.all_experts(3, shape)
+    get = lambda e: {k: w[k][e] for k in ("w13", "s13", "w2", "s2")}
+    sh = {k: w["shared_" + k] for k in ("w13", "s13", "w2", "s2")} if shared else None
+    x, lg = synth.hidden(4, 12, 64), synth.logits(5, 12, 8)
+    return x, lg, get, sh
+
+
+def test_shard_of_all_experts_is_the_layer():
+    x, lg, get, sh = _shard_case(True)
+    full = moe.forward(x, lg, 3, get, 64, shared=sh)["out"]
+    assert np.array_equal(moe.forward(x, lg, 3, get, 64, shared=sh, local=(0, 8))["out"], full)
+
+
+def test_shards_add_up_to_the_layer():
+    """Four shards of two experts each: their partial outputs add up to the
+    whole layer's (float64; only the order of the additions differs)."""
+    x, lg, get, _ = _shard_case(False)
+    full = moe.forward(x, lg, 3, get, 64)["out"]
+    parts = sum(moe.forward(x, lg, 3, get, 64, local=(2 * g, 2))["out"] for g in range(4))
+    assert np.allclose(parts, full, rtol=0, atol=1e-12 * np.max(np.abs(full)))
+    # against a direct restatement for one token and one shard: the slots
+    # whose expert is local, weighted and summed
+    r = moe.route(lg, 3)
+    xf = moe.decode_bf16(x)
+    t, lo = 5, 4
+    want = np.zeros(64)
+    for j in range(3):
+        e = int(r["ids"][t, j])
+        if lo <= e < lo + 2:
+            want += r["w"][t, j] * moe.expert_mlp(xf[t:t + 1], get(e), 64)[0]
+    got = moe.forward(x, lg, 3, get, 64, local=(lo, 2))["out"][t]
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_shard_without_routed_slots_is_the_shared_expert_alone():
+    x, lg, get, sh = _shard_case(True)
+    lg = lg.copy()
+    lg[:, 6:] = -50.0  # experts 6 and 7 never selected (top-3 of 8)
+    out = moe.forward(x, lg, 3, get, 64, shared=sh, local=(6, 2))["out"]
+    assert np.array_equal(out, moe.expert_mlp(moe.decode_bf16(x), sh, 64))
