@@ -419,6 +419,42 @@ __device__ __forceinline__ void transpose_scales(uint32_t lo, uint32_t hi, uint3
   swap32(d[0], d[2]);
   swap32(d[1], d[3]);
 }
+// The same transpose, kept two scales to a dword: c[0] holds the scales of
+// sub-steps 0 and 1 (low and high half), c[1] those of sub-steps 2 and 3.
+__device__ __forceinline__ void transpose_scales_c(uint32_t lo, uint32_t hi, uint32_t (&c)[2]) {
+  uint32_t d[4];
+  transpose_scales(lo, hi, d);
+  c[0] = __builtin_amdgcn_perm(d[1], d[0], 0x05040100u);
+  c[1] = __builtin_amdgcn_perm(d[3], d[2], 0x05040100u);
+}
+// The fp16 scale of sub-step u, in both halves of a dword: from the compact
+// form (two to a dword) or the plain one (one per dword, already doubled).
+__device__ __forceinline__ uint32_t scale_of(const uint32_t (&c)[2], int u) {
+  return __builtin_amdgcn_perm(c[u >> 1], c[u >> 1], (u & 1) ? 0x03020302u : 0x01000100u);
+}
+__device__ __forceinline__ uint32_t scale_of(const uint32_t (&c)[4], int u) { return c[u]; }
+__device__ __forceinline__ void transpose_scales_to(uint32_t lo, uint32_t hi, uint32_t (&c)[2]) {
+  transpose_scales_c(lo, hi, c);
+}
+__device__ __forceinline__ void transpose_scales_to(uint32_t lo, uint32_t hi, uint32_t (&d)[4]) {
+  transpose_scales(lo, hi, d);
+}
+// Lane (r, kq) holds 8 scales of its weight row, groups 8kq..8kq+7 of two
+// super-steps (w[0..3]); afterwards (lo0, hi0) holds groups 4kq..4kq+3 of
+// the first super-step and (lo1, hi1) those of the second, the layout one
+// 8-byte load per super-step gives.  Quarter k takes dwords 2(k&1) and
+// 2(k&1)+1 of quarter k/2 (first) or 2 + k/2 (second).
+__device__ __forceinline__ void split_scale_pair(const uint32_t (&w)[4], uint32_t& lo0, uint32_t& hi0, uint32_t& lo1,
+                                                 uint32_t& hi1) {
+  lo0 = w[0];
+  lo1 = w[2];
+  swap16(lo0, lo1);
+  swap32(lo0, lo1);
+  hi0 = w[1];
+  hi1 = w[3];
+  swap16(hi0, hi1);
+  swap32(hi0, hi1);
+}
 
 // Raw buffer resource over [base, base + bytes): loads take a 32-bit per-lane
 // offset and a scalar per-step offset, and read 0 past the end.
@@ -502,6 +538,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   // it rides in the scalar offset; the lane part alone is bounds-checked
   // and every in-range lane stays inside the weights)
   const uint32_t bl = (uint32_t)r * K2 + 16 * kq, sl = (uint32_t)r * KG * 2 + 8 * kq;
+  const uint32_t sl2 = (uint32_t)r * KG * 2 + 16 * kq;
   uint32_t brow[NBB];
   int col0[NBW];
 #pragma unroll
@@ -559,6 +596,23 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
       sc[b][1] = v[1];
     }
   };
+  // the scales of super-steps S and S + 1 (one 16-byte load per row, half
+  // the load instructions and, since the row's 128-byte line is then read
+  // in two visits instead of four, fewer re-reads of lines the weight stream
+  // has pushed out of L2): lane kq takes groups 8kq..8kq+7 of the 32.  Only
+  // the lane offset is range-checked, so a lane whose super-step is not a
+  // whole one of this row (kq >= 2 when S + 1 is past them) reads nothing.
+  auto load_sc2 = [&](int S, uint32_t (&sc)[NBB][4], bool ok) __attribute__((always_inline)) {
+    const bool in_row = ok && S + (kq >> 1) < S_end_full;
+#pragma unroll
+    for (int b = 0; b < NBB; ++b) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rS, in_row ? sl2 : kOob, S * 32 + brow[b] * KG * 2, 0);
+      sc[b][0] = v[0];
+      sc[b][1] = v[1];
+      sc[b][2] = v[2];
+      sc[b][3] = v[3];
+    }
+  };
   // token of tile row m (m < nr), from its sorted slot; -1 if the slot is
   // not one of the call's
   auto tok_of = [&](int slot) __attribute__((always_inline)) -> int {
@@ -588,7 +642,16 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   __shared__ __attribute__((aligned(16))) _Float16 lds_a0[MB * 4 * kBlkHalves];
   __shared__ __attribute__((aligned(16))) _Float16 lds_a1[MB * 4 * kBlkHalves];
 #define QMOE_LDS_A(BUF) ((BUF) ? lds_a1 : lds_a0)
-  uint32_t sc_cur[NBB][4], sc_nxt[NBB][2];  // this super-step's scales by sub-step; the next one's, raw
+  // Scales: this super-step's by sub-step (sc_cur), the next one's in load
+  // layout (sc_nxt).  Gate+up loads each row's scales two super-steps at a
+  // time (sc_pair, see load_sc2) and keeps sc_cur two to a dword, which pays
+  // for the pair's registers; on MI355X this took gate+up at 90-1024 tokens
+  // 3-5% faster and its L2 misses at 256 tokens from 8.2 to 7.1 GB per call.
+  // Down, whose super-steps move half the bytes through L2 and whose scale
+  // lines stay there, keeps one load per super-step (the pair measured
+  // slower there).
+  constexpr bool kPairSc = GATEUP;
+  uint32_t sc_cur[NBB][kPairSc ? 2 : 4], sc_nxt[NBB][2], sc_pair[NBB][4];
   Frag<NBB> fb0, fb1, fb2, fb3;  // the weights of sub-steps 0..3
   // Down: the first weights go out before the item's rows are looked up,
   // so the round trips of the lookups (sorted slot, routing weight) overlap
@@ -646,7 +709,17 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
       (r & 3) * kBlkHalves + 128 * (r >> 2) + 32 * ((kq + (r >> 2) + kSlotQ * ((r >> 2) + (r & 3))) & 3);
   auto promote_scales = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int b = 0; b < NBB; ++b) transpose_scales(sc_nxt[b][0], sc_nxt[b][1], sc_cur[b]);
+    for (int b = 0; b < NBB; ++b) transpose_scales_to(sc_nxt[b][0], sc_nxt[b][1], sc_cur[b]);
+  };
+  // the first of a pair of super-steps from sc_pair; the second one's scales
+  // wait in sc_nxt
+  auto promote_pair = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int b = 0; b < NBB; ++b) {
+      uint32_t lo0, hi0;
+      split_scale_pair(sc_pair[b], lo0, hi0, sc_nxt[b][0], sc_nxt[b][1]);
+      transpose_scales_to(lo0, hi0, sc_cur[b]);
+    }
   };
   // this wave's blocks of sub-step U of super-step S into buffer BUF, for
   // the NMBC row blocks in use (row block amb0 + MBS*t; a wave-uniform
@@ -664,7 +737,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
 #define QMOE_COMPUTE_AT(F, SC, U, BUF, SLOT0)                                                    \
   do {                                                                                           \
     uint32_t s2_[NBB];                                                                           \
-    _Pragma("unroll") for (int b = 0; b < NBB; ++b) s2_[b] = (SC)[b][(U)];                       \
+    _Pragma("unroll") for (int b = 0; b < NBB; ++b) s2_[b] = scale_of((SC)[b], (U));             \
     half8_t bfa_[NBB], bfb_[NBB];                                                                \
     _Pragma("unroll") for (int b = 0; b < NBB; ++b) bfa_[b] = dq8p(word((F).b[b], 0), s2_[b]);   \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                              \
@@ -695,7 +768,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
 #define QMOE_COMPUTE_IL(F, SC, U, BUF, SB, UB, FNN)                                               \
   do {                                                                                           \
     uint32_t s2_[NBB];                                                                           \
-    _Pragma("unroll") for (int b = 0; b < NBB; ++b) s2_[b] = (SC)[b][(U)];                       \
+    _Pragma("unroll") for (int b = 0; b < NBB; ++b) s2_[b] = scale_of((SC)[b], (U));             \
     half8_t bfa_[NBB], bfb_[NBB];                                                                \
     _Pragma("unroll") for (int b = 0; b < NBB; ++b) bfa_[b] = dq8p(word((F).b[b], 0), s2_[b]);   \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                              \
@@ -767,7 +840,8 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
     const int n = S_end_full - S_begin;
     if (n > 0) {
       if (!kEarlyB) {
-        load_sc(S_begin, sc_nxt, true);
+        if (kPairSc) load_sc2(S_begin, sc_pair, true);
+        else load_sc(S_begin, sc_nxt, true);
         load_b(S_begin, 0, fb0, true);
         QMOE_LOAD_A_TILE(S_begin, 0, true, 0);
         load_b(S_begin, 1, fb1, true);
@@ -777,11 +851,15 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
         wait_vmcnt<0>();
       }
       __syncthreads();
-      promote_scales();
+      if (kPairSc) promote_pair();
+      else promote_scales();
       for (int S = S_begin; S < S_end_full; ++S) {
         // the next super-step, clamped: the last one reloads itself
         const int Sn = min(S + 1, S_end_full - 1);
-        load_sc(Sn, sc_nxt, true);
+        // scales: the second super-step of each pair loads the next pair
+        const bool second = ((S - S_begin) & 1) != 0;
+        if (!kPairSc) load_sc(Sn, sc_nxt, true);
+        else if (second) load_sc2(S + 1, sc_pair, S + 1 < S_end_full);
         if constexpr (GATEUP && NMBC <= kGuPairRowBlocks) {
           // weights in line-half pairs: sub-steps 2 and 3 go out with
           // sub-step 0, the next super-step's 0 and 1 with sub-step 2
@@ -795,11 +873,15 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
           QMOE_SUBSTEP(2, fb2, S, 3, Sn, 0, fb0, 0);
           QMOE_SUBSTEP(3, fb3, Sn, 0, Sn, 1, fb1, 1);
         }
-        promote_scales();
+        if (kPairSc && second) promote_pair();
+        else promote_scales();
       }
     }
     if (has_tail) {  // the partial super-step: groups past K read zeros
-      load_sc(nss_full, sc_nxt, true);
+      // (K is a multiple of 128: a lane's four scales lie in the row or all
+      // past it; only the lane offset is range-checked, so lanes past the
+      // row must not read)
+      load_sc(nss_full, sc_nxt, nss_full * 16 + 4 * kq < ngroups);
       promote_scales();
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -875,7 +957,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
       }
     }
     if (has_tail) {  // the partial super-step: groups past K read zeros
-      load_sc(nss_full, sc_nxt, true);
+      load_sc(nss_full, sc_nxt, nss_full * 16 + 4 * kq < ngroups);
       promote_scales();
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
