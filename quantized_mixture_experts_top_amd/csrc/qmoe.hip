@@ -1499,50 +1499,70 @@ __global__ __launch_bounds__(kThreads) void router_gemv_kernel(RouterArgs a) {
 }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-constexpr int kRouterTile = 64;   // tokens and experts per block
-constexpr int kRouterKC = 64;     // inputs per K chunk (two MFMA k-slices)
+constexpr int kRouterTok = 32;      // tokens per block (two halves of 16)
+constexpr int kRouterExp = 64;      // experts per block
+constexpr int kRouterKC = 64;       // inputs per K chunk (two MFMA k-slices)
+constexpr int kRouterKSplit = 8;    // K chunks dealt round-robin to 8 wave pairs
+constexpr int kRouterThreads = 64 * 2 * kRouterKSplit;
 
-// Larger M: 64-token x 64-expert tiles, 4 waves of 16 tokens each; bf16
-// MFMA 16x16x32 with fp32 accumulators.  Each K chunk of the block's router
-// rows (64 rows x 128 bytes) goes from memory straight into LDS (lane l of a
-// load instruction fills bytes 16l..16l+15 of its 1 KiB), double-buffered;
-// the 16-byte piece p of row n sits at slot p ^ ((n >> 1) & 7), so the 16
-// rows an MFMA operand read touches fall in distinct banks.  Each wave's
-// token fragments come from memory into registers, one chunk ahead.
-__global__ __launch_bounds__(kThreads) void router_tile_kernel(RouterArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 lds_b0[kRouterTile * kRouterKC];
-  __shared__ __attribute__((aligned(16))) _Float16 lds_b1[kRouterTile * kRouterKC];
+// Larger M: 32-token x 64-expert tiles; bf16 MFMA 16x16x32 with fp32
+// accumulators.  The block's 16 waves are 2 token halves x 8 K groups: group
+// g takes K chunks g, g + 8, g + 16, ..., so each wave's chain of dependent
+// chunk loads is an eighth of K long (a 7168-input row in 14 chunk steps
+// rather than 112).  The router's whole input is a few MB, so the call is
+// bound by that chain, not by bytes: on MI355X (384 experts, 7168 inputs)
+// 90 and 1024 tokens took about 34 us against 90 us with one K group (four
+// groups: 39 us); at 4096 tokens it stays near 92 us, set by the chain
+// times the rounds of blocks (one per CU at 128 KiB of LDS).
+// Each group's chunk of the router rows (64 rows x 128 bytes) goes from
+// memory straight into the group's LDS buffer (lane l of a load instruction
+// fills bytes 16l..16l+15 of its 1 KiB), double-buffered; the 16-byte piece
+// p of row n sits at slot p ^ ((n >> 1) & 7), so the 16 rows an MFMA operand
+// read touches fall in distinct banks.  Each wave's token fragments come
+// from memory into registers, one chunk ahead.  All waves run the same
+// number of steps (a group past the last chunk loads and adds zeros), and
+// the groups' partial tiles are added through LDS in group order.
+__global__ __launch_bounds__(kRouterThreads) void router_tile_kernel(RouterArgs a) {
+  __shared__ __attribute__((aligned(16))) _Float16 lds_w[kRouterKSplit * 2 * kRouterExp * kRouterKC];
+  static_assert(sizeof(lds_w) >= kRouterThreads * 16 * sizeof(float), "the partial tiles fit the buffers");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int th = wave & 1, kg = wave >> 1;  // token half, K group
   const int r = lane & 15, kq = lane >> 4;
-  const int ntt = (a.M + kRouterTile - 1) / kRouterTile;
-  const int t0 = ((int)blockIdx.x % ntt) * kRouterTile, e0 = ((int)blockIdx.x / ntt) * kRouterTile;
+  const int ntt = (a.M + kRouterTok - 1) / kRouterTok;
+  const int t0 = ((int)blockIdx.x % ntt) * kRouterTok, e0 = ((int)blockIdx.x / ntt) * kRouterExp;
   const uint32_t row_bytes = (uint32_t)a.H * 2;
   const __amdgpu_buffer_rsrc_t rX = buffer_rsrc(a.x, (uint32_t)a.M * row_bytes);
   const __amdgpu_buffer_rsrc_t rW = buffer_rsrc(a.wr, (uint32_t)a.E * row_bytes);
   // this lane's token row (rows past M read zeros)
-  const int trow = t0 + 16 * wave + r;
+  const int trow = t0 + 16 * th + r;
   const uint32_t xoff = trow < a.M ? (uint32_t)trow * row_bytes + 16 * kq : kOob;
-  // router-row loads: instruction j of this wave fills rows 8(2*wave + j) ..
-  // +7 of the chunk; lane l: row + l/8, LDS slot l%8 holds piece
-  // (l%8) ^ ((row >> 1) & 7)
-  uint32_t woff[2];
+  // router-row loads: the group's two waves fill its 64 rows, instruction j
+  // of wave th rows 8(4th + j) .. +7; lane l: row + l/8, slot l%8
+  uint32_t woff[4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = 8 * (2 * wave + j) + (lane >> 3);
+  for (int j = 0; j < 4; ++j) {
+    const int n = 8 * (4 * th + j) + (lane >> 3);
     const int piece = (lane & 7) ^ ((n >> 1) & 7);
     woff[j] = e0 + n < a.E ? (uint32_t)(e0 + n) * row_bytes + 16 * piece : kOob;
   }
+  _Float16* const gw = lds_w + kg * 2 * kRouterExp * kRouterKC;  // this group's two buffers
   const int nchunks = a.H / kRouterKC;
-  auto load_w = [&](int c, int buf) __attribute__((always_inline)) {
+  const int steps = (nchunks + kRouterKSplit - 1) / kRouterKSplit;
+  // chunk of step it for this group; past the last one every lane reads zeros
+  auto load_w = [&](int it, int buf) __attribute__((always_inline)) {
+    const int c = kRouterKSplit * it + kg;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      load_lds16(rW, (buf ? lds_b1 : lds_b0) + (8 * (2 * wave + j)) * kRouterKC, woff[j], c * kRouterKC * 2);
+    for (int j = 0; j < 4; ++j)
+      load_lds16(rW, gw + buf * kRouterExp * kRouterKC + (8 * (4 * th + j)) * kRouterKC, c < nchunks ? woff[j] : kOob,
+                 c * kRouterKC * 2);
   };
-  auto load_x = [&](int c, u32x4_t (&xf)[2]) __attribute__((always_inline)) {
+  auto load_x = [&](int it, u32x4_t (&xf)[2]) __attribute__((always_inline)) {
+    const int c = kRouterKSplit * it + kg;
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-      xf[s] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rX, xoff, c * kRouterKC * 2 + 64 * s, 0));
+      xf[s] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rX, c < nchunks ? xoff : kOob, c * kRouterKC * 2 + 64 * s, 0));
   };
   float4_t acc[4];
 #pragma unroll
@@ -1552,15 +1572,15 @@ __global__ __launch_bounds__(kThreads) void router_tile_kernel(RouterArgs a) {
   load_x(0, xa);
   wait_vmcnt<0>();
   __syncthreads();
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
-    const bool more = c + 1 < nchunks;
+  for (int it = 0; it < steps; ++it) {
+    const int buf = it & 1;
+    const bool more = it + 1 < steps;
     if (more) {
-      load_w(c + 1, buf ^ 1);
-      load_x(c + 1, xb);
+      load_w(it + 1, buf ^ 1);
+      load_x(it + 1, xb);
     }
     __builtin_amdgcn_sched_barrier(0);
-    const _Float16* lb = buf ? lds_b1 : lds_b0;
+    const _Float16* lb = gw + buf * kRouterExp * kRouterKC;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const bf16x8_t av = __builtin_bit_cast(bf16x8_t, xa[s]);
@@ -1576,17 +1596,30 @@ __global__ __launch_bounds__(kThreads) void router_tile_kernel(RouterArgs a) {
     xa[0] = xb[0];
     xa[1] = xb[1];
   }
-  // lane (r, kq) holds tokens 4kq..4kq+3 of its wave's 16, expert column r
+  // the groups' partial tiles through LDS (the loop ended on a barrier, so
+  // the buffers are free), added in group order by the waves of group 0
+  float* red = reinterpret_cast<float*>(lds_w);
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[((wave * 4 + cb) * 4 + i) * 64 + lane] = acc[cb][i];
+  __syncthreads();
+  if (kg != 0) return;
+  // lane (r, kq) holds tokens 4kq..4kq+3 of its half's 16, expert column r
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
     const int e = e0 + 16 * cb + r;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 16 * wave + 4 * kq + i;
-      if (t < a.M && e < a.E) a.logits[(size_t)t * a.E + e] = acc[cb][i];
+      float v = red[((th * 4 + cb) * 4 + i) * 64 + lane];
+#pragma unroll
+      for (int g = 1; g < kRouterKSplit; ++g) v += red[(((th + 2 * g) * 4 + cb) * 4 + i) * 64 + lane];
+      const int t = t0 + 16 * th + 4 * kq + i;
+      if (t < a.M && e < a.E) a.logits[(size_t)t * a.E + e] = v;
     }
   }
 }
+
 
 // ------------------------------------------------------------- inspection
 
@@ -2035,8 +2068,8 @@ int do_router(qmoe_layer* L, const void* x, const void* w_router, int64_t M, flo
     router_gemv_kernel<<<dim3((unsigned)ceil_div(waves, kThreads / 64)), kThreads, 0, st>>>(a);
     return check_launch(L, "router_gemv_kernel");
   }
-  const int64_t blocks = ceil_div(M, kRouterTile) * ceil_div(L->d.E, kRouterTile);
-  router_tile_kernel<<<dim3((unsigned)blocks), kThreads, 0, st>>>(a);
+  const int64_t blocks = ceil_div(M, kRouterTok) * ceil_div(L->d.E, kRouterExp);
+  router_tile_kernel<<<dim3((unsigned)blocks), kRouterThreads, 0, st>>>(a);
   return check_launch(L, "router_tile_kernel");
 }
 

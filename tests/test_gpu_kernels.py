@@ -539,8 +539,10 @@ def _router_only_layer(E, H, max_rows):
 
 @pytest.mark.parametrize("E,H,M", [
     (384, 7168, 1), (384, 7168, 9), (384, 7168, 16),   # GEMV (one wave per expert and 4 tokens)
-    (384, 7168, 17), (384, 7168, 300),                 # 64x64 MFMA tiles, ragged token tile
+    (384, 7168, 17), (384, 7168, 300),                 # 32x64 MFMA tiles, ragged token tile
+    (384, 7168, 1024), (384, 7168, 4096),              # the layer's sizes
     (100, 1024, 70), (8, 256, 16), (1000, 128, 65),    # experts not a multiple of 64; K of 2 chunks
+    (64, 384, 100),                                    # 6 chunks: two K groups take 2, two take 1
 ])
 def test_router_logits_parity(E, H, M):
     """logits = x @ W_r^T (bf16 inputs, fp32 accumulation) against the
