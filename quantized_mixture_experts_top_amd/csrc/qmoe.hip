@@ -1466,6 +1466,10 @@ __device__ __forceinline__ float dot_bf16x2(uint32_t a, uint32_t b, float acc) {
 // Small M: one wave per (expert, group of up to 4 tokens); each lane takes
 // 8 consecutive inputs of every 512, the 64 lanes' partial sums are added by
 // a butterfly.  The router row is read once per token group, x from cache.
+// The loads of kRouterGemvSteps loop steps go out before their products, so
+// a 7168-input row is 4 round trips to memory rather than 14 (each lane
+// still adds its products in input order).
+constexpr int kRouterGemvSteps = 4;
 __global__ __launch_bounds__(kThreads) void router_gemv_kernel(RouterArgs a) {
   const int lane = threadIdx.x & 63;
   const int wid = (int)blockIdx.x * (kThreads / 64) + (int)(threadIdx.x >> 6);
@@ -1478,7 +1482,26 @@ __global__ __launch_bounds__(kThreads) void router_gemv_kernel(RouterArgs a) {
 #pragma unroll
   for (int u = 0; u < kRouterGemvTokens; ++u) xrow[u] = a.x + (size_t)min(t0 + u, a.M - 1) * runs;  // clamped
   float acc[kRouterGemvTokens] = {};
-  for (int v = lane; v < runs; v += 64) {
+  int v = lane;
+  for (; v + (kRouterGemvSteps - 1) * 64 < runs; v += kRouterGemvSteps * 64) {
+    uint4 w[kRouterGemvSteps], xv[kRouterGemvSteps][kRouterGemvTokens];
+#pragma unroll
+    for (int s = 0; s < kRouterGemvSteps; ++s) {
+      w[s] = wrow[v + 64 * s];
+#pragma unroll
+      for (int u = 0; u < kRouterGemvTokens; ++u) xv[s][u] = xrow[u][v + 64 * s];
+    }
+#pragma unroll
+    for (int s = 0; s < kRouterGemvSteps; ++s)
+#pragma unroll
+      for (int u = 0; u < kRouterGemvTokens; ++u) {
+        acc[u] = dot_bf16x2(w[s].x, xv[s][u].x, acc[u]);
+        acc[u] = dot_bf16x2(w[s].y, xv[s][u].y, acc[u]);
+        acc[u] = dot_bf16x2(w[s].z, xv[s][u].z, acc[u]);
+        acc[u] = dot_bf16x2(w[s].w, xv[s][u].w, acc[u]);
+      }
+  }
+  for (; v < runs; v += 64) {
     const uint4 w = wrow[v];
 #pragma unroll
     for (int u = 0; u < kRouterGemvTokens; ++u) {
