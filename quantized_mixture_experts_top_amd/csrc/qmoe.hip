@@ -660,10 +660,16 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   // (down tiles of one 16-column block per wave only: wider waves have no
   // registers to hold these fragments across the lookups)
   constexpr bool kEarlyB = !GATEUP && NBW == 1;
+  // (a K of only a partial super-step: the tail's first scales and weights)
+  const bool early_tail = kEarlyB && S_end_full == S_begin && has_tail;
   if (kEarlyB && S_end_full > S_begin) {
     load_sc(S_begin, sc_nxt, true);
     load_b(S_begin, 0, fb0, true);
     load_b(S_begin, 1, fb1, true);
+  } else if (early_tail) {
+    load_sc(nss_full, sc_nxt, nss_full * 16 + 4 * kq < ngroups);
+    load_b(nss_full, 0, fb0, nss_full * 16 + kq < ngroups);
+    if (nss_full * 16 + 4 < ngroups) load_b(nss_full, 1, fb1, nss_full * 16 + 4 + kq < ngroups);
   }
   // per tile row: activation offset and the token's scale, read by the
   // epilogue (gate+up: 2^e, which takes x's scaling off g and u; down: its
@@ -830,6 +836,33 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
     wait_vmcnt<0>();                                                                             \
     __syncthreads();                                                                             \
   } while (0)
+  // The partial super-step (K % 512 != 0; groups past K read zeros): its
+  // sub-steps go two at a time, one per LDS buffer, their weights, tiles
+  // and (with the first pair) the scales behind one wait, so a 256-input K
+  // (one GPU's share of an 8-way tensor-parallel down product, all tail)
+  // costs one trip to memory instead of three.  K is a multiple of 128, so a
+  // lane's four scales lie in the row or all past it; only the lane offset
+  // is range-checked, so lanes past the row must not read.
+#define QMOE_TAIL()                                                                              \
+  do {                                                                                           \
+    _Pragma("unroll") for (int u0 = 0; u0 < 4; u0 += 2) {                                        \
+      if (nss_full * 16 + 4 * u0 >= ngroups) break; /* sub-steps wholly past K (wave-uniform) */ \
+      const bool two_ = nss_full * 16 + 4 * (u0 + 1) < ngroups;                                  \
+      __syncthreads(); /* every wave is done reading both buffers */                             \
+      if (!(u0 == 0 && early_tail)) { /* (else already in flight) */                             \
+        if (u0 == 0) load_sc(nss_full, sc_nxt, nss_full * 16 + 4 * kq < ngroups);                 \
+        load_b(nss_full, u0, fb0, nss_full * 16 + 4 * u0 + kq < ngroups);                        \
+        if (two_) load_b(nss_full, u0 + 1, fb1, nss_full * 16 + 4 * (u0 + 1) + kq < ngroups);    \
+      }                                                                                          \
+      QMOE_LOAD_A_TILE(nss_full, u0, nss_full * 16 + 4 * u0 + aseg < ngroups, 0);                 \
+      if (two_) QMOE_LOAD_A_TILE(nss_full, u0 + 1, nss_full * 16 + 4 * (u0 + 1) + aseg < ngroups, 1); \
+      __builtin_amdgcn_s_waitcnt(0);                                                             \
+      __syncthreads();                                                                           \
+      if (u0 == 0) promote_scales();                                                             \
+      QMOE_COMPUTE(fb0, sc_cur, u0, 0);                                                          \
+      if (two_) QMOE_COMPUTE(fb1, sc_cur, u0 + 1, 1);                                            \
+    }                                                                                            \
+  } while (0)
   // The row blocks that hold routed rows are computed without a branch per
   // block: the loop is instantiated for 2, 4, 5, 6, 7 and 8 blocks (about
   // 85 rows per expert at 4096 tokens: 5-7 blocks) and the item's count
@@ -877,25 +910,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
         else promote_scales();
       }
     }
-    if (has_tail) {  // the partial super-step: groups past K read zeros
-      // (K is a multiple of 128: a lane's four scales lie in the row or all
-      // past it; only the lane offset is range-checked, so lanes past the
-      // row must not read)
-      load_sc(nss_full, sc_nxt, nss_full * 16 + 4 * kq < ngroups);
-      promote_scales();
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (nss_full * 16 + 4 * u >= ngroups) break;  // sub-steps wholly past K (wave-uniform)
-        const bool okb = nss_full * 16 + 4 * u + kq < ngroups;
-        const bool oka = nss_full * 16 + 4 * u + aseg < ngroups;
-        __syncthreads();  // every wave is done reading buffer 0
-        load_b(nss_full, u, fb0, okb);
-        QMOE_LOAD_A_TILE(nss_full, u, oka, 0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        QMOE_COMPUTE(fb0, sc_cur, u, 0);
-      }
-    }
+    if (has_tail) QMOE_TAIL();
   };
   // Down items of at most 32 rows: a whole super-step of their activation
   // tile (4 sub-steps x 2 row blocks) fits one buffer, so the block loads
@@ -956,22 +971,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
         promote_scales();
       }
     }
-    if (has_tail) {  // the partial super-step: groups past K read zeros
-      load_sc(nss_full, sc_nxt, nss_full * 16 + 4 * kq < ngroups);
-      promote_scales();
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (nss_full * 16 + 4 * u >= ngroups) break;  // sub-steps wholly past K (wave-uniform)
-        const bool okb = nss_full * 16 + 4 * u + kq < ngroups;
-        const bool oka = nss_full * 16 + 4 * u + aseg < ngroups;
-        __syncthreads();  // every wave is done reading buffer 0
-        load_b(nss_full, u, fb0, okb);
-        QMOE_LOAD_A_TILE(nss_full, u, oka, 0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        QMOE_COMPUTE(fb0, sc_cur, u, 0);
-      }
-    }
+    if (has_tail) QMOE_TAIL();
   };
   if (nmb <= 2) {
     if constexpr (kEarlyB && MB >= 8) kloop_ss(0);
@@ -982,6 +982,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   else if (MB == 8 && nmb == 7) kloop(std::integral_constant<int, 7>{});
   else kloop(std::integral_constant<int, MB>{});
 #undef QMOE_SUBSTEP
+#undef QMOE_TAIL
 #undef QMOE_COMPUTE_IL
 #undef QMOE_SUBSTEP_PAIR
 #undef QMOE_SUBSTEP_NOB
