@@ -16,7 +16,11 @@ layer with a shared expert at M = 512.  The shapes and the sweep are those of
 "The MoE Throughput Lever: Quantifying the INT4 Marlin GEMM on Blackwell PRO
 6000" (sections "The Benchmark: What Was Measured" and "The Two Regimes:
 Weight-Streaming vs. Compute-Bound"); its per-M figures for one RTX PRO 6000
-Blackwell are reported as context, not as a target.
+Blackwell are reported as context, not as a target.  After the sweep it
+times one GPU's share of the sharded layer (section "The Architectural
+Implication: Refining the Engine Design"), 8-way tensor parallel (all 384
+experts with I=256) and expert parallel (48 of the 384 experts), at M = 1,
+9, 256 and 4096, as extra per_M rows.
 
 Prints one JSON line: the headline (M=4096, the largest configuration) as
 tokens/s, the roofline of its dominant kernel (gate+up) from HIP events on
@@ -56,6 +60,10 @@ COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 SWEEP = [("decode", 1), ("decode", 9), ("transition", 90), ("transition", 256), ("plateau", 1024),
          ("skew", 512), ("plateau", 4096)]
 HEADLINE = ("plateau", 4096)
+# one GPU's share of the sharded layer, timed after the sweep (per_M rows only):
+# 8-way tensor parallel (all 384 experts, I=256) and expert parallel (48 of 384)
+SLICES = [("tp8", 1), ("tp8", 9), ("tp8", 256), ("tp8", 4096),
+          ("ep48", 1), ("ep48", 9), ("ep48", 256), ("ep48", 4096)]
 # counter scaling factors: what FETCH_SIZE / WRITE_SIZE (KiB per dispatch) read
 # for a plain device copy of known size (bench.py --calibrate-copy)
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
@@ -420,31 +428,35 @@ def main():
                 raise SystemExit(f"unknown workload {wname}")
             configs.append((wname, int(m.replace("M=", ""))))
     else:
-        configs = list(SWEEP)
+        configs = list(SWEEP) + list(SLICES)
     headline = configs[-1] if args.only else HEADLINE
+    # one upload per weight set (the shapes that differ only in a shared
+    # expert or skewed logits share theirs), one layer handle per shape
     t0 = time.time()
     shapes = {synth.WORKLOADS[w].shape for w, _ in configs}
-    base = synth.WORKLOADS[configs[0][0]].shape
-    w, shared = upload_weights(0, base)
+    wkey = lambda shp: (shp.E, shp.H, shp.I, shp.top_k, shp.local_first, shp.local_count)  # noqa: E731
+    weights = {}
+    for shp in sorted(shapes, key=lambda x: (x.E, x.H, x.I, x.local_count)):
+        if wkey(shp) not in weights:
+            weights[wkey(shp)] = upload_weights(0, shp)
     log(f"weights uploaded in {time.time() - t0:.1f} s")
     max_rows = max(m for _, m in configs)
     layers = {}
     for shp in shapes:
-        assert (shp.E, shp.H, shp.I, shp.top_k, shp.local_first, shp.local_count) == \
-            (base.E, base.H, base.I, base.top_k, base.local_first, base.local_count)
-        layers[shp.shared] = Layer(E=shp.E, H=shp.H, I=shp.I, top_k=shp.top_k, max_rows=max_rows,
-                                   w13=w["w13"], s13=w["s13"], w2=w["w2"], s2=w["s2"],
-                                   shared=shared if shp.shared else None, local_first=shp.local_first,
-                                   local_count=shp.local_count)
-    # warm the GPU up to its steady clocks before anything is timed: a few
-    # calls of the largest configuration
-    wl0, m0 = max(configs, key=lambda c: c[1])
+        w, shared = weights[wkey(shp)]
+        layers[shp] = Layer(E=shp.E, H=shp.H, I=shp.I, top_k=shp.top_k, max_rows=max_rows,
+                            w13=w["w13"], s13=w["s13"], w2=w["w2"], s2=w["s2"],
+                            shared=shared if shp.shared else None, local_first=shp.local_first,
+                            local_count=shp.local_count)
+    # warm the GPU up to its steady clocks before anything is timed: calls
+    # of the headline configuration for one second
+    wl0, m0 = headline
     wl0 = synth.WORKLOADS[wl0]
-    xw = torch.from_numpy(synth.hidden(99, m0, base.H).view(np.int16)).cuda().view(torch.bfloat16)
-    lw = torch.from_numpy(synth.logits(99, m0, base.E, wl0.skew)).cuda()
+    xw = torch.from_numpy(synth.hidden(99, m0, wl0.shape.H).view(np.int16)).cuda().view(torch.bfloat16)
+    lw = torch.from_numpy(synth.logits(99, m0, wl0.shape.E, wl0.skew)).cuda()
     t1 = time.time()
     while time.time() - t1 < 1.0:
-        layers[wl0.shape.shared].forward(xw, lw)
+        layers[wl0.shape].forward(xw, lw)
         torch.cuda.synchronize()
     del xw, lw
 
@@ -454,7 +466,7 @@ def main():
         small = M <= 64
         steps = args.steps if args.steps is not None else (100 if small else 20)
         warmup = args.warmup if args.warmup is not None else (50 if small else 5)
-        r = time_config(layers[wl.shape.shared], wl.shape, wl, M, steps, warmup, graph=args.graph)
+        r = time_config(layers[wl.shape], wl.shape, wl, M, steps, warmup, graph=args.graph)
         page = PAGE_MS_PER_CALL.get(M) if wname in ("decode", "transition", "plateau", "skew") else None
         r["page_us_per_call_context"] = page * 1e3 if page else None
         r["gate_up_traffic_bytes"] = stored_traffic(wname, M)
