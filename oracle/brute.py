@@ -117,3 +117,27 @@ def router_logits(x_bits, wr_bits):
             row.append(acc)
         out.append(row)
     return out
+
+
+def _f32(v: float) -> float:
+    """Round a Python float to the nearest float32 value."""
+    return struct.unpack("<f", struct.pack("<f", v))[0]
+
+
+def sigmoid_route(logits, k, bias=None, scale=1.0):
+    """The sigmoid router by explicit loops: per expert the score
+    1 / (1 + e^(-l)) and the selection key (score + bias) rounded to float32
+    as the selection is made; the k largest keys by repeated arg-max (ties to
+    the lower index); the selected scores renormalised times the scale.
+    Returns (ids, weights) as lists."""
+    all_ids, all_w = [], []
+    for row in logits:
+        scores = [1.0 / (1.0 + math.exp(-float(l))) for l in row]
+        keys = [_f32(_f32(s) + (_f32(float(bias[e])) if bias is not None else 0.0)) for e, s in enumerate(scores)]
+        ids = _topk_argmax(keys, k)
+        tot = 0.0
+        for e in ids:
+            tot += scores[e]
+        all_ids.append(ids)
+        all_w.append([scores[e] / tot * scale for e in ids])
+    return all_ids, all_w

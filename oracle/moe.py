@@ -32,7 +32,12 @@ the design notes):
 * activation: h = SiLU(gate) * up with SiLU(z) = z / (1 + exp(-z));
 * within an expert, routed rows are ordered by ascending token index;
 * combine: out[t] = sum over j = 0..k-1 of w[t,j] * y(t,j), in j order; a
-  shared expert, when present, is added afterwards with weight 1.0.
+  shared expert, when present, is added afterwards with weight 1.0;
+* optional sigmoid scoring (the pages state top-8 routing but no scoring
+  function; this is the router of the model family whose shapes the pages
+  benchmark, stated as an option): scores s = 1 / (1 + e^(-l)), selection by
+  s + b (a per-expert bias that steers selection only), weights = the
+  selected scores renormalised and times a routed scaling factor.
 
 Everything is computed in float64.  Integer results (ids, counts, offsets,
 perm) are exact.
@@ -102,7 +107,8 @@ def router_logits(x_bits: np.ndarray, wr_bits: np.ndarray) -> np.ndarray:
 
 def select_topk(logits: np.ndarray, k: int) -> np.ndarray:
     """Per token, the k experts with the largest logit, ties to the lower
-    expert index, in that order.  [M, E] -> int32 [M, k]."""
+    expert index, in that order.  [M, E] -> int32 [M, k].  (Also used with
+    the sigmoid scoring's float32 selection keys in place of logits.)"""
     lg = np.asarray(logits, dtype=np.float32)
     M, E = lg.shape
     if not (1 <= k <= E):
@@ -152,11 +158,41 @@ def sort_slots(ids: np.ndarray, E: int):
     return perm, inv
 
 
-def route(logits: np.ndarray, k: int) -> dict:
-    """All routing outputs of one call."""
+def sigmoid_scores(logits: np.ndarray) -> np.ndarray:
+    """Scores of the sigmoid router: s = 1 / (1 + e^(-l)), float64 [M, E]."""
+    return 1.0 / (1.0 + np.exp(-np.asarray(logits, dtype=np.float64)))
+
+
+def sigmoid_selection_keys(logits: np.ndarray, bias=None) -> np.ndarray:
+    """Selection keys of the sigmoid router: s + b per expert, taken in
+    float32 (the precision the selection is made in): the score rounded to
+    float32, plus the bias, rounded again.  [M, E] float32."""
+    s32 = sigmoid_scores(logits).astype(np.float32)
+    if bias is None:
+        return s32
+    return (s32 + np.asarray(bias, dtype=np.float32)[None, :]).astype(np.float32)
+
+
+def sigmoid_weights(logits: np.ndarray, ids: np.ndarray, scale: float) -> np.ndarray:
+    """The selected experts' scores renormalised to sum to 1, times the
+    routed scaling factor (the bias does not enter).  -> float64 [M, k]."""
+    sel = np.take_along_axis(sigmoid_scores(logits), ids.astype(np.int64), axis=1)
+    return sel / sel.sum(axis=1, keepdims=True) * float(scale)
+
+
+def route(logits: np.ndarray, k: int, scoring=None) -> dict:
+    """All routing outputs of one call.  scoring: None (softmax over all
+    experts, selected weights renormalised) or {"kind": "sigmoid", "bias":
+    float [E] or None, "scale": routed scaling factor}."""
     E = np.asarray(logits).shape[1]
-    ids = select_topk(logits, k)
-    w = routing_weights(logits, ids)
+    if scoring is None or scoring.get("kind", "softmax") == "softmax":
+        ids = select_topk(logits, k)
+        w = routing_weights(logits, ids)
+    elif scoring["kind"] == "sigmoid":
+        ids = select_topk(sigmoid_selection_keys(logits, scoring.get("bias")), k)
+        w = sigmoid_weights(logits, ids, scoring.get("scale", 1.0))
+    else:
+        raise ValueError(f"unknown scoring {scoring['kind']}")
     counts, offsets = count_and_scan(ids, E)
     perm, inv = sort_slots(ids, E)
     return {"ids": ids, "w": w, "counts": counts, "offsets": offsets, "perm": perm, "inv_perm": inv}
@@ -203,7 +239,7 @@ def combine(w_row: np.ndarray, y_rows, shared_row=None) -> np.ndarray:
 
 
 def forward(x_bits: np.ndarray, logits: np.ndarray, k: int, get_expert, I: int,
-            shared=None, tokens=None, return_h: bool = False, local=None) -> dict:
+            shared=None, tokens=None, return_h: bool = False, local=None, scoring=None) -> dict:
     """The layer: out[t] = sum_j w[t,j] * MLP_{ids[t,j]}(x[t]) (+ shared
     expert), float64.
 
@@ -218,10 +254,12 @@ def forward(x_bits: np.ndarray, logits: np.ndarray, k: int, get_expert, I: int,
     Lever ...", section "The Architectural Implication: Refining the Engine
     Design"): routing over all experts as above, but the sum takes only the
     slots routed to experts first .. first + count - 1 (the shard's partial
-    output; the shards' outputs add up to the whole layer's)."""
+    output; the shards' outputs add up to the whole layer's).
+
+    scoring: as in route()."""
     xf = decode_bf16(x_bits)
     M, H = xf.shape
-    r = route(logits, k)
+    r = route(logits, k, scoring)
     ids, w = r["ids"], r["w"]
     sel = np.arange(M) if tokens is None else np.asarray(tokens, dtype=np.int64)
     Y = {}  # (t, j) -> y row

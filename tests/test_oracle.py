@@ -391,3 +391,59 @@ def test_shard_without_routed_slots_is_the_shared_expert_alone():
     lg[:, 6:] = -50.0  # experts 6 and 7 never selected (top-3 of 8)
     out = moe.forward(x, lg, 3, get, 64, shared=sh, local=(6, 2))["out"]
     assert np.array_equal(out, moe.expert_mlp(moe.decode_bf16(x), sh, 64))
+
+
+# ---------------------------------------------------------------- sigmoid scoring
+# The optional sigmoid router (scores 1/(1+e^-l), selection by score + a
+# per-expert bias in float32, selected scores renormalised times a scale).
+
+
+def test_sigmoid_routing_matches_explicit_loops():
+    rng = np.random.default_rng(11)
+    lg = rng.standard_normal((6, 20)).astype(np.float32)
+    bias = (0.2 * rng.standard_normal(20)).astype(np.float32)
+    r = moe.route(lg, 4, {"kind": "sigmoid", "bias": bias, "scale": 2.5})
+    ids, w = brute.sigmoid_route(lg.tolist(), 4, bias.tolist(), 2.5)
+    assert r["ids"].tolist() == ids
+    np.testing.assert_allclose(r["w"], np.array(w), rtol=1e-12)
+
+
+def test_sigmoid_without_bias_selects_as_softmax():
+    """The sigmoid is increasing, so with no bias the selection (and its
+    order) is the softmax router's: the largest logits."""
+    lg = np.random.default_rng(12).standard_normal((64, 384)).astype(np.float32)
+    a = moe.route(lg, 8, {"kind": "sigmoid", "bias": None, "scale": 1.0})
+    b = moe.route(lg, 8)
+    assert np.array_equal(a["ids"], b["ids"])
+
+
+def test_sigmoid_weights_sum_to_the_scale():
+    lg = np.random.default_rng(13).standard_normal((32, 64)).astype(np.float32)
+    bias = np.linspace(-0.3, 0.3, 64).astype(np.float32)
+    r = moe.route(lg, 6, {"kind": "sigmoid", "bias": bias, "scale": 2.827})
+    np.testing.assert_allclose(r["w"].sum(axis=1), 2.827, rtol=1e-13)
+    r1 = moe.route(lg, 1, {"kind": "sigmoid", "bias": bias, "scale": 2.827})
+    np.testing.assert_allclose(r1["w"], 2.827, rtol=1e-15)
+
+
+def test_sigmoid_bias_steers_selection_not_weights():
+    """A bias larger than any score difference puts its expert first for
+    every token; its weight is still its own score's share."""
+    lg = np.random.default_rng(14).standard_normal((16, 32)).astype(np.float32)
+    bias = np.zeros(32, dtype=np.float32)
+    bias[7] = 10.0
+    r = moe.route(lg, 3, {"kind": "sigmoid", "bias": bias, "scale": 1.0})
+    assert (r["ids"][:, 0] == 7).all()
+    s = 1.0 / (1.0 + np.exp(-lg.astype(np.float64)))
+    expect = s[:, 7] / np.take_along_axis(s, r["ids"].astype(np.int64), axis=1).sum(axis=1)
+    np.testing.assert_allclose(r["w"][:, 0], expect, rtol=1e-13)
+
+
+def test_sigmoid_equal_logits_closed_form():
+    """Equal logits: every score is the same, so the selection is the top-k
+    of the bias (ties to the lower index) and each weight is scale / k."""
+    lg = np.zeros((3, 10), dtype=np.float32)
+    bias = np.array([0.1, 0.5, 0.5, -1.0, 0.3, 0.5, 0.0, 0.2, 0.3, 0.1], dtype=np.float32)
+    r = moe.route(lg, 4, {"kind": "sigmoid", "bias": bias, "scale": 3.0})
+    assert r["ids"].tolist() == [[1, 2, 5, 4]] * 3
+    np.testing.assert_allclose(r["w"], 0.75, rtol=1e-15)
