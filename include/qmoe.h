@@ -13,6 +13,8 @@
  *     ids[t, 0..k-1] = the top_k experts by router logit (descending,
  *                      ties to the lower expert index)
  *     w[t, j]        = softmax(logits[t])[ids[t,j]], renormalised over j
+ *                      (the default scoring; qmoe_layer_desc.scoring below
+ *                      selects the sigmoid router instead)
  *     out[t]         = sum_j w[t,j] * Down_e( SiLU(Gate_e x_t) * (Up_e x_t) ),
  *                      e = ids[t,j], summed in j order
  *                      (+ Down_s(SiLU(Gate_s x_t) * (Up_s x_t)) with weight 1
@@ -83,7 +85,7 @@
 extern "C" {
 #endif
 
-#define QMOE_VERSION 3
+#define QMOE_VERSION 4
 
 enum qmoe_status {
   QMOE_OK = 0,
@@ -127,7 +129,24 @@ typedef struct {
      whole layer's.  local_count = 0: all E experts are local. */
   int32_t local_first;
   int32_t local_count;
+  /* Router scoring.  The pages state top-8 routing over 384 experts but not
+     how the experts are scored ("The MoE Throughput Lever ...", section "The
+     Context: Why This Measurement Matters").
+     QMOE_SCORING_SOFTMAX (0, the default): the top_k logits, weights = the
+     softmax over all E logits renormalised over the selected experts.
+     QMOE_SCORING_SIGMOID (1): the sigmoid router of the model family whose
+     shapes the pages benchmark: each expert's score s = 1/(1+e^-l) in fp32;
+     the top_k by the fp32 key s + expert_bias[e] (ties to the lower index;
+     the bias steers selection only); weights = s / (sum of the selected s) *
+     routed_scale.  expert_bias: NULL (no bias) or device fp32 [E] over all E
+     experts (also for a shard), finite; only with the sigmoid scoring.
+     routed_scale: 0 means 1; otherwise finite and > 0. */
+  int32_t scoring;
+  float routed_scale;
+  const float* expert_bias;
 } qmoe_layer_desc;
+#define QMOE_SCORING_SOFTMAX 0
+#define QMOE_SCORING_SIGMOID 1
 
 typedef struct qmoe_layer qmoe_layer;
 

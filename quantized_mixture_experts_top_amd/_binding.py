@@ -36,7 +36,11 @@ class LayerDesc(ctypes.Structure):
         ("shared_w13", ctypes.c_void_p), ("shared_s13", ctypes.c_void_p),
         ("shared_w2", ctypes.c_void_p), ("shared_s2", ctypes.c_void_p),
         ("local_first", ctypes.c_int32), ("local_count", ctypes.c_int32),
+        ("scoring", ctypes.c_int32), ("routed_scale", ctypes.c_float), ("expert_bias", ctypes.c_void_p),
     ]
+
+
+SCORING_SOFTMAX, SCORING_SIGMOID = 0, 1
 
 
 class Stats(ctypes.Structure):
@@ -91,7 +95,7 @@ SIGNATURES = {
     "qmoe_read_item_count": (ctypes.c_int, [_VP, _I64, _VP, _SZ, _VP, _VP]),
 }
 
-ABI_VERSION = 3  # QMOE_VERSION of include/qmoe.h
+ABI_VERSION = 4  # QMOE_VERSION of include/qmoe.h
 _lib = None
 
 

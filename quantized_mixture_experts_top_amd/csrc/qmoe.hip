@@ -83,6 +83,9 @@ struct RouteArgs {
   int* tickets;    // the GEMV split-K tickets, cleared here for the call
   int n_tickets;
   int lo, nloc;    // local experts [lo, lo + nloc) (an expert-parallel shard; else 0, E)
+  int scoring;            // QMOE_SCORING_SOFTMAX or QMOE_SCORING_SIGMOID
+  float rscale;           // sigmoid: routed scaling factor
+  const float* bias;      // sigmoid: per-expert selection bias [E] or nullptr
 };
 
 constexpr int kRouteThreads = 1024;  // routing blocks: up to 16 waves
@@ -153,25 +156,46 @@ __device__ void route_items(const RouteArgs& a, int* s_cnt, int* s_off, bool wri
   __syncthreads();
 }
 
-// The top_k experts of token t (one wave): order-preserving keys of the
-// logits; each of k rounds takes the largest key and, among experts holding
-// it, the lowest index.  Lane j < k returns the j-th selection and its
-// renormalised weight.  EPL = logits per lane (E <= 64 * EPL).
+// The top_k experts of token t (one wave): order-preserving keys held in
+// registers; each of k rounds takes the largest key and, among experts
+// holding it, the lowest index.  Lane j < k returns the j-th selection and
+// its weight.  EPL = logits per lane (E <= 64 * EPL).  The key is the logit
+// (softmax scoring) or, for the sigmoid scoring, the fp32 score
+// s = 1 / (1 + e^-l) plus the expert's selection bias.
 template <int EPL>
 __device__ __forceinline__ void wave_topk(const RouteArgs& a, int t, int lane, int& my_e, float& my_w) {
   const int E = a.E, k = a.k;
+  const bool sig = a.scoring == QMOE_SCORING_SIGMOID;
   const float* row = a.logits + (size_t)t * E;
   // (loads clamped into the row rather than predicated, so they all issue
   // before the first wait; absent and taken experts have key 0, below every
-  // finite logit's)
-  float lv[EPL];
+  // finite value's)
+  float lv[EPL], bv[EPL];
 #pragma unroll
   for (int s = 0; s < EPL; ++s) lv[s] = row[min(s * 64 + lane, E - 1)];
-  uint32_t key[EPL];
+  if (sig) {
 #pragma unroll
-  for (int s = 0; s < EPL; ++s) key[s] = (s * 64 + lane < E) ? ordered_key(lv[s]) : 0u;
+    for (int s = 0; s < EPL; ++s) bv[s] = a.bias ? a.bias[min(s * 64 + lane, E - 1)] : 0.0f;
+  }
+  uint32_t key[EPL];
+  float sc[EPL];  // sigmoid scores
+#pragma unroll
+  for (int s = 0; s < EPL; ++s) {
+    // q = min(s, 1 - s) from e^-|l| <= 1, then s = 1 - q for l >= 0: one
+    // rounding near 1 (1 / (1 + e^-l) rounds 1 + e^-l first and reaches 1.0
+    // a factor of two early in e^-l), and no overflow of e^-l for l << 0
+    float kv = lv[s];
+    sc[s] = 0.0f;
+    if (sig) {
+      const float e = expf(-fabsf(lv[s]));
+      const float q = e / (1.0f + e);
+      sc[s] = lv[s] >= 0.0f ? 1.0f - q : q;
+      kv = sc[s] + bv[s];
+    }
+    key[s] = (s * 64 + lane < E) ? ordered_key(kv) : 0u;
+  }
   my_e = 0;
-  float my_l = 0.0f;
+  float my_l = 0.0f, my_s = 0.0f;
   for (int j = 0; j < k; ++j) {
     uint32_t best = 0;
 #pragma unroll
@@ -183,13 +207,30 @@ __device__ __forceinline__ void wave_topk(const RouteArgs& a, int t, int lane, i
       const uint64_t m = __ballot(key[s] == best);
       if (e_sel < 0 && m != 0) e_sel = s * 64 + __ffsll((long long)m) - 1;
     }
+    float sel_sc = 0.0f;  // the selected expert's score, from the lane holding it
+    if (sig) {
+      float mine = 0.0f;
+#pragma unroll
+      for (int s = 0; s < EPL; ++s)
+        if (s == (e_sel >> 6)) mine = sc[s];
+      sel_sc = __shfl(mine, e_sel & 63, 64);
+    }
 #pragma unroll
     for (int s = 0; s < EPL; ++s)
       if (s * 64 + lane == e_sel) key[s] = 0;
     if (lane == j) {
       my_e = e_sel;
       my_l = from_ordered_key(best);
+      my_s = sel_sc;
     }
+  }
+  if (sig) {
+    // the selected scores renormalised, times the routed scaling factor
+    float sum = lane < k ? my_s : 0.0f;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
+    my_w = (lane < k ? my_s : 0.0f) / sum * a.rscale;
+    return;
   }
   // renormalised softmax over the selected logits: the full-softmax
   // denominator cancels, so w_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0)
@@ -1749,6 +1790,7 @@ struct qmoe_layer {
   int device = 0;
   bool shared = false;
   int lo = 0, nloc = 0;     // local experts [lo, lo + nloc) (all E unless a shard)
+  float rscale = 1.0f;      // routed scaling factor of the sigmoid scoring
   void* scratch = nullptr;  // device address of this device's scratch array
   std::mutex receipt_mu;
   qmoe_receipt last{};      // receipt of the last completed forward call
@@ -1909,6 +1951,9 @@ int do_route(qmoe_layer* L, const void* x, const float* logits, int64_t M, void*
   a.max_items = (int)max_items_for(lay.T, M, lay.S, L->nloc, bmc);
   a.lo = L->lo;
   a.nloc = L->nloc;
+  a.scoring = L->d.scoring;
+  a.rscale = L->rscale;
+  a.bias = L->d.expert_bias;
   a.ctrl = at<int>(ws, lay.ctrl);
   a.ids = at<int>(ws, lay.ids);
   a.wts = at<float>(ws, lay.wts);
@@ -2136,6 +2181,12 @@ int qmoe_layer_create(const qmoe_layer_desc* d, qmoe_layer** out) {
   if (d->local_count < 0 || d->local_count > d->E || d->local_first < 0 ||
       (d->local_count > 0 && d->local_first > d->E - d->local_count))
     return fail(QMOE_ERR_ARG, "local experts [local_first, local_first + local_count) must lie in [0, E)");
+  if (d->scoring != QMOE_SCORING_SOFTMAX && d->scoring != QMOE_SCORING_SIGMOID)
+    return fail(QMOE_ERR_ARG, "scoring must be QMOE_SCORING_SOFTMAX or QMOE_SCORING_SIGMOID");
+  if (d->expert_bias && d->scoring != QMOE_SCORING_SIGMOID)
+    return fail(QMOE_ERR_ARG, "expert_bias is only for the sigmoid scoring");
+  if (!(std::isfinite(d->routed_scale) && d->routed_scale >= 0.0f))
+    return fail(QMOE_ERR_ARG, "routed_scale must be finite and >= 0 (0 means 1)");
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return fail(QMOE_ERR_DEVICE, "no HIP device (hipGetDevice failed)");
   hipDeviceProp_t prop;
@@ -2153,6 +2204,7 @@ int qmoe_layer_create(const qmoe_layer_desc* d, qmoe_layer** out) {
   L->scratch = sp;
   L->lo = d->local_count ? d->local_first : 0;
   L->nloc = d->local_count ? d->local_count : d->E;
+  L->rscale = d->routed_scale == 0.0f ? 1.0f : d->routed_scale;
   *out = L;
   return QMOE_OK;
 }

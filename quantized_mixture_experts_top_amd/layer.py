@@ -10,7 +10,7 @@ import ctypes
 import numpy as np
 import torch
 
-from ._binding import LayerDesc, Receipt, Stats, check, load_library
+from ._binding import SCORING_SIGMOID, SCORING_SOFTMAX, LayerDesc, Receipt, Stats, check, load_library
 
 GROUP = 32
 
@@ -42,7 +42,7 @@ class Layer:
     references to the tensors (the library borrows their memory)."""
 
     def __init__(self, *, E, H, I, top_k, max_rows, w13, s13, w2, s2, shared=None, local_first=0,
-                 local_count=0):
+                 local_count=0, scoring="softmax", expert_bias=None, routed_scale=0.0):
         self.lib = load_library()
         self.E, self.H, self.I, self.top_k, self.max_rows = E, H, I, top_k, max_rows
         self._keep = [w13, s13, w2, s2]
@@ -50,9 +50,18 @@ class Layer:
         if shared:
             self._keep += [sh["w13"], sh["s13"], sh["w2"], sh["s2"]]
         self.has_shared = bool(shared)
+        # router scoring: "softmax" (default) or "sigmoid" (expert_bias: fp32 [E]
+        # device tensor or None; routed_scale: 0 means 1)
+        if scoring not in ("softmax", "sigmoid"):
+            raise ValueError(f"scoring must be 'softmax' or 'sigmoid', not {scoring!r}")
+        if expert_bias is not None:
+            if expert_bias.dtype != torch.float32 or tuple(expert_bias.shape) != (E,) or not expert_bias.is_cuda:
+                raise ValueError("expert_bias must be a float32 [E] device tensor")
+            self._keep.append(expert_bias)
+        sc = SCORING_SIGMOID if scoring == "sigmoid" else SCORING_SOFTMAX
         desc = LayerDesc(E, H, I, top_k, GROUP, max_rows, _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2),
                          _ptr(sh.get("w13")), _ptr(sh.get("s13")), _ptr(sh.get("w2")), _ptr(sh.get("s2")),
-                         local_first, local_count)
+                         local_first, local_count, sc, float(routed_scale), _ptr(expert_bias))
         self.local_first, self.local_count = local_first, (local_count or E)
         handle = ctypes.c_void_p()
         check(self.lib.qmoe_layer_create(ctypes.byref(desc), ctypes.byref(handle)))
@@ -217,9 +226,10 @@ class Layer:
 
 
 def layer_from_numpy(weights: dict, *, E, H, I, top_k, max_rows, device="cuda", local_first=0,
-                     local_count=0) -> Layer:
+                     local_count=0, scoring="softmax", expert_bias=None, routed_scale=0.0) -> Layer:
     """Copy numpy weights (as produced by the seeded generators) to the GPU
-    and create a Layer over them."""
+    and create a Layer over them (expert_bias: float32 [E] numpy array or
+    None, copied too)."""
     def dev(a):
         if a.dtype == np.uint16:
             a = a.view(np.int16)
@@ -230,4 +240,5 @@ def layer_from_numpy(weights: dict, *, E, H, I, top_k, max_rows, device="cuda", 
     return Layer(E=E, H=H, I=I, top_k=top_k, max_rows=max_rows,
                  w13=dev(weights["w13"]), s13=dev(weights["s13"]),
                  w2=dev(weights["w2"]), s2=dev(weights["s2"]), shared=shared, local_first=local_first,
-                 local_count=local_count)
+                 local_count=local_count, scoring=scoring, routed_scale=routed_scale,
+                 expert_bias=None if expert_bias is None else dev(np.asarray(expert_bias, dtype=np.float32)))

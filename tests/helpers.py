@@ -31,11 +31,11 @@ def dev(a: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def make_layer(shape: synth.LayerShape, seed: int, max_rows: int, weights: dict | None = None):
+def make_layer(shape: synth.LayerShape, seed: int, max_rows: int, weights: dict | None = None, **layer_kw):
     from quantized_mixture_experts_top_amd import layer_from_numpy
     w = weights if weights is not None else synth.all_experts(seed, shape)
     layer = layer_from_numpy(w, E=shape.E, H=shape.H, I=shape.I, top_k=shape.top_k,
-                             max_rows=max_rows, device="cuda")
+                             max_rows=max_rows, device="cuda", **layer_kw)
     return layer, w
 
 

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert lib.qmoe_version() == B.ABI_VERSION == 3
+    assert lib.qmoe_version() == B.ABI_VERSION == 4
 
 
 def _desc(**kw):
@@ -48,9 +48,13 @@ def _desc(**kw):
              w13=0x1000, s13=0x2000, w2=0x3000, s2=0x4000,
              shared_w13=None, shared_s13=None, shared_w2=None, shared_s2=None)
     d.update(kw)
-    return B.LayerDesc(d["E"], d["H"], d["I"], d["top_k"], d["group_size"], d["max_rows"],
+    desc = B.LayerDesc(d["E"], d["H"], d["I"], d["top_k"], d["group_size"], d["max_rows"],
                        d["w13"], d["s13"], d["w2"], d["s2"],
                        d["shared_w13"], d["shared_s13"], d["shared_w2"], d["shared_s2"])
+    for f in ("local_first", "local_count", "scoring", "routed_scale", "expert_bias"):
+        if f in d:
+            setattr(desc, f, d[f])
+    return desc
 
 
 @pytest.mark.parametrize("field,value,needle", [
@@ -58,6 +62,9 @@ def _desc(**kw):
     ("H", 160, "H must"), ("I", 48, "I must"), ("I", 96, "I must"), ("top_k", 0, "top_k"), ("top_k", 9, "top_k"), ("group_size", 64, "group_size"),
     ("max_rows", 0, "max_rows"), ("w13", None, "w13"), ("s13", None, "s13"), ("w2", None, "w2"),
     ("s2", None, "s2"), ("shared_w13", 0x5000, "shared expert"), ("w13", 0x1001, "aligned"),
+    ("local_count", 9, "local experts"), ("scoring", 2, "scoring must"),
+    ("expert_bias", 0x6000, "expert_bias is only"), ("routed_scale", -1.0, "routed_scale"),
+    ("routed_scale", float("nan"), "routed_scale"), ("routed_scale", float("inf"), "routed_scale"),
 ])
 def test_create_rejects_bad_fields(lib, field, value, needle):
     h = ctypes.c_void_p()

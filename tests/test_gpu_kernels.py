@@ -671,3 +671,100 @@ def test_expert_parallel_shards(M, shared):
     err = rel_err(total, full["out"])
     say(f"  shards summed vs the whole layer: rel err {err:.3e}")
     assert err <= REL_TOL
+
+
+# ----------------------------------------------------- sigmoid router scoring
+
+SIG_SCALE = 2.5
+
+
+def _expert_bias(seed, E):
+    """A per-expert selection bias of the size a load-balancing bias takes
+    (a few hundredths), float32."""
+    return (np.random.default_rng(seed).standard_normal(E) * 0.05).astype(np.float32)
+
+
+def _check_sigmoid_routing(layer, M, lg, k, E, bias, scale):
+    """ids against the oracle's float32 selection keys: equal, or, for a
+    token whose keys the two sides round a few ulp apart (the GPU's expf is
+    not correctly rounded), a valid top-k of those keys within that margin;
+    weights, counts, offsets and perm from the GPU's own ids to the oracle's
+    rules (weights to W_REL_TOL, the rest bit-exact)."""
+    from helpers import W_REL_TOL
+    r = {key: v.cpu().numpy() for key, v in layer.read_routing(M).items()}
+    ids = r["ids"]
+    ref = oracle_moe.route(lg, k, {"kind": "sigmoid", "bias": bias, "scale": scale})
+    keys = oracle_moe.sigmoid_selection_keys(lg, bias).astype(np.float64)
+    near = np.nonzero(np.any(ids != ref["ids"], axis=1))[0]
+    for t in near:
+        sel = ids[t].astype(np.int64)
+        assert np.unique(sel).size == k and sel.min() >= 0 and sel.max() < E, f"token {t}: ids {sel}"
+        tol = 4.0 * float(np.spacing(np.float32(max(1.0, np.max(np.abs(keys[t]))))))
+        ks = keys[t, sel]
+        assert np.all(ks[:-1] >= ks[1:] - tol), f"token {t}: selection order {ks}"
+        rest = np.setdiff1d(np.arange(E), sel)
+        if rest.size:
+            assert np.max(keys[t, rest]) <= ks.min() + tol, f"token {t}: an unselected key beats a selected one"
+    assert near.size <= 2 + M // 1000, f"{near.size} tokens off the oracle's selection"
+    if M:
+        wref = oracle_moe.sigmoid_weights(lg, ids, scale)
+        werr = np.max(np.abs(r["w"].astype(np.float64) - wref) / wref)
+        assert werr <= W_REL_TOL, f"sigmoid routing weight rel err {werr:.2e}"
+        assert np.allclose(r["w"].astype(np.float64).sum(axis=1), scale, rtol=1e-5)
+    counts, offsets = oracle_moe.count_and_scan(ids, E)
+    perm, _ = oracle_moe.sort_slots(ids, E)
+    assert np.array_equal(r["counts"], counts) and np.array_equal(r["offsets"], offsets)
+    assert np.array_equal(r["perm"], perm)
+    return near.size
+
+
+@pytest.mark.parametrize("E,k,M,kind,biased", [
+    (384, 8, 1, "normal", True),
+    (384, 8, 9, "normal", True),
+    (384, 8, 100, "normal", False),
+    (384, 8, 1024, "normal", True),
+    (384, 8, 4096, "normal", True),
+    (64, 4, 300, "ties", True),        # equal logits: equal scores, the bias or the index decides
+    (384, 8, 256, "saturated", False), # logits x30: scores of exactly 1.0 in float32, ties to the index
+    (16, 16, 130, "normal", True),     # every expert selected, in key order
+    (1000, 32, 70, "normal", True),    # experts not a multiple of 64
+])
+def test_sigmoid_routing(E, k, M, kind, biased):
+    say(f"sigmoid route E={E} k={k} M={M} {kind} bias={biased}")
+    shape = synth.LayerShape(E=E, H=128, I=128, top_k=k)
+    bias = _expert_bias(7, E) if biased else None
+    layer, _ = make_layer(shape, 1, M, scoring="sigmoid", expert_bias=bias, routed_scale=SIG_SCALE)
+    lg = synth.logits(3, M, E) * np.float32(30.0) if kind == "saturated" else _logits(kind, 3, M, E)
+    layer.route(dev_bf16(synth.hidden(2, M, 128)), dev(lg))
+    n = _check_sigmoid_routing(layer, M, lg, k, E, bias, SIG_SCALE)
+    say(f"  {n} near-tie tokens checked for validity")
+    layer.close()
+
+
+@pytest.mark.parametrize("E,H,I,k,M,shared", [
+    (64, 512, 256, 4, 3, False),    # GEMV items
+    (16, 512, 256, 4, 130, True),   # 128-row tiles, shared expert
+])
+def test_sigmoid_forward_parity(E, H, I, k, M, shared):
+    """The whole layer under the sigmoid router against the oracle's, and the
+    fused router + layer call bit-equal to the two-step path."""
+    import torch
+    say(f"sigmoid forward E={E} H={H} I={I} k={k} M={M} shared={shared}")
+    shape = synth.LayerShape(E=E, H=H, I=I, top_k=k, shared=shared)
+    bias = _expert_bias(11, E)
+    layer, w = make_layer(shape, 5, M, scoring="sigmoid", expert_bias=bias, routed_scale=SIG_SCALE)
+    x, wr = synth.hidden(6, M, H), synth.router_weights(8, E, H)
+    xd, wrd = dev_bf16(x), dev_bf16(wr)
+    lg = layer.router_logits(xd, wrd)
+    out = layer.forward(xd, lg).clone()
+    fused = layer.forward_router(xd, wrd)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int16), out.view(torch.int16))
+    lgn = lg.cpu().numpy()
+    scoring = {"kind": "sigmoid", "bias": bias, "scale": SIG_SCALE}
+    ref = oracle_moe.forward(x, lgn, k, expert_getter(w), I, shared=shared_of(w), scoring=scoring)
+    assert _check_sigmoid_routing(layer, M, lgn, k, E, bias, SIG_SCALE) == 0
+    err = rel_err(out.float().cpu().numpy(), ref["out"])
+    say(f"  rel err {err:.3e}")
+    assert err <= REL_TOL
+    layer.close()
