@@ -156,6 +156,16 @@ __device__ void route_items(const RouteArgs& a, int* s_cnt, int* s_off, bool wri
   __syncthreads();
 }
 
+// Sigmoid score s = 1 / (1 + e^-l) in fp32, formed as q = min(s, 1 - s) from
+// e^-|l| <= 1 and then s = 1 - q for l >= 0: one rounding near 1 (rounding
+// 1 + e^-l first would reach 1.0 a factor of two early in e^-l), and no
+// overflow of e^-l for l << 0.
+__device__ __forceinline__ float sigmoid_score(float l) {
+  const float e = expf(-fabsf(l));
+  const float q = e / (1.0f + e);
+  return l >= 0.0f ? 1.0f - q : q;
+}
+
 // The top_k experts of token t (one wave): order-preserving keys held in
 // registers; each of k rounds takes the largest key and, among experts
 // holding it, the lowest index.  Lane j < k returns the j-th selection and
@@ -178,24 +188,10 @@ __device__ __forceinline__ void wave_topk(const RouteArgs& a, int t, int lane, i
     for (int s = 0; s < EPL; ++s) bv[s] = a.bias ? a.bias[min(s * 64 + lane, E - 1)] : 0.0f;
   }
   uint32_t key[EPL];
-  float sc[EPL];  // sigmoid scores
 #pragma unroll
-  for (int s = 0; s < EPL; ++s) {
-    // q = min(s, 1 - s) from e^-|l| <= 1, then s = 1 - q for l >= 0: one
-    // rounding near 1 (1 / (1 + e^-l) rounds 1 + e^-l first and reaches 1.0
-    // a factor of two early in e^-l), and no overflow of e^-l for l << 0
-    float kv = lv[s];
-    sc[s] = 0.0f;
-    if (sig) {
-      const float e = expf(-fabsf(lv[s]));
-      const float q = e / (1.0f + e);
-      sc[s] = lv[s] >= 0.0f ? 1.0f - q : q;
-      kv = sc[s] + bv[s];
-    }
-    key[s] = (s * 64 + lane < E) ? ordered_key(kv) : 0u;
-  }
+  for (int s = 0; s < EPL; ++s) key[s] = (s * 64 + lane < E) ? ordered_key(sig ? sigmoid_score(lv[s]) + bv[s] : lv[s]) : 0u;
   my_e = 0;
-  float my_l = 0.0f, my_s = 0.0f;
+  float my_l = 0.0f;
   for (int j = 0; j < k; ++j) {
     uint32_t best = 0;
 #pragma unroll
@@ -207,29 +203,22 @@ __device__ __forceinline__ void wave_topk(const RouteArgs& a, int t, int lane, i
       const uint64_t m = __ballot(key[s] == best);
       if (e_sel < 0 && m != 0) e_sel = s * 64 + __ffsll((long long)m) - 1;
     }
-    float sel_sc = 0.0f;  // the selected expert's score, from the lane holding it
-    if (sig) {
-      float mine = 0.0f;
-#pragma unroll
-      for (int s = 0; s < EPL; ++s)
-        if (s == (e_sel >> 6)) mine = sc[s];
-      sel_sc = __shfl(mine, e_sel & 63, 64);
-    }
 #pragma unroll
     for (int s = 0; s < EPL; ++s)
       if (s * 64 + lane == e_sel) key[s] = 0;
     if (lane == j) {
       my_e = e_sel;
       my_l = from_ordered_key(best);
-      my_s = sel_sc;
     }
   }
   if (sig) {
-    // the selected scores renormalised, times the routed scaling factor
-    float sum = lane < k ? my_s : 0.0f;
+    // the selected scores (the same arithmetic again, from the logit: a read
+    // of the row just loaded) renormalised, times the routed scaling factor
+    const float my_s = lane < k ? sigmoid_score(row[my_e]) : 0.0f;
+    float sum = my_s;
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
-    my_w = (lane < k ? my_s : 0.0f) / sum * a.rscale;
+    my_w = my_s / sum * a.rscale;
     return;
   }
   // renormalised softmax over the selected logits: the full-softmax
@@ -245,25 +234,38 @@ __device__ __forceinline__ void wave_topk(const RouteArgs& a, int t, int lane, i
 
 // x -> fp16 operand format, one wave per token row: the row's largest |x|
 // sets its exponent e, and the row is stored times 2^-e (exact), so any
-// finite bf16 row fits fp16.
+// finite bf16 row fits fp16.  A lane holds up to kConvRuns runs of 8 inputs
+// (rows of up to 8192 inputs whole), all requested before the first is
+// used, so a row costs one trip to memory and is converted from registers;
+// a longer row goes in chunks of that size and is read a second time.
+constexpr int kConvRuns = 16;
 __device__ __forceinline__ void convert_x_row(const RouteArgs& a, int t, int lane) {
   const int runs = a.H / 8;
   const uint4* __restrict__ row = a.x + (size_t)t * runs;
+  uint4* __restrict__ dst = a.xa + (size_t)t * runs;
+  uint4 r[kConvRuns];
   uint32_t amax = 0;
-  int v = lane;
-  for (; v + 3 * 64 < runs; v += 4 * 64) {  // four loads in flight per lane
-    uint4 r[4];
+  for (int c0 = 0; c0 < runs; c0 += 64 * kConvRuns) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) r[u] = row[v + u * 64];
+    for (int u = 0; u < kConvRuns; ++u) {
+      const int v = c0 + u * 64 + lane;
+      r[u] = v < runs ? row[v] : make_uint4(0u, 0u, 0u, 0u);
+    }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) amax = max(amax, absmax_bf16x8(r[u]));
+    for (int u = 0; u < kConvRuns; ++u) amax = max(amax, absmax_bf16x8(r[u]));
   }
-  for (; v < runs; v += 64) amax = max(amax, absmax_bf16x8(row[v]));
   const int e = row_exponent(wave_max_u32(amax));
   const float sc = pow2f(-e);
-  uint4* __restrict__ dst = a.xa + (size_t)t * runs;
-  for (v = lane; v < runs; v += 64) dst[v] = bf16x8_to_aformat(row[v], sc);  // the row again, from cache
   if (lane == 0) a.xexp[t] = e;
+  if (runs <= 64 * kConvRuns) {  // the row is still in r
+#pragma unroll
+    for (int u = 0; u < kConvRuns; ++u) {
+      const int v = u * 64 + lane;
+      if (v < runs) dst[v] = bf16x8_to_aformat(r[u], sc);
+    }
+    return;
+  }
+  for (int v = lane; v < runs; v += 64) dst[v] = bf16x8_to_aformat(row[v], sc);  // long rows: again, from cache
 }
 
 // A call of at most 64 tokens is routed by one block of one wave per token
