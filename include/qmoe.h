@@ -139,8 +139,11 @@ typedef struct {
      the top_k by the fp32 key s + expert_bias[e] (ties to the lower index;
      the bias steers selection only); weights = s / (sum of the selected s) *
      routed_scale.  expert_bias: NULL (no bias) or device fp32 [E] over all E
-     experts (also for a shard), finite; only with the sigmoid scoring.
-     routed_scale: 0 means 1; otherwise finite and > 0. */
+     experts (also for a shard), borrowed like the weights and read by every
+     routing call; only with the sigmoid scoring.  Its values must be finite
+     (it is not read at creation; a non-finite bias leaves the selection
+     undefined).  routed_scale: 0 means 1; otherwise finite and > 0
+     (QMOE_ERR_ARG otherwise). */
   int32_t scoring;
   float routed_scale;
   const float* expert_bias;

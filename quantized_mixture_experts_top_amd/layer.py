@@ -55,8 +55,9 @@ class Layer:
         if scoring not in ("softmax", "sigmoid"):
             raise ValueError(f"scoring must be 'softmax' or 'sigmoid', not {scoring!r}")
         if expert_bias is not None:
-            if expert_bias.dtype != torch.float32 or tuple(expert_bias.shape) != (E,) or not expert_bias.is_cuda:
-                raise ValueError("expert_bias must be a float32 [E] device tensor")
+            if (expert_bias.dtype != torch.float32 or tuple(expert_bias.shape) != (E,)
+                    or expert_bias.device != w13.device):
+                raise ValueError("expert_bias must be a float32 [E] tensor on the weights' device")
             self._keep.append(expert_bias)
         sc = SCORING_SIGMOID if scoring == "sigmoid" else SCORING_SOFTMAX
         desc = LayerDesc(E, H, I, top_k, GROUP, max_rows, _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2),
