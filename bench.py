@@ -241,6 +241,17 @@ def cpu_baseline(shape, M, skew, budget_s=20.0, seed=0):
             "sample": sample, **info}
 
 
+_SCRUB = []
+
+
+def _scrub_buffer():
+    """A 1 GiB device buffer (allocated and filled once) whose read evicts the caches."""
+    import torch
+    if not _SCRUB:
+        _SCRUB.append(torch.zeros((1 << 30) // 8, dtype=torch.int64, device="cuda"))
+    return _SCRUB[0]
+
+
 def time_config(layer, shape, wl, M, steps, warmup, graph=False):
     """Whole-layer throughput and per-kernel durations of M-token calls."""
     import torch
@@ -289,6 +300,21 @@ def time_config(layer, shape, wl, M, steps, warmup, graph=False):
     torch.cuda.synchronize()
     stage = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)] for i in range(steps)])
     per_call_us = np.array([evs[i][0].elapsed_time(evs[i][4]) for i in range(steps)]) * 1e3
+    # ---- cache-cold calls: before each, a 1 GiB read evicts the L2s and
+    # the 256 MB last-level cache, so no weight line of an earlier call is
+    # still on chip (the timed region above runs calls back to back, whose
+    # touched experts differ from step to step but may overlap).  A read,
+    # not a write: dirty lines left by a write would be written back during
+    # the timed call and charge it with traffic that is not its own.
+    cold = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    scrub = _scrub_buffer()
+    for i, s in enumerate(range(warmup, n)):
+        scrub.sum()
+        cold[i][0].record(stream)
+        layer.forward(xs[s], ls[s], out=out)
+        cold[i][1].record(stream)
+    torch.cuda.synchronize()
+    cold_us = np.array([c[0].elapsed_time(c[1]) for c in cold]) * 1e3
     graph_res = None
     if graph:
         outs = [torch.empty_like(out) for _ in range(n)]
@@ -360,6 +386,7 @@ def time_config(layer, shape, wl, M, steps, warmup, graph=False):
         "gate_up_flops_per_launch": rows * f13,
         "gate_up_us": float(st_ms[1] * 1e3),
         "bracketed_call_us_p10_p50_p90": [float(np.percentile(per_call_us, q)) for q in (10, 50, 90)],
+        "cold_call_us_p10_p50_p90": [float(np.percentile(cold_us, q)) for q in (10, 50, 90)],
         "router_us": router_us,
         "receipt": {k: receipt[k] for k in ("regime", "rows_per_item", "nt_codes", "launches", "max_items",
                                              "items_built", "gate_up_blocks", "down_blocks", "workspace_bytes")},
@@ -475,6 +502,7 @@ def main():
         log(f"{key_of(wname, M)}: {r['us_per_call']:.1f} us/call, {r['tokens_per_s']:.0f} tok/s, "
             f"layer {r['layer_hbm_frac'] * 100:.1f}% HBM / {r['layer_mfma_frac'] * 100:.1f}% MFMA, stages(us) "
             + ", ".join(f"{k}={v:.1f}" for k, v in r["stage_us"].items())
+            + f", cold call p50 {r['cold_call_us_p10_p50_p90'][1]:.1f} us"
             + (f", graph {r['graph_us_per_call']:.1f} us" if "graph_us_per_call" in r else ""))
 
     hw, hm = headline
