@@ -162,14 +162,20 @@ typedef struct qmoe_layer qmoe_layer;
 int qmoe_layer_create(const qmoe_layer_desc* desc, qmoe_layer** out);
 void qmoe_layer_destroy(qmoe_layer* layer);
 
-/* Bytes of workspace a call with M tokens needs (0 <= M <= max_rows). */
+/* Bytes of workspace a call with M tokens needs (0 <= M <= max_rows): one
+   scratch allocation per call holds routing, work list, h, y and split-K
+   partials (the single scratch allocation the engagement receipts of
+   "perf(exl3): accelerate fat-expert prefill" count, section "Engagement
+   and fallback proof").  The caller allocates and owns it. */
 int qmoe_workspace_size(const qmoe_layer* layer, int64_t M, size_t* bytes);
 
 /* Enqueue a clear of a workspace's control words.  Optional: no call
    depends on what a workspace held before. */
 int qmoe_workspace_init(qmoe_layer* layer, void* workspace, size_t ws_bytes, void* stream);
 
-/* The whole layer: route, gate+up, down, combine: four kernel launches,
+/* The whole layer ("The MoE Throughput Lever ...", sections "The Context:
+   Why This Measurement Matters" and "The Benchmark: What Was Measured"):
+   route, gate+up, down, combine: four kernel launches,
    five for calls of more than 64 tokens (their routing takes two: the top-k
    of every token, then one block per 64-token chunk for the counts, the
    scan, the sorted positions and the work list).
@@ -216,7 +222,17 @@ int qmoe_forward_router(qmoe_layer* layer, const void* x, const void* w_router, 
 
 /* The same four steps one at a time, on one workspace and in this order
    (each reads what the previous one left in the workspace).  They let a
-   caller time or check each step alone.
+   caller time or check each step alone.  Sources: top-8 routing ("The MoE
+   Throughput Lever ...", section "The Context: Why This Measurement
+   Matters"); the per-expert counts and their scan ("Detailed results",
+   section "Nsight Compute on the stock kernel"); sorted routing, the
+   stacked gate+up GEMM over a shared input and the results scattered back
+   per token ("perf(exl3): accelerate fat-expert prefill", description and
+   sections "Rollout" and "Engagement and fallback proof": its direct and
+   scatter calls); INT4 group-32 weights with 16-bit activations ("The MoE
+   Throughput Lever ...", section "The Benchmark: What Was Measured").
+   Errors: as qmoe_forward (argument, workspace and device checks return
+   before anything is enqueued).
      qmoe_route     top-k routing, expert counts and their exclusive scan,
                     the stable sort of routed slots by expert, the flat list
                     of (expert, row-tile) work items, and x converted to the
