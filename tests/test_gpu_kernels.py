@@ -635,18 +635,25 @@ def test_gemv_split_k(E, H, I, k, M, shared):
 
 @pytest.mark.parametrize("M", [3, 24, 130])  # GEMV items; tiles; tiles with two routing kernels
 @pytest.mark.parametrize("shared", [False, True])
-def test_expert_parallel_shards(M, shared):
+@pytest.mark.parametrize("scoring", ["softmax", "sigmoid"])
+def test_expert_parallel_shards(M, shared, scoring):
     """Four shards of four experts each route over all 16 experts and compute
     their own: each shard's output, counts and offsets against the oracle's
     shard, and the four outputs against the whole layer (the shared expert,
-    when there is one, held by shard 0 only, as it would be computed once)."""
+    when there is one, held by shard 0 only, as it would be computed once).
+    Under the sigmoid scoring every shard gets the bias of all 16 experts."""
     import torch
     E, H, I, k = 16, 512, 256, 4
     shape = synth.LayerShape(E=E, H=H, I=I, top_k=k, shared=shared)
     w = synth.all_experts(71, shape)
     x, lg = synth.hidden(72, M, H), synth.logits(73, M, E)
     get, sh = expert_getter(w), shared_of(w)
-    full = oracle_moe.forward(x, lg, k, get, I, shared=sh)
+    sc_kw, sc_ref = {}, None
+    if scoring == "sigmoid":
+        bias = _expert_bias(74, E)
+        sc_kw = {"scoring": "sigmoid", "expert_bias": bias, "routed_scale": SIG_SCALE}
+        sc_ref = {"kind": "sigmoid", "bias": bias, "scale": SIG_SCALE}
+    full = oracle_moe.forward(x, lg, k, get, I, shared=sh, scoring=sc_ref)
     total = np.zeros_like(full["out"])
     for g in range(4):
         lo = 4 * g
@@ -654,9 +661,11 @@ def test_expert_parallel_shards(M, shared):
         if shared and g == 0:
             part.update({"shared_" + key: w["shared_" + key] for key in ("w13", "s13", "w2", "s2")})
         from quantized_mixture_experts_top_amd import layer_from_numpy
-        layer = layer_from_numpy(part, E=E, H=H, I=I, top_k=k, max_rows=M, local_first=lo, local_count=4)
+        layer = layer_from_numpy(part, E=E, H=H, I=I, top_k=k, max_rows=M, local_first=lo, local_count=4,
+                                 **sc_kw)
         out = layer.forward(dev_bf16(x), dev(lg)).float().cpu().numpy()
-        ref = oracle_moe.forward(x, lg, k, get, I, shared=sh if g == 0 else None, local=(lo, 4))
+        ref = oracle_moe.forward(x, lg, k, get, I, shared=sh if g == 0 else None, local=(lo, 4),
+                                 scoring=sc_ref)
         rt = layer.read_routing(M)
         assert np.array_equal(rt["ids"].cpu().numpy(), full["ids"])
         assert np.array_equal(rt["counts"].cpu().numpy(), full["counts"][lo:lo + 4])
