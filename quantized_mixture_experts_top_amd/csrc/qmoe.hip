@@ -1054,8 +1054,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
           const float sc = lds_sc[row];
           const float gt = acc[mb][2 * c][i] * sc;
           const float up = acc[mb][2 * c + 1][i] * inv_pow2f(sc) * ((col & 1) ? 0.0625f : 1.0f);
-          const float hv = gt / (1.0f + __expf(-gt)) * up;
-          g.h_out[(size_t)pos * g.N + ((col & ~7) | inv_perm8(col & 7))] = (_Float16)hv;
+          g.h_out[(size_t)pos * g.N + ((col & ~7) | inv_perm8(col & 7))] = silu_mul_h(gt, up);
         } else {
           const int slot = lds_slot[row];
           if (slot < 0 || slot >= g.R) continue;
@@ -1105,10 +1104,14 @@ __host__ __device__ constexpr size_t gemv_lds_bytes(int K) {
   return (size_t)kGemvRows * (K / 32) * kGemvGroupBytes;
 }
 
-// Two waves per SIMD: the ping-pong of whole super-steps holds 80 registers
-// of weights; capped at three waves the compiler spills inside the K loop,
-// which measured slower on MI355X than two waves without spills.
-constexpr int kGemvWPE = 2;
+// Three waves per SIMD: the ping-pong of whole super-steps holds 80 registers
+// of weights, and each per-row-count instance of the body fits in 168
+// registers without spills (capped at four waves it spills inside the K
+// loop).  Measured on MI355X against two waves: the 9-token call 281 -> 269
+// us, the I=256 slice at one token 35.3 -> 30.5 us.  A deeper ring of
+// super-steps per wave (three or four in flight, two waves) measured 4-12%
+// slower than more waves with two in flight.
+constexpr int kGemvWPE = 3;
 // NT: weight codes are read with the non-temporal cache policy.  A plain
 // streaming read measured about 6.7 TB/s that way against 6.2 TB/s with the
 // default policy on MI355X; it pays only while each expert's codes are read
@@ -1199,237 +1202,241 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kGemvW
         f.sc[b][m] = __builtin_amdgcn_raw_buffer_load_b16(rS, ok ? sl : kOob, (brow[b] + 4 * m) * KG * 2 + S * 32, 0);
   };
 
-  // the first super-step's loads go out before the rows are staged
-  Super fa, fb;
-  if (S_end_full > S_begin) load_super(S_begin, fa, true);
-  // each row's slot, token and scale are read now, so their dependent round
-  // trips overlap the weight stream instead of following it.  Gate+up: 2^e
-  // (x rows are held times 2^-e); down: the routing weight times 2^2e (h
-  // rows are held times 2^-2e)
-  int slot_of[kGemvRows], tok_of[kGemvRows];
-  float sc_of[kGemvRows];
-#pragma unroll
-  for (int t = 0; t < kGemvRows; ++t) {
-    const int sl = t < nr ? g.perm[pos0 + t] : -1;
-    const int tok = (sl >= 0 && sl < g.R) ? (sl < g.T ? sl / g.k : sl - g.T) : -1;
-    slot_of[t] = sl;
-    tok_of[t] = tok < g.M ? tok : -1;
-  }
-#pragma unroll
-  for (int t = 0; t < kGemvRows; ++t) {
-    const int e = tok_of[t] >= 0 ? g.xexp[tok_of[t]] : 0;
-    const int sl = slot_of[t];
-    sc_of[t] = GATEUP ? pow2f(e) : ((sl >= 0 && sl < g.T) ? g.wts[sl] : 1.0f) * pow2f(2 * e);
-  }
-
-  // ---- stage the item's activation rows (operand format) in LDS: group
-  // gi's four 16-byte runs at gi * 80 bytes
-  extern __shared__ __attribute__((aligned(16))) uint32_t gemv_lds[];
-  u32x4_t* lds_x = reinterpret_cast<u32x4_t*>(gemv_lds);
-  constexpr int kGroupRuns = kGemvGroupBytes / 16;  // 5: 4 runs + 1 of padding
-  const int runs = g.K / 8;
-  // (only this split's super-steps: runs [v_lo, v_hi))
-  const int v_lo = S_begin * (kSuper / 8), v_hi = min(S_end * (kSuper / 8), runs);
-  // and the group's code offset 8 * sum(x) as fp32 in the first word of its
-  // padding (the four runs of a group sit in four adjacent lanes)
-  for (int t = 0; t < nr; ++t) {
-    uint32_t off;
-    if (GATEUP) {
-      off = tok_of[t] >= 0 ? (uint32_t)tok_of[t] * (uint32_t)g.K * 2 : kOob;
-    } else {
-      off = (uint32_t)(pos0 + t) * (uint32_t)g.K * 2;
-    }
-    for (int v0 = v_lo; v0 < v_hi; v0 += kThreads) {  // v_lo, v_hi multiples of 4: groups stay whole
-      const int v = v0 + tid;
-      const bool in = v < v_hi;
-      const u32x4_t xr = __builtin_bit_cast(
-          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rA, (off == kOob || !in) ? kOob : off + 16 * v, 0, 0));
-      float sx = 0.f;  // sum of the run's 8 inputs (positions 2, 3, 6, 7 are stored divided by 16)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const half2_t hv = as_half2(xr[i]);
-        sx += ((i & 1) ? 16.f : 1.f) * ((float)hv[0] + (float)hv[1]);
-      }
-      sx += __shfl_xor(sx, 1, 64);
-      sx += __shfl_xor(sx, 2, 64);
-      if (in) {
-        u32x4_t* grp = lds_x + (t * ngroups + (v >> 2)) * kGroupRuns;
-        grp[v & 3] = xr;
-        if ((v & 3) == 0) reinterpret_cast<float*>(grp + 4)[0] = 8.f * sx;
-      }
-    }
-  }
-  __syncthreads();
-
-  float acc[NBB][4][kGemvRows];
-#pragma unroll
-  for (int b = 0; b < NBB; ++b)
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int t = 0; t < kGemvRows; ++t) acc[b][m][t] = 0.f;
-
-  // Super-step S from registers.  A group past K (partial last super-step)
-  // has scale 0 and reads the row's last group, so it adds exactly zero.
-  auto compute_super = [&](int S, const Super& f, auto rows_tag) __attribute__((always_inline)) {
+  // Everything from here on is instantiated per row count of the item (1 or
+  // 2), so each instance is register-allocated on its own (one-row items do
+  // not carry the second row's lookups, activations and sums).
+  auto path = [&](auto rows_tag) __attribute__((always_inline)) {
     constexpr int NR = decltype(rows_tag)::value;
-    const int gi = min(S * 16 + j, ngroups - 1);
-    u32x4_t xv[NR][4];
-    float cx[NR];  // 8 * sum(x) of the group
+    // the first super-step's loads go out before the rows are staged
+    Super fa, fb;
+    if (S_end_full > S_begin) load_super(S_begin, fa, true);
+    // each row's slot, token and scale are read now, so their dependent round
+    // trips overlap the weight stream instead of following it.  Gate+up: 2^e
+    // (x rows are held times 2^-e); down: the routing weight times 2^2e (h
+    // rows are held times 2^-2e)
+    int slot_of[NR], tok_of[NR];
+    float sc_of[NR];
 #pragma unroll
     for (int t = 0; t < NR; ++t) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xv[t][i] = lds_x[(t * ngroups + gi) * kGroupRuns + i];
-      cx[t] = reinterpret_cast<const float*>(lds_x + (t * ngroups + gi) * kGroupRuns + 4)[0];
+      const int sl = t < nr ? g.perm[pos0 + t] : -1;
+      const int tok = (sl >= 0 && sl < g.R) ? (sl < g.T ? sl / g.k : sl - g.T) : -1;
+      slot_of[t] = sl;
+      tok_of[t] = tok < g.M ? tok : -1;
     }
+#pragma unroll
+    for (int t = 0; t < NR; ++t) {
+      const int e = tok_of[t] >= 0 ? g.xexp[tok_of[t]] : 0;
+      const int sl = slot_of[t];
+      sc_of[t] = GATEUP ? pow2f(e) : ((sl >= 0 && sl < g.T) ? g.wts[sl] : 1.0f) * pow2f(2 * e);
+    }
+
+    // ---- stage the item's activation rows (operand format) in LDS: group
+    // gi's four 16-byte runs at gi * 80 bytes
+    extern __shared__ __attribute__((aligned(16))) uint32_t gemv_lds[];
+    u32x4_t* lds_x = reinterpret_cast<u32x4_t*>(gemv_lds);
+    constexpr int kGroupRuns = kGemvGroupBytes / 16;  // 5: 4 runs + 1 of padding
+    const int runs = g.K / 8;
+    // (only this split's super-steps: runs [v_lo, v_hi))
+    const int v_lo = S_begin * (kSuper / 8), v_hi = min(S_end * (kSuper / 8), runs);
+    // and the group's code offset 8 * sum(x) as fp32 in the first word of its
+    // padding (the four runs of a group sit in four adjacent lanes)
+    for (int t = 0; t < nr; ++t) {
+      uint32_t off;
+      if (GATEUP) {
+        off = tok_of[t] >= 0 ? (uint32_t)tok_of[t] * (uint32_t)g.K * 2 : kOob;
+      } else {
+        off = (uint32_t)(pos0 + t) * (uint32_t)g.K * 2;
+      }
+      for (int v0 = v_lo; v0 < v_hi; v0 += kThreads) {  // v_lo, v_hi multiples of 4: groups stay whole
+        const int v = v0 + tid;
+        const bool in = v < v_hi;
+        const u32x4_t xr = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rA, (off == kOob || !in) ? kOob : off + 16 * v, 0, 0));
+        float sx = 0.f;  // sum of the run's 8 inputs (positions 2, 3, 6, 7 are stored divided by 16)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const half2_t hv = as_half2(xr[i]);
+          sx += ((i & 1) ? 16.f : 1.f) * ((float)hv[0] + (float)hv[1]);
+        }
+        sx += __shfl_xor(sx, 1, 64);
+        sx += __shfl_xor(sx, 2, 64);
+        if (in) {
+          u32x4_t* grp = lds_x + (t * ngroups + (v >> 2)) * kGroupRuns;
+          grp[v & 3] = xr;
+          if ((v & 3) == 0) reinterpret_cast<float*>(grp + 4)[0] = 8.f * sx;
+        }
+      }
+    }
+    __syncthreads();
+
+    float acc[NBB][4][NR];
 #pragma unroll
     for (int b = 0; b < NBB; ++b)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        float p[NR];
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int t = 0; t < NR; ++t) p[t] = 0.f;
+        for (int t = 0; t < NR; ++t) acc[b][m][t] = 0.f;
+
+    // Super-step S from registers.  A group past K (partial last super-step)
+    // has scale 0 and reads the row's last group, so it adds exactly zero.
+    auto compute_super = [&](int S, const Super& f) __attribute__((always_inline)) {
+      const int gi = min(S * 16 + j, ngroups - 1);
+      u32x4_t xv[NR][4];
+      float cx[NR];  // 8 * sum(x) of the group
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // the masked nibbles as fp16 bit patterns: q * 2^-24 (subnormal),
-          // or 16q * 2^-24 for the odd inputs
-          const uint32_t w = word(f.b[b][m], i), w8 = w >> 8;
-          const half2_t w0 = as_half2(w & 0x000F000Fu);   // inputs 0, 4
-          const half2_t w1 = as_half2(w & 0x00F000F0u);   // 1, 5 (x16)
-          const half2_t w2 = as_half2(w8 & 0x000F000Fu);  // 2, 6
-          const half2_t w3 = as_half2(w8 & 0x00F000F0u);  // 3, 7 (x16)
+      for (int t = 0; t < NR; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xv[t][i] = lds_x[(t * ngroups + gi) * kGroupRuns + i];
+        cx[t] = reinterpret_cast<const float*>(lds_x + (t * ngroups + gi) * kGroupRuns + 4)[0];
+      }
+#pragma unroll
+      for (int b = 0; b < NBB; ++b)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          float p[NR];
+#pragma unroll
+          for (int t = 0; t < NR; ++t) p[t] = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // the masked nibbles as fp16 bit patterns: q * 2^-24 (subnormal),
+            // or 16q * 2^-24 for the odd inputs
+            const uint32_t w = word(f.b[b][m], i), w8 = w >> 8;
+            const half2_t w0 = as_half2(w & 0x000F000Fu);   // inputs 0, 4
+            const half2_t w1 = as_half2(w & 0x00F000F0u);   // 1, 5 (x16)
+            const half2_t w2 = as_half2(w8 & 0x000F000Fu);  // 2, 6
+            const half2_t w3 = as_half2(w8 & 0x00F000F0u);  // 3, 7 (x16)
+#pragma unroll
+            for (int t = 0; t < NR; ++t) {
+              p[t] = __builtin_amdgcn_fdot2(w0, as_half2(xv[t][i][0]), p[t], false);
+              p[t] = __builtin_amdgcn_fdot2(w1, as_half2(xv[t][i][1]), p[t], false);
+              p[t] = __builtin_amdgcn_fdot2(w2, as_half2(xv[t][i][2]), p[t], false);
+              p[t] = __builtin_amdgcn_fdot2(w3, as_half2(xv[t][i][3]), p[t], false);
+            }
+          }
+          // sum x*(q-8) = 2^24 * p - 8 * sum(x), times the group's scale
+          const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)f.sc[b][m]);
+#pragma unroll
+          for (int t = 0; t < NR; ++t) acc[b][m][t] = fmaf(s, fmaf(p[t], 16777216.f, -cx[t]), acc[b][m][t]);
+        }
+    };
+
+    // Ping-pong over whole super-steps: the next one's loads are issued
+    // before the current one is computed (a scheduling fence keeps them
+    // there), so a wave always has one super-step in flight.  The loop runs
+    // while two remain and the last one or two are peeled, so every load is
+    // used and the load counters stay exact.
+    {
+      const int last = S_end_full - 1;
+      int S = S_begin;
+      for (; S + 2 <= last; S += 2) {
+        load_super(S + 1, fb, true);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_super(S, fa);
+        load_super(S + 2, fa, true);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_super(S + 1, fb);
+      }
+      if (S + 1 == last) {
+        load_super(S + 1, fb, true);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_super(S, fa);
+        compute_super(S + 1, fb);
+      } else if (S == last) {
+        compute_super(S, fa);
+      }
+      if (has_tail) {  // the partial super-step: lanes past the last group read 0
+        load_super(nss_full, fa, nss_full * 16 + j < ngroups);
+        compute_super(nss_full, fa);
+      }
+    }
+
+    // ---- add over the 16 lanes of a row (they hold different groups); then
+    // lane (q, j < 4) takes row 4j + q of each block
+    float res[NBB][NR];
+#pragma unroll
+    for (int b = 0; b < NBB; ++b)
+#pragma unroll
+      for (int t = 0; t < NR; ++t) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          float v = acc[b][m][t];
+          v += __shfl_xor(v, 1, 64);
+          v += __shfl_xor(v, 2, 64);
+          v += __shfl_xor(v, 4, 64);
+          v += __shfl_xor(v, 8, 64);
+          acc[b][m][t] = v;
+        }
+        res[b][t] = j == 0 ? acc[b][0][t] : j == 1 ? acc[b][1][t] : j == 2 ? acc[b][2][t] : acc[b][3][t];
+      }
+    const int r = 4 * j + q;  // this lane's row in each block (lanes with j < 4)
+    // ---- split-K: every split stores its partial sums and takes a ticket;
+    // the last to arrive reads all of them and adds them in split order, so
+    // the sum does not depend on the order of arrival, then runs the epilogue.
+    // No block waits.  (A device-scope release and acquire around the ticket
+    // write back and invalidate the XCD's L2: measured 4x slower on MI355X.)
+    if (g.splits > 1) {
+      __shared__ int s_last;
+      const int tile = item * g.nblk + nb;
+      // partials go through with system-coherent stores (write-through past
+      // the XCD's L2) and are read back with system-coherent loads, so no L2
+      // writeback or invalidate is needed around the ticket
+      const __amdgpu_buffer_rsrc_t rP = buffer_rsrc(g.part + (size_t)tile * g.splits * 256, (uint32_t)g.splits * 1024);
+      constexpr int kSys = 1 | 16;  // sc0 | sc1
+      if (j < 4) {
+#pragma unroll
+        for (int b = 0; b < NBB; ++b)
+#pragma unroll
+          for (int t = 0; t < NR; ++t)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(res[b][t]), rP,
+                                                  4 * (split * 256 + (wn * 4 + b * NR + t) * 16 + r), 0, kSys);
+      }
+      wait_vmcnt<0>();  // the partials have reached memory
+      __syncthreads();
+      if (tid == 0) s_last = atomicAdd(&g.tickets[tile], 1) == g.splits - 1;
+      __syncthreads();
+      if (!s_last) return;
+      if (j < 4) {
+#pragma unroll
+        for (int b = 0; b < NBB; ++b)
 #pragma unroll
           for (int t = 0; t < NR; ++t) {
-            p[t] = __builtin_amdgcn_fdot2(w0, as_half2(xv[t][i][0]), p[t], false);
-            p[t] = __builtin_amdgcn_fdot2(w1, as_half2(xv[t][i][1]), p[t], false);
-            p[t] = __builtin_amdgcn_fdot2(w2, as_half2(xv[t][i][2]), p[t], false);
-            p[t] = __builtin_amdgcn_fdot2(w3, as_half2(xv[t][i][3]), p[t], false);
+            const uint32_t o = 4 * ((wn * 4 + b * NR + t) * 16 + r);
+            float v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rP, o, 0, kSys));
+            for (int sp = 1; sp < g.splits; ++sp)
+              v += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rP, o + sp * 1024, 0, kSys));
+            res[b][t] = v;
           }
-        }
-        // sum x*(q-8) = 2^24 * p - 8 * sum(x), times the group's scale
-        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)f.sc[b][m]);
-#pragma unroll
-        for (int t = 0; t < NR; ++t) acc[b][m][t] = fmaf(s, fmaf(p[t], 16777216.f, -cx[t]), acc[b][m][t]);
       }
-  };
+      if (tid == 0) g.tickets[tile] = 0;
+    }
+    if (j >= 4) return;
 
-  // Ping-pong over whole super-steps: the next one's loads are issued
-  // before the current one is computed (a scheduling fence keeps them
-  // there), so a wave always has one super-step in flight.  The loop runs
-  // while two remain and the last one or two are peeled, so every load is
-  // used and the load counters stay exact.
-  auto run = [&](auto rows_tag) __attribute__((always_inline)) {
-    const int last = S_end_full - 1;
-    int S = S_begin;
-    for (; S + 2 <= last; S += 2) {
-      load_super(S + 1, fb, true);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_super(S, fa, rows_tag);
-      load_super(S + 2, fa, true);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_super(S + 1, fb, rows_tag);
-    }
-    if (S + 1 == last) {
-      load_super(S + 1, fb, true);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_super(S, fa, rows_tag);
-      compute_super(S + 1, fb, rows_tag);
-    } else if (S == last) {
-      compute_super(S, fa, rows_tag);
-    }
-    if (has_tail) {  // the partial super-step: lanes past the last group read 0
-      load_super(nss_full, fa, nss_full * 16 + j < ngroups);
-      compute_super(nss_full, fa, rows_tag);
+    // ---- epilogue: lane (q, j) holds weight row r = 4j + q of each block
+#pragma unroll
+    for (int t = 0; t < NR; ++t) {
+      if (t >= nr) continue;
+      const int pos = pos0 + t;
+      if (GATEUP) {
+        if (col0[0] >= g.N) continue;
+        const int col = col0[0] + r;
+        // g = res * 2^e; h is stored times 2^-2e, odd columns divided by 16
+        const float gt = res[0][t] * sc_of[t];
+        const float up = res[1][t] * inv_pow2f(sc_of[t]) * ((col & 1) ? 0.0625f : 1.0f);
+        g.h_out[(size_t)pos * g.N + ((col & ~7) | inv_perm8(col & 7))] = silu_mul_h(gt, up);
+      } else {
+        const int slot = slot_of[t];
+        if (slot < 0 || slot >= g.R) continue;
+        const float wv = sc_of[t];
+#pragma unroll
+        for (int c = 0; c < NBW; ++c) {
+          if (col0[c] >= g.N) continue;
+          g.y_out[(size_t)slot * g.N + col0[c] + r] = (uint16_t)f32_to_bf16_rne(wv * res[c][t]);
+        }
+      }
     }
   };
-  if (nr == 1) run(std::integral_constant<int, 1>{});
-  else run(std::integral_constant<int, 2>{});
-
-  // ---- add over the 16 lanes of a row (they hold different groups); then
-  // lane (q, j < 4) takes row 4j + q of each block
-  float res[NBB][kGemvRows];
-#pragma unroll
-  for (int b = 0; b < NBB; ++b)
-#pragma unroll
-    for (int t = 0; t < kGemvRows; ++t) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        float v = acc[b][m][t];
-        v += __shfl_xor(v, 1, 64);
-        v += __shfl_xor(v, 2, 64);
-        v += __shfl_xor(v, 4, 64);
-        v += __shfl_xor(v, 8, 64);
-        acc[b][m][t] = v;
-      }
-      res[b][t] = j == 0 ? acc[b][0][t] : j == 1 ? acc[b][1][t] : j == 2 ? acc[b][2][t] : acc[b][3][t];
-    }
-  const int r = 4 * j + q;  // this lane's row in each block (lanes with j < 4)
-  // ---- split-K: every split stores its partial sums and takes a ticket;
-  // the last to arrive reads all of them and adds them in split order, so
-  // the sum does not depend on the order of arrival, then runs the epilogue.
-  // No block waits.  (A device-scope release and acquire around the ticket
-  // write back and invalidate the XCD's L2: measured 4x slower on MI355X.)
-  if (g.splits > 1) {
-    __shared__ int s_last;
-    const int tile = item * g.nblk + nb;
-    // partials go through with system-coherent stores (write-through past
-    // the XCD's L2) and are read back with system-coherent loads, so no L2
-    // writeback or invalidate is needed around the ticket
-    const __amdgpu_buffer_rsrc_t rP = buffer_rsrc(g.part + (size_t)tile * g.splits * 256, (uint32_t)g.splits * 1024);
-    constexpr int kSys = 1 | 16;  // sc0 | sc1
-    if (j < 4) {
-#pragma unroll
-      for (int b = 0; b < NBB; ++b)
-#pragma unroll
-        for (int t = 0; t < kGemvRows; ++t)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(res[b][t]), rP,
-                                                4 * (split * 256 + (wn * 4 + b * kGemvRows + t) * 16 + r), 0, kSys);
-    }
-    wait_vmcnt<0>();  // the partials have reached memory
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&g.tickets[tile], 1) == g.splits - 1;
-    __syncthreads();
-    if (!s_last) return;
-    if (j < 4) {
-#pragma unroll
-      for (int b = 0; b < NBB; ++b)
-#pragma unroll
-        for (int t = 0; t < kGemvRows; ++t) {
-          const uint32_t o = 4 * ((wn * 4 + b * kGemvRows + t) * 16 + r);
-          float v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rP, o, 0, kSys));
-          for (int sp = 1; sp < g.splits; ++sp)
-            v += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rP, o + sp * 1024, 0, kSys));
-          res[b][t] = v;
-        }
-    }
-    if (tid == 0) g.tickets[tile] = 0;
-  }
-  if (j >= 4) return;
-
-  // ---- epilogue: lane (q, j) holds weight row r = 4j + q of each block
-#pragma unroll
-  for (int t = 0; t < kGemvRows; ++t) {
-    if (t >= nr) continue;
-    const int pos = pos0 + t;
-    if (GATEUP) {
-      if (col0[0] >= g.N) continue;
-      const int col = col0[0] + r;
-      // g = res * 2^e; h is stored times 2^-2e, odd columns divided by 16
-      const float gt = res[0][t] * sc_of[t];
-      const float up = res[1][t] * inv_pow2f(sc_of[t]) * ((col & 1) ? 0.0625f : 1.0f);
-      const float hv = gt / (1.0f + __expf(-gt)) * up;
-      g.h_out[(size_t)pos * g.N + ((col & ~7) | inv_perm8(col & 7))] = (_Float16)hv;
-    } else {
-      const int slot = slot_of[t];
-      if (slot < 0 || slot >= g.R) continue;
-      const float wv = sc_of[t];
-#pragma unroll
-      for (int c = 0; c < NBW; ++c) {
-        if (col0[c] >= g.N) continue;
-        g.y_out[(size_t)slot * g.N + col0[c] + r] = (uint16_t)f32_to_bf16_rne(wv * res[c][t]);
-      }
-    }
-  }
+  if (nr == 1) path(std::integral_constant<int, 1>{});
+  else path(std::integral_constant<int, 2>{});
 }
 
 // ---------------------------------------------------------------- combine

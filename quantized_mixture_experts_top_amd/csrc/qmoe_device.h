@@ -89,6 +89,16 @@ __device__ __forceinline__ float pow2f(int n) { return __int_as_float((n + 127) 
 // 1/p for p = 2^n, n in [-126, 126] (exact; no division).
 __device__ __forceinline__ float inv_pow2f(float p) { return __int_as_float(0x7F000000 - __float_as_int(p)); }
 
+// h = SiLU(g) * u as stored: the product rounded to fp32, then to fp16.  The
+// empty asm pins the fp32 value, so the compiler cannot fuse the product into
+// the conversion (one rounding instead of two) in some kernels or
+// instantiations and not in others: every path gives the same bits.
+__device__ __forceinline__ _Float16 silu_mul_h(float gt, float up) {
+  float hv = gt / (1.0f + __expf(-gt)) * up;
+  asm volatile("" : "+v"(hv));
+  return (_Float16)hv;
+}
+
 // Largest |value| of 8 bf16 (one 16-byte run) as a magnitude bit pattern:
 // for finite values the order of the 15-bit patterns is the order of the
 // magnitudes.
