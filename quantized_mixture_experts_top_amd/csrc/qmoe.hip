@@ -913,10 +913,14 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   // zero rows, which are never stored).
   auto kloop = [&](auto nmbc_tag) __attribute__((always_inline)) {
     constexpr int NMBC = decltype(nmbc_tag)::value;
+    // scale pairs in every gate+up loop but the 8-block one, whose 128
+    // accumulators leave no room for them: there the pair was spilled, and
+    // its reload waited for every load in flight
+    constexpr bool kPair = kPairSc && NMBC < 8;
     const int n = S_end_full - S_begin;
     if (n > 0) {
       if (!kEarlyB) {
-        if (kPairSc) load_sc2(S_begin, sc_pair, true);
+        if (kPair) load_sc2(S_begin, sc_pair, true);
         else load_sc(S_begin, sc_nxt, true);
         load_b(S_begin, 0, fb0, true);
         QMOE_LOAD_A_TILE(S_begin, 0, true, 0);
@@ -927,29 +931,35 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
         wait_vmcnt<0>();
       }
       __syncthreads();
-      if (kPairSc) promote_pair();
+      if (kPair) promote_pair();
       else promote_scales();
       for (int S = S_begin; S < S_end_full; ++S) {
         // the next super-step, clamped: the last one reloads itself
         const int Sn = min(S + 1, S_end_full - 1);
         // scales: the second super-step of each pair loads the next pair
         const bool second = ((S - S_begin) & 1) != 0;
-        if (!kPairSc) load_sc(Sn, sc_nxt, true);
-        else if (second) load_sc2(S + 1, sc_pair, S + 1 < S_end_full);
+        if (!kPair) load_sc(Sn, sc_nxt, true);
         if constexpr (GATEUP && NMBC <= kGuPairRowBlocks) {
           // weights in line-half pairs: sub-steps 2 and 3 go out with
-          // sub-step 0, the next super-step's 0 and 1 with sub-step 2
+          // sub-step 0, the next super-step's 0 and 1 with sub-step 2.  The
+          // next scale pair goes out with sub-step 3's tile, whose deadline
+          // it shares: held from there to its use it takes no registers
+          // through the other sub-steps (issued with sub-step 0, it was
+          // spilled in the 8-block loop, and reloading it waited for every
+          // load in flight)
           QMOE_SUBSTEP_PAIR(0, fb0, S, 1, S, 2, fb2, fb3, 0);
           QMOE_SUBSTEP_NOB(1, fb1, S, 2, 1);
           QMOE_SUBSTEP_PAIR(2, fb2, S, 3, Sn, 0, fb0, fb1, 0);
+          if (second) load_sc2(S + 1, sc_pair, S + 1 < S_end_full);
           QMOE_SUBSTEP_NOB(3, fb3, Sn, 0, 1);
         } else {
+          if (kPair && second) load_sc2(S + 1, sc_pair, S + 1 < S_end_full);
           QMOE_SUBSTEP(0, fb0, S, 1, S, 2, fb2, 0);
           QMOE_SUBSTEP(1, fb1, S, 2, S, 3, fb3, 1);
           QMOE_SUBSTEP(2, fb2, S, 3, Sn, 0, fb0, 0);
           QMOE_SUBSTEP(3, fb3, Sn, 0, Sn, 1, fb1, 1);
         }
-        if (kPairSc && second) promote_pair();
+        if (kPair && second) promote_pair();
         else promote_scales();
       }
     }
@@ -1016,14 +1026,55 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
     }
     if (has_tail) QMOE_TAIL();
   };
+  // ---- epilogue: lane holds rows mb*16 + 4*kq + i of column r of each
+  // block.  It runs inside each row-block instance (NMBC blocks), so an
+  // instance keeps only its own blocks' accumulators live through its K loop.
+  auto epilogue = [&](auto nmbc_tag) __attribute__((always_inline)) {
+    constexpr int NMBC = decltype(nmbc_tag)::value;
+#pragma unroll
+    for (int c = 0; c < NBW; ++c) {
+      if (col0[c] >= g.N) continue;
+      const int col = col0[c] + r;
+#pragma unroll
+      for (int mb = 0; mb < NMBC; ++mb) {
+        if (mb >= nmb) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = mb * 16 + 4 * kq + i;
+          if (row >= nr) continue;
+          const int pos = pos0 + row;
+          if (GATEUP) {
+            // g = acc * 2^e; h is stored times 2^-2e: SiLU(g) * (acc_up * 2^-e),
+            // odd columns divided by 16 (operand format)
+            const float sc = lds_sc[row];
+            const float gt = acc[mb][2 * c][i] * sc;
+            const float up = acc[mb][2 * c + 1][i] * inv_pow2f(sc) * ((col & 1) ? 0.0625f : 1.0f);
+            g.h_out[(size_t)pos * g.N + ((col & ~7) | inv_perm8(col & 7))] = silu_mul_h(gt, up);
+          } else {
+            const int slot = lds_slot[row];
+            if (slot < 0 || slot >= g.R) continue;
+            g.y_out[(size_t)slot * g.N + col] = (uint16_t)f32_to_bf16_rne(lds_sc[row] * acc[mb][c][i]);
+          }
+        }
+      }
+    }
+  };
+  auto body = [&](auto nmbc_tag) __attribute__((always_inline)) {
+    kloop(nmbc_tag);
+    epilogue(nmbc_tag);
+  };
   if (nmb <= 2) {
-    if constexpr (kEarlyB && MB >= 8) kloop_ss(0);
-    else kloop(std::integral_constant<int, (MB < 2 ? MB : 2)>{});
-  } else if (nmb <= 4) kloop(std::integral_constant<int, (MB < 4 ? MB : 4)>{});
-  else if (MB == 8 && nmb == 5) kloop(std::integral_constant<int, 5>{});
-  else if (nmb <= 6) kloop(std::integral_constant<int, (MB < 6 ? MB : 6)>{});
-  else if (MB == 8 && nmb == 7) kloop(std::integral_constant<int, 7>{});
-  else kloop(std::integral_constant<int, MB>{});
+    if constexpr (kEarlyB && MB >= 8) {
+      kloop_ss(0);
+      epilogue(std::integral_constant<int, 2>{});
+    } else {
+      body(std::integral_constant<int, (MB < 2 ? MB : 2)>{});
+    }
+  } else if (nmb <= 4) body(std::integral_constant<int, (MB < 4 ? MB : 4)>{});
+  else if (MB == 8 && nmb == 5) body(std::integral_constant<int, 5>{});
+  else if (nmb <= 6) body(std::integral_constant<int, (MB < 6 ? MB : 6)>{});
+  else if (MB == 8 && nmb == 7) body(std::integral_constant<int, 7>{});
+  else body(std::integral_constant<int, MB>{});
 #undef QMOE_SUBSTEP
 #undef QMOE_TAIL
 #undef QMOE_COMPUTE_IL
@@ -1034,35 +1085,6 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
 #undef QMOE_LOAD_A_TILE
 #undef QMOE_LOAD_A_TILE_AT
 #undef QMOE_LDS_A
-
-  // ---- epilogue: lane holds rows mb*16 + 4*kq + i of column r of each block
-#pragma unroll
-  for (int c = 0; c < NBW; ++c) {
-    if (col0[c] >= g.N) continue;
-    const int col = col0[c] + r;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      if (mb >= nmb) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = mb * 16 + 4 * kq + i;
-        if (row >= nr) continue;
-        const int pos = pos0 + row;
-        if (GATEUP) {
-          // g = acc * 2^e; h is stored times 2^-2e: SiLU(g) * (acc_up * 2^-e),
-          // odd columns divided by 16 (operand format)
-          const float sc = lds_sc[row];
-          const float gt = acc[mb][2 * c][i] * sc;
-          const float up = acc[mb][2 * c + 1][i] * inv_pow2f(sc) * ((col & 1) ? 0.0625f : 1.0f);
-          g.h_out[(size_t)pos * g.N + ((col & ~7) | inv_perm8(col & 7))] = silu_mul_h(gt, up);
-        } else {
-          const int slot = lds_slot[row];
-          if (slot < 0 || slot >= g.R) continue;
-          g.y_out[(size_t)slot * g.N + col] = (uint16_t)f32_to_bf16_rne(lds_sc[row] * acc[mb][c][i]);
-        }
-      }
-    }
-  }
 }
 
 // -------------------------------------------------------- GEMV (1-2 rows)
