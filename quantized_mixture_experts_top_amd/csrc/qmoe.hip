@@ -94,51 +94,47 @@ constexpr int kRouteWaves = kRouteThreads / 64;  // also token rows per conversi
 // Counts, offsets and the flat work list from the per-expert row counts in
 // s_cnt[0..E) (the caller's threads wrote them before calling), all in LDS.
 // One wave does both exclusive scans (row offsets and work-item offsets)
-// over the E+1 entries at once: lane l sums its run of ceil((E+1)/64)
-// consecutive experts, a 6-step shuffle scan combines the 64 lane totals,
-// and each lane walks its run again to write offsets and, when `write` is
-// set, the counts, offsets and items to the workspace.  This replaces a
-// serial loop over the expert counts, and needs no block barrier between
-// the two scans.  The shared expert (entry E, a row per token) gets the
-// first items: its tiles are the longest of a call and should not be the
-// last to start.
+// over the E+1 entries at once: lane l reads its run of ceil((E+1)/64)
+// consecutive counts into registers, sums them, DPP scans combine the 64
+// lane totals, and each lane walks its run again to write offsets and, when
+// `write` is set, the counts, offsets and items to the workspace.  This
+// replaces a serial loop over the expert counts, and needs no block barrier
+// between the two scans.  The shared expert (entry E, a row per token) gets
+// the first items: its tiles are the longest of a call and should not be
+// the last to start.  Items hold a power of two rows (bmc), so the item
+// counts are shifts.
+constexpr int kMaxRun = (QMOE_MAX_EXPERTS + 1 + 63) / 64;  // counts per lane
 __device__ void route_items(const RouteArgs& a, int* s_cnt, int* s_off, bool write) {
   const int tid = threadIdx.x, E = a.nloc, n = E + 1, bmc = a.bmc;  // over the local experts
+  const int lg = 31 - __builtin_clz(bmc);
   if (tid == 0) s_cnt[E] = a.S;  // the shared expert takes every token
   __syncthreads();
   if (tid < 64) {
     const int lane = tid, per = (n + 63) / 64, e0 = lane * per;
-    int c_loc = 0, i_loc = 0;
-    for (int u = 0; u < per; ++u) {
-      const int e = e0 + u;
-      if (e < n) {
-        const int c = s_cnt[e];
-        c_loc += c;
-        i_loc += (c + bmc - 1) / bmc;
-      }
-    }
-    int c_inc = c_loc, i_inc = i_loc;
+    int cnt[kMaxRun];
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int oc = __shfl_up(c_inc, off, 64), oi = __shfl_up(i_inc, off, 64);
-      if (lane >= off) {
-        c_inc += oc;
-        i_inc += oi;
-      }
+    for (int u = 0; u < kMaxRun; ++u) cnt[u] = (u < per && e0 + u < n) ? s_cnt[e0 + u] : 0;
+    int c_loc = 0, i_loc = 0;
+#pragma unroll
+    for (int u = 0; u < kMaxRun; ++u) {
+      c_loc += cnt[u];
+      i_loc += (cnt[u] + bmc - 1) >> lg;
     }
-    const int nsh = (a.S + bmc - 1) / bmc;  // the shared expert's items
+    const int c_inc = wave_incl_scan_add(c_loc), i_inc = wave_incl_scan_add(i_loc);
+    const int nsh = (a.S + bmc - 1) >> lg;  // the shared expert's items
     int c_run = c_inc - c_loc, i_run = i_inc - i_loc;
-    for (int u = 0; u < per; ++u) {
+#pragma unroll
+    for (int u = 0; u < kMaxRun; ++u) {
       const int e = e0 + u;
-      if (e >= n) break;
-      const int c = s_cnt[e], ni = (c + bmc - 1) / bmc;
+      if (u >= per || e >= n) break;
+      const int c = cnt[u], ni = (c + bmc - 1) >> lg;
       s_off[e] = c_run;
       if (write) {
         a.counts[e] = c;
         a.offsets[e] = c_run;
         const int base = e == E ? 0 : i_run + nsh;
         for (int i = 0; i < ni; ++i) {
-          const int r0 = i * bmc;
+          const int r0 = i << lg;
           if (base + i < a.max_items) a.items[base + i] = make_int4(e, r0, min(bmc, c - r0), c_run + r0);
         }
       }
@@ -172,21 +168,34 @@ __device__ __forceinline__ float sigmoid_score(float l) {
 // its weight.  EPL = logits per lane (E <= 64 * EPL).  The key is the logit
 // (softmax scoring) or, for the sigmoid scoring, the fp32 score
 // s = 1 / (1 + e^-l) plus the expert's selection bias.
+// (in two parts: the row's loads, issued early where the caller has other
+// work to overlap with their trip to memory, and the selection)
 template <int EPL>
-__device__ __forceinline__ void wave_topk(const RouteArgs& a, int t, int lane, int& my_e, float& my_w) {
+struct TopkRow {
+  float lv[EPL], bv[EPL];
+};
+template <int EPL>
+__device__ __forceinline__ void topk_load(const RouteArgs& a, int t, int lane, TopkRow<EPL>& r) {
+  const int E = a.E;
+  const float* row = a.logits + (size_t)t * E;
+  // (loads clamped into the row rather than predicated, so they all issue
+  // before the first wait)
+#pragma unroll
+  for (int s = 0; s < EPL; ++s) r.lv[s] = row[min(s * 64 + lane, E - 1)];
+  if (a.scoring == QMOE_SCORING_SIGMOID) {
+#pragma unroll
+    for (int s = 0; s < EPL; ++s) r.bv[s] = a.bias ? a.bias[min(s * 64 + lane, E - 1)] : 0.0f;
+  }
+}
+template <int EPL>
+__device__ __forceinline__ void topk_pick(const RouteArgs& a, int t, int lane, const TopkRow<EPL>& r, int& my_e,
+                                          float& my_w) {
   const int E = a.E, k = a.k;
   const bool sig = a.scoring == QMOE_SCORING_SIGMOID;
   const float* row = a.logits + (size_t)t * E;
-  // (loads clamped into the row rather than predicated, so they all issue
-  // before the first wait; absent and taken experts have key 0, below every
-  // finite value's)
-  float lv[EPL], bv[EPL];
-#pragma unroll
-  for (int s = 0; s < EPL; ++s) lv[s] = row[min(s * 64 + lane, E - 1)];
-  if (sig) {
-#pragma unroll
-    for (int s = 0; s < EPL; ++s) bv[s] = a.bias ? a.bias[min(s * 64 + lane, E - 1)] : 0.0f;
-  }
+  const float* lv = r.lv;
+  const float* bv = r.bv;
+  // (absent and taken experts have key 0, below every finite value's)
   uint32_t key[EPL];
 #pragma unroll
   for (int s = 0; s < EPL; ++s) key[s] = (s * 64 + lane < E) ? ordered_key(sig ? sigmoid_score(lv[s]) + bv[s] : lv[s]) : 0u;
@@ -230,6 +239,12 @@ __device__ __forceinline__ void wave_topk(const RouteArgs& a, int t, int lane, i
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
   my_w = ex / sum;
+}
+template <int EPL>
+__device__ __forceinline__ void wave_topk(const RouteArgs& a, int t, int lane, int& my_e, float& my_w) {
+  TopkRow<EPL> r;
+  topk_load<EPL>(a, t, lane, r);
+  topk_pick<EPL>(a, t, lane, r, my_e, my_w);
 }
 
 // x -> fp16 operand format, one wave per token row: the row's largest |x|
@@ -285,13 +300,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_single_kernel(RouteArgs a
     if (t < a.M) convert_x_row(a, t, lane);
     return;
   }
+  // each wave's first token row goes out before the clears, which then
+  // overlap its trip to memory (up to 512 experts: with more, the row does
+  // not fit the registers left across the clears)
+  constexpr bool kEarly = EPL <= 8;
+  TopkRow<EPL> row;
+  if (kEarly && wave < a.M) topk_load<EPL>(a, wave, lane, row);
   for (int e = tid; e < E; e += nthr) cm[e][0] = cm[e][1] = 0u;
   for (int i = tid; i < a.n_tickets; i += nthr) a.tickets[i] = 0;
   __syncthreads();
   for (int t = wave; t < a.M; t += nw) {
     int my_e;
     float my_w;
-    wave_topk<EPL>(a, t, lane, my_e, my_w);
+    if (!kEarly || t != wave) topk_load<EPL>(a, t, lane, row);
+    topk_pick<EPL>(a, t, lane, row, my_e, my_w);
     if (lane < k) {
       a.ids[(size_t)t * k + lane] = my_e;
       a.wts[(size_t)t * k + lane] = my_w;

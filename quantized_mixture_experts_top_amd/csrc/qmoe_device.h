@@ -176,6 +176,25 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
+// Inclusive prefix sum over the wave's 64 lanes by DPP: shifts by 1, 2, 4
+// and 8 lanes within each row of 16 (lanes shifted in from outside the row
+// add 0), then row 0's total into row 1 and row 2's into row 3 (row_bcast:15),
+// and the total of rows 0-1 into rows 2-3 (row_bcast:31).  Rows a step does
+// not write keep `old` = 0 and add nothing.
+template <int kCtrl, int kRowMask, bool kBound>
+__device__ __forceinline__ int dpp_add_step(int v) {
+  return v + __builtin_amdgcn_update_dpp(0, v, kCtrl, kRowMask, 0xF, kBound);
+}
+__device__ __forceinline__ int wave_incl_scan_add(int v) {
+  v = dpp_add_step<0x111, 0xF, true>(v);   // row_shr:1
+  v = dpp_add_step<0x112, 0xF, true>(v);   // row_shr:2
+  v = dpp_add_step<0x114, 0xF, true>(v);   // row_shr:4
+  v = dpp_add_step<0x118, 0xF, true>(v);   // row_shr:8
+  v = dpp_add_step<0x142, 0xA, false>(v);  // row_bcast:15 into rows 1, 3
+  v = dpp_add_step<0x143, 0xC, false>(v);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 __device__ __forceinline__ float4_t mfma16x16x32(half8_t a, half8_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
