@@ -178,7 +178,9 @@ int qmoe_workspace_init(qmoe_layer* layer, void* workspace, size_t ws_bytes, voi
    route, gate+up, down, combine: four kernel launches,
    five for calls of more than 64 tokens (their routing takes two: the top-k
    of every token, then one block per 64-token chunk for the counts, the
-   scan, the sorted positions and the work list).
+   scan, the sorted positions and the work list), and two more in a mixed
+   call (QMOE_REGIME_MIXED: gate+up and down each also run the dot-product
+   GEMV over the experts of 1-2 rows).
    x: bf16 [M,H] (any finite values; see the ranges above); logits: fp32
    [M,E], finite; out: bf16 [M,H] (device pointers, 16-byte aligned).
    M == 0 is a no-op.  Graph-capturable for a fixed M (no memset nodes). */
@@ -285,7 +287,8 @@ typedef struct {
   uint64_t workspace_bytes_last;
   uint64_t workspace_bytes_peak;
   uint64_t prefill_tiles;     /* gate+up launches on 128-row MFMA tiles */
-  uint64_t gemv_tiles;        /* gate+up launches on <= 2-row dot-product items */
+  uint64_t gemv_tiles;        /* gate+up launches on <= 2-row dot-product items
+                                 (a mixed call counts one of each) */
   uint64_t gemv_nt_launches;  /* dot-product launches (gate+up and down) reading the
                                  weight codes with the non-temporal cache policy:
                                  calls with M*top_k <= E and no shared expert */
@@ -303,10 +306,14 @@ int qmoe_reset_stats(qmoe_layer* layer);
    prefill", sections "Summary" and "Engagement and fallback proof". */
 #define QMOE_REGIME_GEMV 1   /* dot-product GEMV on work items of <= 2 routed rows */
 #define QMOE_REGIME_TILES 2  /* 128-row MFMA tiles */
+#define QMOE_REGIME_MIXED 3  /* tiles for the experts of more than 2 rows and the
+                                dot-product GEMV (one more launch per product) for
+                                those of 1-2 rows: tile-regime calls that average
+                                at most 4 routed rows per expert */
 typedef struct {
   uint64_t seq;             /* 1-based number of the forward call on this handle */
   int64_t M;
-  int32_t regime;           /* QMOE_REGIME_GEMV or QMOE_REGIME_TILES */
+  int32_t regime;           /* QMOE_REGIME_GEMV, _TILES or _MIXED */
   int32_t rows_per_item;    /* routed rows per work item: 2 or 128 */
   int32_t nt_codes;         /* 1: the GEMV read weight codes non-temporal */
   int32_t shared_expert;    /* 1: a shared expert was applied */
@@ -314,7 +321,9 @@ typedef struct {
   int32_t route_kernels;    /* 1 (calls of <= 64 tokens) or 2 */
   int64_t max_items;        /* work items the GEMM grids were sized for (an upper
                                bound of the items routing builds) */
-  int64_t gate_up_blocks;   /* grid sizes of the launches */
+  int64_t gate_up_blocks;   /* grid sizes of the launches (a mixed call: of its
+                               tile launches; its dot-product launches have
+                               local experts x column blocks) */
   int64_t down_blocks;
   int64_t combine_blocks;
   uint64_t workspace_bytes; /* workspace bytes the call used */

@@ -64,7 +64,7 @@ class Receipt(ctypes.Structure):
 
     def as_dict(self) -> dict:
         d = {n: int(getattr(self, n)) for n, _ in self._fields_}
-        d["regime"] = {1: "gemv", 2: "tiles"}.get(d["regime"], d["regime"])
+        d["regime"] = {1: "gemv", 2: "tiles", 3: "mixed"}.get(d["regime"], d["regime"])
         return d
 
 

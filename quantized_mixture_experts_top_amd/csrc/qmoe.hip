@@ -42,7 +42,7 @@ namespace {
 
 constexpr int kThreads = 256;   // every kernel: 4 waves of 64
 constexpr int kChunk = 64;      // tokens per routing chunk = bits of one mask word
-constexpr int kCtrlWords = 64;  // [1] number of work items
+constexpr int kCtrlWords = 64;  // [1] work items, [2] a mixed call's dot-product items
 constexpr int kKStep = 128;     // inputs per K-step of a wave (4 lane groups x 32)
 
 // Shape of the 128-row MFMA tiles: MB row blocks of 16 per work item, NBW
@@ -78,6 +78,8 @@ struct RouteArgs {
   int* perm;
   int* inv_perm;
   int4* items;
+  int4* items_gv;  // a mixed call: one dot-product item per expert of 1..gv rows (gv = 0: none)
+  int gv;
   uint4* xa;   // fp16 A-format [M, H], row t times 2^-xexp[t]
   int* xexp;   // [M] per-token exponent
   int* tickets;    // the GEMV split-K tickets, cleared here for the call
@@ -114,20 +116,28 @@ __device__ void route_items(const RouteArgs& a, int* s_cnt, int* s_off, bool wri
     int cnt[kMaxRun];
 #pragma unroll
     for (int u = 0; u < kMaxRun; ++u) cnt[u] = (u < per && e0 + u < n) ? s_cnt[e0 + u] : 0;
-    int c_loc = 0, i_loc = 0;
+    // (a mixed call: a routed expert of 1..gv rows takes one dot-product
+    // item instead of tile items)
+    auto light = [&](int e, int c) { return e < E && c >= 1 && c <= a.gv; };
+    int c_loc = 0, i_loc = 0, g_loc = 0;
 #pragma unroll
     for (int u = 0; u < kMaxRun; ++u) {
+      const bool lt = light(e0 + u, cnt[u]);
       c_loc += cnt[u];
-      i_loc += (cnt[u] + bmc - 1) >> lg;
+      i_loc += lt ? 0 : (cnt[u] + bmc - 1) >> lg;
+      g_loc += lt ? 1 : 0;
     }
     const int c_inc = wave_incl_scan_add(c_loc), i_inc = wave_incl_scan_add(i_loc);
+    const int g_inc = a.gv ? wave_incl_scan_add(g_loc) : 0;
     const int nsh = (a.S + bmc - 1) >> lg;  // the shared expert's items
-    int c_run = c_inc - c_loc, i_run = i_inc - i_loc;
+    int c_run = c_inc - c_loc, i_run = i_inc - i_loc, g_run = g_inc - g_loc;
 #pragma unroll
     for (int u = 0; u < kMaxRun; ++u) {
       const int e = e0 + u;
       if (u >= per || e >= n) break;
-      const int c = cnt[u], ni = (c + bmc - 1) >> lg;
+      const int c = cnt[u];
+      const bool lt = light(e, c);
+      const int ni = lt ? 0 : (c + bmc - 1) >> lg;
       s_off[e] = c_run;
       if (write) {
         a.counts[e] = c;
@@ -137,15 +147,18 @@ __device__ void route_items(const RouteArgs& a, int* s_cnt, int* s_off, bool wri
           const int r0 = i << lg;
           if (base + i < a.max_items) a.items[base + i] = make_int4(e, r0, min(bmc, c - r0), c_run + r0);
         }
+        if (lt) a.items_gv[g_run] = make_int4(e, 0, c, c_run);
       }
       c_run += c;
       i_run += ni;
+      g_run += lt ? 1 : 0;
     }
     if (lane == 63) {
       s_off[n] = c_run;
       if (write) {
         a.offsets[n] = c_run;
         a.ctrl[1] = min(i_run, a.max_items);
+        a.ctrl[2] = g_run;
       }
     }
   }
@@ -435,6 +448,7 @@ struct GemmArgs {
   const uint16_t* s_sh;
   int E, K, N, Nw, nblk, max_items, T, k, M, R;
   const int* ctrl;
+  int count_at;  // the ctrl word holding the item count: 1, or 2 for a mixed call's dot-product items
   const int4* items;
   const int* perm;
   const float* wts;
@@ -578,7 +592,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   // the item is read together with the item count (clamped into the list,
   // so both loads go out at once; a block past the count then returns)
   const int4 it = g.items[min(item, g.max_items - 1)];
-  const int n_items = min(g.ctrl[1], g.max_items);
+  const int n_items = min(g.ctrl[g.count_at], g.max_items);
   if (item >= n_items) return;
   const int e = it.x, nr = it.z, pos0 = it.w;
   // work items come from the workspace: reject any that do not fit it
@@ -1181,7 +1195,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kGemvW
   // the item is read together with the item count (clamped into the list,
   // so both loads go out at once; a block past the count then returns)
   const int4 it = g.items[min(item, g.max_items - 1)];
-  const int n_items = min(g.ctrl[1], g.max_items);
+  const int n_items = min(g.ctrl[g.count_at], g.max_items);
   if (item >= n_items) return;
   const int e = it.x, nr = it.z, pos0 = it.w;
   if (e < 0 || e > g.E || nr <= 0 || nr > kGemvRows || pos0 < 0 || pos0 > g.R - nr) return;
@@ -1797,7 +1811,8 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
   int64_t T, S, R, C, max_items_all;
-  size_t ctrl, ids, wts, counts, offsets, perm, inv_perm, items, xexp, logits, xa, h, y, part, tickets, total;
+  size_t ctrl, ids, wts, counts, offsets, perm, inv_perm, items, items_gv, xexp, logits, xa, h, y, part, tickets,
+      total;
   int splits_gu, splits_dn;  // GEMV split-K of the call (1 = none)
   int64_t n_tickets;
 };
@@ -1881,6 +1896,7 @@ Layout make_layout(const qmoe_layer* L, int64_t M) {
   l.perm = take(l.R * 4);
   l.inv_perm = take(l.T * 4);
   l.items = take(l.max_items_all * 16);
+  l.items_gv = take(L->nloc * 16);
   l.xexp = take(M * 4);
   l.logits = take(M * E * 4);  // router logits of qmoe_forward_router
   l.xa = take(M * H * 2);
@@ -1918,6 +1934,23 @@ Regime regime_of(const qmoe_layer* L, int64_t M) {
   return kPrefill;
 }
 int rows_per_item(Regime rg) { return rg == kGemv ? kGemvRows : kPrefillRows; }
+
+// A mixed call: in the tile regime, while calls average at most
+// kMixedMaxRowsPerExpert routed rows per expert, a routed expert of 1 or 2
+// rows takes one dot-product GEMV item (a second work list) instead of a
+// 128-row tile item: the GEMV streams an expert's weights faster per block
+// than a tile does, and such an expert's tile computes mostly zero rows.
+// Each product then runs the tile launch and a GEMV launch over that list.
+// Measured on MI355X (E=384, H=7168, I=2048, top-8): at M=90 (1.9 rows per
+// expert, two thirds of the touched experts light) the call 1,700 -> 1,539
+// us; at 256 tokens (5.3 rows, a tenth light) and on the skewed 512-token
+// call within 1%, while the I=256 and 48-expert slices at 256 tokens ran
+// 5-7% slower (the extra launches outweigh their few light experts).
+constexpr int kMixedMaxRowsPerExpert = 4;
+bool mixed_call(const qmoe_layer* L, int64_t M) {
+  return regime_of(L, M) == kPrefill && M * L->d.top_k <= kMixedMaxRowsPerExpert * (int64_t)L->d.E &&
+         L->d.H <= kGemvMaxK && L->d.I <= kGemvMaxK;
+}
 
 // Split-K of a GEMV launch: a grid of fewer than kSplitMaxTiles blocks (a
 // few experts with narrow rows: one GPU's share of a tensor-parallel layer
@@ -2015,6 +2048,8 @@ int do_route(qmoe_layer* L, const void* x, const float* logits, int64_t M, void*
   a.perm = at<int>(ws, lay.perm);
   a.inv_perm = at<int>(ws, lay.inv_perm);
   a.items = at<int4>(ws, lay.items);
+  a.items_gv = at<int4>(ws, lay.items_gv);
+  a.gv = mixed_call(L, M) ? kGemvRows : 0;
   a.xa = at<uint4>(ws, lay.xa);
   a.xexp = at<int>(ws, lay.xexp);
   a.tickets = at<int>(ws, lay.tickets);
@@ -2060,6 +2095,7 @@ void fill_gemm_args(const qmoe_layer* L, int64_t M, void* ws, const Layout& lay,
   g.R = (int)lay.R;
   g.k = L->d.top_k;
   g.ctrl = at<int>(ws, lay.ctrl);
+  g.count_at = 1;
   g.items = at<int4>(ws, lay.items);
   g.perm = at<int>(ws, lay.perm);
   g.wts = at<float>(ws, lay.wts);
@@ -2113,21 +2149,28 @@ int launch_gemm(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream
 }
 
 template <bool GATEUP>
-int launch_gemv(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t st) {
+int launch_gemv(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t st, bool mixed = false) {
   constexpr int WN = kThreads / 64;
   GemmArgs g;
   fill_gemm_args<GATEUP>(L, M, ws, lay, g);
-  g.max_items = (int)max_items_for(lay.T, M, lay.S, L->nloc, kGemvRows);
+  if (mixed) {  // the light experts' list of a mixed call: at most one item per local expert
+    g.items = at<int4>(ws, lay.items_gv);
+    g.count_at = 2;
+    g.max_items = L->nloc;
+    g.splits = 1;
+  } else {
+    g.max_items = (int)max_items_for(lay.T, M, lay.S, L->nloc, kGemvRows);
+    g.splits = GATEUP ? lay.splits_gu : lay.splits_dn;
+  }
   const int cols = GATEUP ? 16 : 32;  // output columns per wave
   g.nblk = (int)ceil_div(g.N, WN * cols);
-  g.splits = GATEUP ? lay.splits_gu : lay.splits_dn;
   const int64_t blocks = (int64_t)g.nblk * g.max_items * g.splits;
   if (blocks > 0x7FFFFFFF) return fail(QMOE_ERR_UNSUPPORTED, "grid too large");
   const size_t lds = gemv_lds_bytes(g.K);
   // non-temporal code reads while each expert's codes are read about once:
   // at most one routed row per expert on average and no shared expert (whose
   // codes every item of the call reads)
-  const bool nt = M * L->d.top_k <= L->d.E && L->d.shared_w13 == nullptr;
+  const bool nt = !mixed && M * L->d.top_k <= L->d.E && L->d.shared_w13 == nullptr;
   if (nt) {
     gemv_kernel<GATEUP, true><<<dim3((unsigned)blocks), kThreads, lds, st>>>(g);
     L->gemv_nt++;
@@ -2135,7 +2178,7 @@ int launch_gemv(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream
     gemv_kernel<GATEUP, false><<<dim3((unsigned)blocks), kThreads, lds, st>>>(g);
   L->gemm_launches++;
   if (g.splits > 1) L->splitk_launches++;
-  if (t_rc) {
+  if (t_rc && !mixed) {
     t_rc->max_items = g.max_items;
     t_rc->nt_codes = nt ? 1 : 0;
     (GATEUP ? t_rc->splits_gate_up : t_rc->splits_down) = g.splits;
@@ -2150,12 +2193,17 @@ int do_gate_up(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_
     return launch_gemv<true>(L, M, ws, lay, st);
   }
   L->prefill_tiles++;
-  return launch_gemm<kTileMB, kGuWN, kGuNBW, true>(L, M, ws, lay, st);
+  const int rc = launch_gemm<kTileMB, kGuWN, kGuNBW, true>(L, M, ws, lay, st);
+  if (rc != QMOE_OK || !mixed_call(L, M)) return rc;
+  L->gemv_tiles++;
+  return launch_gemv<true>(L, M, ws, lay, st, true);
 }
 
 int do_down(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream_t st) {
   if (regime_of(L, M) == kGemv) return launch_gemv<false>(L, M, ws, lay, st);
-  return launch_gemm<kTileMB, kDnWN, kDnNBW, false>(L, M, ws, lay, st);
+  const int rc = launch_gemm<kTileMB, kDnWN, kDnNBW, false>(L, M, ws, lay, st);
+  if (rc != QMOE_OK || !mixed_call(L, M)) return rc;
+  return launch_gemv<false>(L, M, ws, lay, st, true);
 }
 
 int do_combine(qmoe_layer* L, int64_t M, void* out, void* ws, const Layout& lay, hipStream_t st) {
@@ -2319,7 +2367,7 @@ int forward_impl(qmoe_layer* L, const void* x, const float* logits, int64_t M, v
   qmoe_receipt r{};
   r.M = M;
   const Regime rg = regime_of(L, M);
-  r.regime = rg == kGemv ? QMOE_REGIME_GEMV : QMOE_REGIME_TILES;
+  r.regime = rg == kGemv ? QMOE_REGIME_GEMV : mixed_call(L, M) ? QMOE_REGIME_MIXED : QMOE_REGIME_TILES;
   r.rows_per_item = rows_per_item(rg);
   r.shared_expert = L->shared ? 1 : 0;
   r.route_kernels = lay.C == 1 ? 1 : 2;

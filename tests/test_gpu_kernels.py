@@ -160,6 +160,12 @@ FWD_CASES = [
     (4, 1536, 1536, 1, 400, True),
     (4, 1536, 1536, 1, 500, False),
     (4, 1536, 1536, 1, 500, True),
+    # mixed calls (tiles, at most 4 rows per expert on average): experts of
+    # 1-2 rows on the dot-product GEMV, the rest (and the shared expert) on
+    # tiles, every token compared
+    (64, 1024, 512, 4, 40, False),
+    (64, 1024, 512, 4, 40, True),
+    (32, 2048, 1536, 4, 30, True),   # 4 whole super-steps in gate+up, 3 in down
 ]
 
 
@@ -445,11 +451,14 @@ def test_counters_and_workspace_accounting():
     layer.reset_stats()
     layer.forward(x, lg)
     s = layer.stats()
+    # 16 tokens x top-2 over 8 experts: tiles, 4 rows per expert on average,
+    # so a mixed call (each product also runs the dot-product GEMV)
+    assert layer.receipt()["regime"] == "mixed"
     assert s["forward_calls"] == 1 and s["route_calls"] == 1
-    assert s["gemm_launches"] == 2 and s["launches"] == 4
+    assert s["gemm_launches"] == 4 and s["launches"] == 6
     assert s["workspace_inits"] == 0
     assert s["workspace_bytes_last"] == s["workspace_bytes_peak"] == layer.workspace_bytes(16) > 0
-    assert s["prefill_tiles"] + s["gemv_tiles"] == 1
+    assert s["prefill_tiles"] == 1 and s["gemv_tiles"] == 1
     assert s["gemv_nt_launches"] == 0  # 16 tokens x top-2 > 8 experts
 
 
@@ -479,7 +488,8 @@ def test_errors_from_the_library():
     (64, 1024, 512, 4, 9, False),    # GEMV, codes non-temporal (M*k <= E, no shared expert)
     (64, 1024, 512, 4, 20, True),    # GEMV with a shared expert (default cache policy)
     (64, 1024, 512, 4, 130, True),   # tiles; routing in two kernels (more than 64 tokens)
-    (8, 256, 128, 2, 16, False),     # tiles; one routing kernel
+    (8, 256, 128, 2, 16, False),     # mixed (4 rows per expert); one routing kernel
+    (64, 1024, 512, 4, 40, True),    # mixed with a shared expert (always on tiles)
 ])
 def test_receipt_exact_counts(E, H, I, k, M, shared):
     """The per-call receipt names the regime, cache policy, launches, grid
@@ -494,18 +504,20 @@ def test_receipt_exact_counts(E, H, I, k, M, shared):
     r = layer.receipt()
     counts = oracle_moe.route(lg, k)["counts"]
     gemv = 4 * M * k <= 7 * E
+    mixed = not gemv and M * k <= 4 * E  # experts of 1-2 rows then leave the tile list
     rpi = 2 if gemv else 128
-    items = sum(math.ceil(int(c) / rpi) for c in counts) + (math.ceil(M / rpi) if shared else 0)
+    items = sum(math.ceil(int(c) / rpi) for c in counts if not (mixed and 1 <= c <= 2)) + \
+        (math.ceil(M / rpi) if shared else 0)
     T = M * k
     max_items = T // rpi + min(E, T) + (math.ceil(M / rpi) if shared else 0)
     say(f"receipt E={E} M={M} shared={shared}: {r}; device items {layer.item_count(M)} (expected {items})")
     assert layer.item_count(M) == items
     assert r["seq"] == 2 and r["M"] == M
-    assert r["regime"] == ("gemv" if gemv else "tiles") and r["rows_per_item"] == rpi
+    assert r["regime"] == ("gemv" if gemv else "mixed" if mixed else "tiles") and r["rows_per_item"] == rpi
     assert r["nt_codes"] == int(gemv and T <= E and not shared)
     assert r["shared_expert"] == int(shared) and r["static_scratch"] == 0
     assert r["route_kernels"] == (1 if M <= 64 else 2)
-    assert r["launches"] == 3 + r["route_kernels"]
+    assert r["launches"] == 3 + r["route_kernels"] + (2 if mixed else 0)
     assert r["max_items"] == max_items >= items
     if gemv:
         # a launch of fewer than 128 blocks splits K (about 512 blocks in all,
