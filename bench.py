@@ -143,18 +143,23 @@ def is_gate_up_kernel(name: str) -> bool:
 
 
 def summarize_counters(key: str, fetch_csv: str, write_csv: str, path: str = COUNTERS) -> int:
-    """Mean HBM bytes per gate+up dispatch from one FETCH_SIZE and one
-    WRITE_SIZE counter pass (rocprofv3 csv), scaled by the copy calibration,
-    stored under `key` with the current source hash (entries taken on other
-    sources are dropped)."""
+    """HBM bytes of a call's gate+up stage (its one launch, or in a mixed call
+    its tile launch and its dot-product launch together), mean over the calls
+    of one FETCH_SIZE and one WRITE_SIZE counter pass (rocprofv3 csv), scaled
+    by the copy calibration, stored under `key` with the current source hash
+    (entries taken on other sources are dropped)."""
     def per_dispatch(p, counter):
-        vals = {}
+        vals, tiles = {}, set()
         for r in csv.DictReader(open(p)):
             if r["Counter_Name"] == counter and is_gate_up_kernel(r["Kernel_Name"]):
                 vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+                if "gemm_kernel<" in r["Kernel_Name"]:
+                    tiles.add(r["Dispatch_Id"])
         if not vals:
             raise SystemExit(f"no gate+up dispatches with {counter} in {p}")
-        return statistics.mean(vals.values())
+        # a tile call has one tile launch (plus a dot-product one when mixed),
+        # a dot-product call one dot-product launch
+        return sum(vals.values()) / (len(tiles) or len(vals))
     b = per_dispatch(fetch_csv, "FETCH_SIZE") * 1024 * FETCH_FACTOR + \
         per_dispatch(write_csv, "WRITE_SIZE") * 1024 * WRITE_FACTOR
     c = {}
@@ -165,8 +170,9 @@ def summarize_counters(key: str, fetch_csv: str, write_csv: str, path: str = COU
             c = {}
     if c.get("source_sha256_16") != source_hash():
         c = {"source_sha256_16": source_hash()}
-    c["note"] = (f"HBM bytes per gate+up launch (read + written, mean over the launches of `bench.py --only "
-                 f"<workload>:<M>`), FETCH_SIZE x {FETCH_FACTOR:.3f} and WRITE_SIZE x {WRITE_FACTOR:.3f} "
+    c["note"] = (f"HBM bytes per gate+up stage (read + written, mean over the calls of `bench.py --only "
+                 f"<workload>:<M>`; a mixed call's tile and dot-product launches together), "
+                 f"FETCH_SIZE x {FETCH_FACTOR:.3f} and WRITE_SIZE x {WRITE_FACTOR:.3f} "
                  f"(factors from a 1 GiB device copy: bench.py --calibrate-copy)")
     c.setdefault("gate_up_bytes_per_launch", {})[key] = int(round(b))
     with open(path, "w") as f:
