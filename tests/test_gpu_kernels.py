@@ -330,7 +330,10 @@ def test_uninitialised_workspace(M):
     assert torch.equal(out.view(torch.int16), want.view(torch.int16))
 
 
-@pytest.mark.parametrize("M", [9, 130])  # GEMV items, one routing block; tiles, three meeting at a ticket
+# GEMV items, one routing block; a mixed call (2.5 rows per expert: tiles and
+# the dot-product GEMV over the experts of 1-2 rows); tiles, three routing
+# blocks meeting at a ticket
+@pytest.mark.parametrize("M", [9, 40, 130])
 def test_graph_capture_replays_match_eager(M):
     """The whole forward captured into a HIP graph (fixed M; workspace,
     inputs and output allocated before the capture) replays to the eager
