@@ -56,8 +56,10 @@ constexpr int kKStep = 128;     // inputs per K-step of a wave (4 lane groups x 
 constexpr int kTileMB = 8;  // row blocks of 16 per tile
 constexpr int kGuWN = 4, kGuNBW = 2, kGuWPE = 2;
 constexpr int kDnWN = 8, kDnNBW = 1, kDnWPE = 4;
-// Gate+up K loops of up to this many 16-row blocks issue their weights in
-// line-half pairs: 2-4% faster at 90-1024 tokens on the 384-expert layer.
+// Gate+up K loops of up to this many 16-row blocks issue their weights two
+// sub-steps at a time: 2-4% faster at 90-1024 tokens on the 384-expert layer
+// (measured with the codes in row order, where the two sub-steps were the
+// halves of each row's 128-byte line).
 // Larger gate+up loops have no registers left for the extra live fragment
 // (it spills); in the down tiles pairing measured neutral to 3-5% slower.
 constexpr int kGuPairRowBlocks = 4;
@@ -563,8 +565,9 @@ constexpr int kSuper = 4 * kKStep;     // inputs per super-step (16 groups)
 //
 // K is walked in super-steps of 512 inputs (16 groups of 32).  In sub-step
 // u lane group kq (= lane/16) decodes group 4u + kq: the 16 code bytes at
-// 64u + 16kq of the row's 256-byte chunk, so the four lanes of a row read
-// 64 contiguous bytes.  The scales come from one 8-byte load per row and
+// 64u + 16kq of the row's 256-byte chunk, which the codes' tile order
+// (the layer's copy) puts at 16 * lane of the block's 1 KiB for the
+// sub-step, so one load instruction reads 1 KiB contiguous.  The scales come from one 8-byte load per row and
 // super-step (lane kq: groups 4kq..4kq+3) and a transpose across the row's
 // four lanes.  The MFMA k-slot order is free as long as the activations
 // follow it, so the activation fragment of sub-step u, MFMA i is inputs
@@ -612,11 +615,13 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   const __amdgpu_buffer_rsrc_t rS = buffer_rsrc(sbase, (uint32_t)g.Nw * KG * 2);
   const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(g.a, g.a_bytes);
 
-  // offsets of this lane's code chunk and scale quad within a 16-row B
-  // block (vector), and each B block's first weight row (wave-uniform, so
-  // it rides in the scalar offset; the lane part alone is bounds-checked
-  // and every in-range lane stays inside the weights)
-  const uint32_t bl = (uint32_t)r * K2 + 16 * kq, sl = (uint32_t)r * KG * 2 + 8 * kq;
+  // offsets of this lane's code chunk (tile order: lane l's 16 bytes of a
+  // sub-step at 16 l of the block's 1 KiB for it, so a load instruction
+  // reads 1 KiB contiguous) and scale quad within a 16-row B block
+  // (vector), and each B block's first weight row (wave-uniform, so it
+  // rides in the scalar offset; the lane part alone is bounds-checked and
+  // every in-range lane stays inside the weights)
+  const uint32_t tl = 16u * (uint32_t)lane, sl = (uint32_t)r * KG * 2 + 8 * kq;
   const uint32_t sl2 = (uint32_t)r * KG * 2 + 16 * kq;
   uint32_t brow[NBB];
   int col0[NBW];
@@ -651,19 +656,20 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
 #pragma unroll
     for (int b = 0; b < NBB; ++b)
       f.b[b] = __builtin_bit_cast(
-          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rB, ok ? bl + 64 * u : kOob, S * (kSuper / 2) + brow[b] * K2, 0));
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rB, ok ? tl + 1024u * u : kOob, S * (kSuper * 8) + brow[b] * K2, 0));
   };
-  // the codes of sub-steps u and u + 1 of super-step S: per B block the two
-  // halves of the same 128-byte line of each row, issued back to back (a
-  // line's halves requested in adjacent instructions are served at the full
-  // streaming rate, a sub-step apart at about 12% less on MI355X)
+  // the codes of sub-steps u and u + 1 of super-step S: per B block 2 KiB
+  // contiguous in the tile order, issued back to back (in row order these
+  // were the halves of each row's 128-byte line, served at the full
+  // streaming rate when requested in adjacent instructions, a sub-step
+  // apart at about 12% less on MI355X)
   auto load_b2 = [&](int S, int u, Frag<NBB>& f0, Frag<NBB>& f1, bool ok) __attribute__((always_inline)) {
 #pragma unroll
     for (int b = 0; b < NBB; ++b) {
       f0.b[b] = __builtin_bit_cast(
-          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rB, ok ? bl + 64 * u : kOob, S * (kSuper / 2) + brow[b] * K2, 0));
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rB, ok ? tl + 1024u * u : kOob, S * (kSuper * 8) + brow[b] * K2, 0));
       f1.b[b] = __builtin_bit_cast(
-          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rB, ok ? bl + 64 * (u + 1) : kOob, S * (kSuper / 2) + brow[b] * K2, 0));
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rB, ok ? tl + 1024u * (u + 1) : kOob, S * (kSuper * 8) + brow[b] * K2, 0));
     }
   };
   // the four scales of super-step S, as two dwords per B block
@@ -860,7 +866,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
       _Pragma("unroll") for (int b = 0; b < NBB; ++b) {                                          \
         if (b % 4 == i)                                                                          \
           (FNN).b[b] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(        \
-              rB, bl + 64 * (UB), (SB) * (kSuper / 2) + brow[b] * K2, 0));                       \
+              rB, tl + 1024u * (UB), (SB) * (kSuper * 8) + brow[b] * K2, 0));                       \
       }                                                                                          \
       half8_t* cur_ = (i & 1) ? bfb_ : bfa_;                                                     \
       half8_t* nxt_ = (i & 1) ? bfa_ : bfb_;                                                     \
@@ -895,7 +901,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
     __syncthreads();                                                                             \
   } while (0)
   // The same with the weights of the two sub-steps after next issued as
-  // line-half pairs (FN0, FN1), or with no weights (a sub-step whose pair
+  // pairs (FN0, FN1), or with no weights (a sub-step whose pair
   // went out with the previous one's).  All loads are waited for except the
   // pair just issued.
 #define QMOE_SUBSTEP_PAIR(U, FCUR, SA, UA, SB, UB, FN0, FN1, BUF)                               \
@@ -976,7 +982,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
         const bool second = ((S - S_begin) & 1) != 0;
         if (!kPair) load_sc(Sn, sc_nxt, true);
         if constexpr (GATEUP && NMBC <= kGuPairRowBlocks) {
-          // weights in line-half pairs: sub-steps 2 and 3 go out with
+          // weights two sub-steps at a time: sub-steps 2 and 3 go out with
           // sub-step 0, the next super-step's 0 and 1 with sub-step 2.  The
           // next scale pair goes out with sub-step 3's tile, whose deadline
           // it shares: held from there to its use it takes no registers
@@ -1136,8 +1142,11 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
 // weight row, 16 groups of 32.  Lane (q, j) of a wave (q = lane/16) takes
 // group j of every super-step, for rows 4m + q (m = 0..3) of each 16-row
 // weight block, so one load instruction reads four whole 256-byte chunks
-// (eight full cache lines), and a lane reads its group's activations once
-// per super-step for all of its rows.  Each lane loads its group's scale
+// (eight full cache lines) of the codes as the caller gave them, in row
+// order (the MFMA tiles read the layer's tile-order copy instead: in that
+// order these loads would read 64-byte halves of 16 lines, which measured
+// 15-27% slower), and a lane reads its group's activations once per
+// super-step for all of its rows.  Each lane loads its group's scale
 // per row.  The 16 lanes of a row hold partial sums over different groups;
 // a butterfly over those lanes adds them once, after the K loop.
 //
@@ -1214,9 +1223,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kGemvW
   const __amdgpu_buffer_rsrc_t rS = buffer_rsrc(sbase, (uint32_t)g.Nw * KG * 2);
   const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(g.a, g.a_bytes);
 
-  // lane part of the code and scale offsets (row q, group j), and each
-  // block's first weight row (wave-uniform, in the scalar offset; every
-  // in-range lane stays inside the weights)
+  // lane part of the code and scale offsets (row q, group j; the codes as
+  // the caller gave them, in row order), and each block's first weight row
+  // (wave-uniform, in the scalar offset; every in-range lane stays inside
+  // the weights)
   const uint32_t bl = (uint32_t)q * K2 + 16 * j, sl = (uint32_t)q * KG * 2 + 2 * j;
   uint32_t brow[NBB];
   int col0[NBW];
@@ -1753,15 +1763,31 @@ __global__ __launch_bounds__(kRouterThreads) void router_tile_kernel(RouterArgs 
 }
 
 
+// ------------------------------------------------------- code tile order
+
+// The layer's copy of a code array in tile order (tiled_code_offset): one
+// thread per 16-byte chunk of the destination, so the writes are whole
+// lines; rows is a multiple of 16 and K2 = K/2 of 64.
+__global__ __launch_bounds__(kThreads) void tile_codes_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                               long long chunks, int K2) {
+  const long long c = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (c >= chunks) return;
+  const long long blk = c / K2;  // 16-row block: 16 * K2 bytes = K2 chunks
+  const int w = (int)(c % K2), sub = w / 64, l = w % 64;
+  const long long n = blk * 16 + (l & 15);  // row r = l % 16, lane part kq = l / 16
+  dst[c] = src[(n * K2 + sub * 64 + (l >> 4) * 16) / 16];
+}
+
 // ------------------------------------------------------------- inspection
 
+// w: one expert's codes in tile order (K2 = K/2 bytes per row)
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t* w, const uint16_t* s, int N,
                                                             int K, uint16_t* out) {
   const long long idx = (long long)blockIdx.x * kThreads + threadIdx.x;
   const int per_row = K / 8;
   if (idx >= (long long)N * per_row) return;
   const int n = (int)(idx / per_row), d = (int)(idx % per_row);
-  half8_t v = dq8(w[idx], s[(size_t)n * (K / 32) + d / 4]);
+  half8_t v = dq8(w[tiled_code_offset(n, 4 * (size_t)d, K / 2) / 4], s[(size_t)n * (K / 32) + d / 4]);
 #pragma unroll
   for (int p = 0; p < 8; ++p)
     if (x16_pos(p)) v[p] = v[p] * (_Float16)0.0625f;  // exact: undo the operand's x16
@@ -1866,6 +1892,10 @@ struct qmoe_layer {
   std::atomic<uint64_t> receipt_seq{0};  // forward calls since creation (not reset by qmoe_reset_stats)
   std::atomic<uint64_t> forward_calls{0}, route_calls{0}, gemm_launches{0}, launches{0}, inits{0},
       ws_last{0}, ws_peak{0}, prefill_tiles{0}, gemv_tiles{0}, gemv_nt{0}, splitk_launches{0};
+  // the codes in tile order: one device allocation made at creation and
+  // freed at destruction (the descriptor's code pointers are read once)
+  void* tiled = nullptr;
+  const uint8_t *w13 = nullptr, *w2 = nullptr, *sh_w13 = nullptr, *sh_w2 = nullptr;
 };
 
 namespace {
@@ -2104,9 +2134,9 @@ void fill_gemm_args(const qmoe_layer* L, int64_t M, void* ws, const Layout& lay,
   g.part = at<float>(ws, lay.part);
   g.tickets = at<int>(ws, lay.tickets);
   if (GATEUP) {
-    g.w = L->d.w13;
+    g.w = L->w13;
     g.s = L->d.s13;
-    g.w_sh = L->d.shared_w13;
+    g.w_sh = L->sh_w13;
     g.s_sh = L->d.shared_s13;
     g.K = H;
     g.N = I;
@@ -2116,9 +2146,9 @@ void fill_gemm_args(const qmoe_layer* L, int64_t M, void* ws, const Layout& lay,
     g.h_out = at<_Float16>(ws, lay.h);
     g.y_out = nullptr;
   } else {
-    g.w = L->d.w2;
+    g.w = L->w2;
     g.s = L->d.s2;
-    g.w_sh = L->d.shared_w2;
+    g.w_sh = L->sh_w2;
     g.s_sh = L->d.shared_s2;
     g.K = I;
     g.N = H;
@@ -2153,6 +2183,9 @@ int launch_gemv(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream
   constexpr int WN = kThreads / 64;
   GemmArgs g;
   fill_gemm_args<GATEUP>(L, M, ws, lay, g);
+  // the dot-product GEMV reads the codes as given (row order)
+  g.w = GATEUP ? L->d.w13 : L->d.w2;
+  g.w_sh = GATEUP ? L->d.shared_w13 : L->d.shared_w2;
   if (mixed) {  // the light experts' list of a mixed call: at most one item per local expert
     g.items = at<int4>(ws, lay.items_gv);
     g.count_at = 2;
@@ -2253,6 +2286,49 @@ int qmoe_version(void) { return QMOE_VERSION; }
 
 const char* qmoe_last_error(void) { return g_err.c_str(); }
 
+namespace {
+// The layer's codes in tile order: w13 [L, 2I, H/2] and w2 [L, H, I/2] of
+// the L local experts (and the shared expert's), copied once into one
+// allocation, which the MFMA tiles read (the dot-product GEMV reads the
+// caller's codes as given).  The device is synchronised before (the
+// caller's writes of the codes, on any stream, are complete) and after (the
+// copy is complete before any stream can use it).
+int make_tiled_codes(qmoe_layer* L) {
+  const int64_t H = L->d.H, I = L->d.I, nl = L->nloc;
+  if (hipDeviceSynchronize() != hipSuccess) return fail(QMOE_ERR_DEVICE, "hipDeviceSynchronize failed");
+  const int64_t b13 = 2 * I * (H / 2), b2 = H * (I / 2);  // code bytes of one expert
+  const int64_t total = nl * (b13 + b2) + (L->shared ? b13 + b2 : 0);
+  if (hipMalloc(&L->tiled, (size_t)total) != hipSuccess) {
+    L->tiled = nullptr;
+    (void)hipGetLastError();
+    return fail(QMOE_ERR_DEVICE, "cannot allocate " + std::to_string(total) + " bytes for the tile-ordered codes");
+  }
+  uint8_t* base = static_cast<uint8_t*>(L->tiled);
+  struct Part {
+    const void* src;
+    uint8_t* dst;
+    int64_t rows, K2;
+  };
+  const Part parts[4] = {{L->d.w13, base, nl * 2 * I, H / 2},
+                         {L->d.w2, base + nl * b13, nl * H, I / 2},
+                         {L->d.shared_w13, base + nl * (b13 + b2), 2 * I, H / 2},
+                         {L->d.shared_w2, base + nl * (b13 + b2) + b13, H, I / 2}};
+  for (int i = 0; i < (L->shared ? 4 : 2); ++i) {
+    const Part& p = parts[i];
+    const long long chunks = p.rows * p.K2 / 16;
+    tile_codes_kernel<<<dim3((unsigned)ceil_div(chunks, kThreads)), kThreads, 0, nullptr>>>(
+        static_cast<const uint4*>(p.src), reinterpret_cast<uint4*>(p.dst), chunks, (int)p.K2);
+    if (hipGetLastError() != hipSuccess) return fail(QMOE_ERR_LAUNCH, "tile_codes_kernel launch failed");
+  }
+  if (hipDeviceSynchronize() != hipSuccess) return fail(QMOE_ERR_DEVICE, "tiling the codes failed");
+  L->w13 = parts[0].dst;
+  L->w2 = parts[1].dst;
+  L->sh_w13 = L->shared ? parts[2].dst : nullptr;
+  L->sh_w2 = L->shared ? parts[3].dst : nullptr;
+  return QMOE_OK;
+}
+}  // namespace
+
 int qmoe_layer_create(const qmoe_layer_desc* d, qmoe_layer** out) {
   if (!out) return fail(QMOE_ERR_ARG, "out is NULL");
   *out = nullptr;
@@ -2306,11 +2382,19 @@ int qmoe_layer_create(const qmoe_layer_desc* d, qmoe_layer** out) {
   L->lo = d->local_count ? d->local_first : 0;
   L->nloc = d->local_count ? d->local_count : d->E;
   L->rscale = d->routed_scale == 0.0f ? 1.0f : d->routed_scale;
+  const int rc = make_tiled_codes(L);
+  if (rc != QMOE_OK) {
+    qmoe_layer_destroy(L);
+    return rc;
+  }
   *out = L;
   return QMOE_OK;
 }
 
-void qmoe_layer_destroy(qmoe_layer* L) { delete L; }
+void qmoe_layer_destroy(qmoe_layer* L) {
+  if (L && L->tiled) (void)hipFree(L->tiled);
+  delete L;
+}
 
 int qmoe_workspace_size(const qmoe_layer* L, int64_t M, size_t* bytes) {
   if (!L || !bytes) return fail(QMOE_ERR_ARG, "layer or bytes is NULL");
@@ -2512,10 +2596,10 @@ int qmoe_dequant_debug(qmoe_layer* L, int32_t expert, int32_t which, uint16_t* o
   const uint8_t* w;
   const uint16_t* s;
   if (expert < L->nloc) {
-    w = (which == 0 ? L->d.w13 : L->d.w2) + (size_t)expert * N * (K / 2);
+    w = (which == 0 ? L->w13 : L->w2) + (size_t)expert * N * (K / 2);
     s = (which == 0 ? L->d.s13 : L->d.s2) + (size_t)expert * N * (K / 32);
   } else {
-    w = which == 0 ? L->d.shared_w13 : L->d.shared_w2;
+    w = which == 0 ? L->sh_w13 : L->sh_w2;
     s = which == 0 ? L->d.shared_s13 : L->d.shared_s2;
   }
   const int64_t n = (int64_t)N * (K / 8);

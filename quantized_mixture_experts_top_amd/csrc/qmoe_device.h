@@ -89,6 +89,17 @@ __device__ __forceinline__ float pow2f(int n) { return __int_as_float((n + 127) 
 // 1/p for p = 2^n, n in [-126, 126] (exact; no division).
 __device__ __forceinline__ float inv_pow2f(float p) { return __int_as_float(0x7F000000 - __float_as_int(p)); }
 
+// Tile order of the weight codes (the library's copy; rows of K2 = K/2
+// bytes, K a multiple of 128): each 16-row block's codes are stored
+// sub-step by sub-step (128 inputs: 64 bytes of each of its 16 rows, 1 KiB),
+// and within a sub-step lane l = 16 kq + r's 16 bytes (row r, bytes
+// 16 kq .. 16 kq + 15 of the sub-step) sit at 16 l: the order in which one
+// wave's load instruction of an MFMA tile reads them, so that instruction
+// reads 1 KiB contiguous.  Byte offset of code byte b of row n:
+__host__ __device__ constexpr size_t tiled_code_offset(size_t n, size_t b, size_t K2) {
+  return (n / 16) * 16 * K2 + (b / 64) * 1024 + (((b % 64) / 16) * 16 + n % 16) * 16 + b % 16;
+}
+
 // h = SiLU(g) * u as stored: the product rounded to fp32, then to fp16.  The
 // empty asm pins the fp32 value, so the compiler cannot fuse the product into
 // the conversion (one rounding instead of two) in some kernels or

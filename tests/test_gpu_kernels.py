@@ -543,13 +543,18 @@ def test_receipt_exact_counts(E, H, I, k, M, shared):
 
 
 def _router_only_layer(E, H, max_rows):
-    """A layer handle for router calls only: the router kernels read no
-    expert weights, so tiny placeholder tensors stand in for them."""
+    """A layer handle for router calls only.  Creation copies the weight
+    codes into the layer's tile order, so the code arrays have their full
+    shapes (zeros, I = 128); the router kernels read no expert weights and
+    nothing reads the scales here, so a tiny placeholder stands in for
+    them."""
     import torch
     from quantized_mixture_experts_top_amd import Layer
-    ph = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    I = 128
+    w13 = torch.zeros((E, 2 * I, H // 2), dtype=torch.uint8, device="cuda")
+    w2 = torch.zeros((E, H, I // 2), dtype=torch.uint8, device="cuda")
     ps = torch.zeros(128, dtype=torch.int16, device="cuda")
-    return Layer(E=E, H=H, I=128, top_k=min(8, E), max_rows=max_rows, w13=ph, s13=ps, w2=ph, s2=ps)
+    return Layer(E=E, H=H, I=I, top_k=min(8, E), max_rows=max_rows, w13=w13, s13=ps, w2=w2, s2=ps)
 
 
 @pytest.mark.parametrize("E,H,M", [
