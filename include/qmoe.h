@@ -159,18 +159,20 @@ typedef struct qmoe_layer qmoe_layer;
 /* Validate the description and create a handle.  Fails with QMOE_ERR_ARG on
    a bad field (the message names it), then with QMOE_ERR_DEVICE if no HIP
    device can be queried and QMOE_ERR_UNSUPPORTED if the current device is
-   not gfx950.  Then copies the weight codes (w13, w2 and the shared
-   expert's; all of them, also for a handle used only for router calls)
-   into the handle's own device allocation in tile order, for the MFMA
-   tiles: each
-   16-row block's codes stored 128 inputs at a time (64 bytes of each of its
-   rows, 1 KiB), the 16 bytes of row r at bytes 16 kq .. 16 kq + 15 of that
-   span placed at 16 (16 kq + r), so each MFMA-tile load instruction reads
-   1 KiB contiguous.  The device is synchronised before the copy (the codes
-   must have been written, on any stream) and after it; QMOE_ERR_DEVICE if
-   the allocation fails.  The scales are not read here: the ranges above
-   (group scales <= 511.75) are the caller's to keep.  Nothing is read from
-   the environment. */
+   not gfx950.  Then copies the weight codes and scales (w13, s13, w2, s2
+   and the shared expert's; all of them at their full sizes, also for a
+   handle used only for router calls) into the handle's own device
+   allocation in tile order, for the MFMA tiles: each 16-row block's codes
+   stored 128 inputs at a time (64 bytes of each of its rows, 1 KiB), the
+   16 bytes of row r at bytes 16 kq .. 16 kq + 15 of that span placed at
+   16 (16 kq + r), and its scales 512 inputs at a time (16 groups of each
+   row, 512 bytes), the scales of groups 4 kq .. 4 kq + 3 of row r placed at
+   8 (16 kq + r), so each MFMA-tile load instruction reads 1 KiB or 512
+   bytes contiguous.  The device is synchronised before the copy (the
+   weights must have been written, on any stream) and after it;
+   QMOE_ERR_DEVICE if the allocation fails.  The scales' values are not
+   checked: the ranges above (group scales <= 511.75) are the caller's to
+   keep.  Nothing is read from the environment. */
 int qmoe_layer_create(const qmoe_layer_desc* desc, qmoe_layer** out);
 void qmoe_layer_destroy(qmoe_layer* layer);
 
@@ -283,8 +285,8 @@ int qmoe_read_intermediate(qmoe_layer* layer, int64_t M, const void* workspace, 
                            int32_t which, float* out_f32, void* stream);
 
 /* Decode one expert's weights with the same device function the GEMMs use,
-   from the handle's tile-order copy of the codes (so the copy is checked
-   too), and write the fp16 operand values in natural order: which = 0:
+   from the handle's tile-order copy of the codes and scales (so the copy
+   is checked too), and write the fp16 operand values in natural order: which = 0:
    [2I, H] from w13/s13, which = 1: [H, I] from w2/s2.  expert == E selects
    the shared expert.  out: uint16 fp16 bit patterns, device memory. */
 int qmoe_dequant_debug(qmoe_layer* layer, int32_t expert, int32_t which, uint16_t* out_f16,

@@ -520,22 +520,6 @@ __device__ __forceinline__ void transpose_scales_to(uint32_t lo, uint32_t hi, ui
 __device__ __forceinline__ void transpose_scales_to(uint32_t lo, uint32_t hi, uint32_t (&d)[4]) {
   transpose_scales(lo, hi, d);
 }
-// Lane (r, kq) holds 8 scales of its weight row, groups 8kq..8kq+7 of two
-// super-steps (w[0..3]); afterwards (lo0, hi0) holds groups 4kq..4kq+3 of
-// the first super-step and (lo1, hi1) those of the second, the layout one
-// 8-byte load per super-step gives.  Quarter k takes dwords 2(k&1) and
-// 2(k&1)+1 of quarter k/2 (first) or 2 + k/2 (second).
-__device__ __forceinline__ void split_scale_pair(const uint32_t (&w)[4], uint32_t& lo0, uint32_t& hi0, uint32_t& lo1,
-                                                 uint32_t& hi1) {
-  lo0 = w[0];
-  lo1 = w[2];
-  swap16(lo0, lo1);
-  swap32(lo0, lo1);
-  hi0 = w[1];
-  hi1 = w[3];
-  swap16(hi0, hi1);
-  swap32(hi0, hi1);
-}
 
 // Raw buffer resource over [base, base + bytes): loads take a 32-bit per-lane
 // offset and a scalar per-step offset, and read 0 past the end.
@@ -615,14 +599,14 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   const __amdgpu_buffer_rsrc_t rS = buffer_rsrc(sbase, (uint32_t)g.Nw * KG * 2);
   const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(g.a, g.a_bytes);
 
-  // offsets of this lane's code chunk (tile order: lane l's 16 bytes of a
-  // sub-step at 16 l of the block's 1 KiB for it, so a load instruction
-  // reads 1 KiB contiguous) and scale quad within a 16-row B block
-  // (vector), and each B block's first weight row (wave-uniform, so it
-  // rides in the scalar offset; the lane part alone is bounds-checked and
-  // every in-range lane stays inside the weights)
-  const uint32_t tl = 16u * (uint32_t)lane, sl = (uint32_t)r * KG * 2 + 8 * kq;
-  const uint32_t sl2 = (uint32_t)r * KG * 2 + 16 * kq;
+  // offsets of this lane's code chunk and scale quad within a 16-row B
+  // block (vector; tile order: lane l's 16 bytes of a sub-step at 16 l of
+  // the block's 1 KiB for it, its 8 bytes of scales of a super-step at 8 l
+  // of the block's 512 bytes for it, so a load instruction reads 1 KiB or
+  // 512 bytes contiguous), and each B block's first weight row
+  // (wave-uniform, so it rides in the scalar offset; the lane part alone is
+  // bounds-checked and every in-range lane stays inside the weights)
+  const uint32_t tl = 16u * (uint32_t)lane, sl = 8u * (uint32_t)lane;
   uint32_t brow[NBB];
   int col0[NBW];
 #pragma unroll
@@ -676,26 +660,9 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   auto load_sc = [&](int S, uint32_t (&sc)[NBB][2], bool ok) __attribute__((always_inline)) {
 #pragma unroll
     for (int b = 0; b < NBB; ++b) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rS, ok ? sl : kOob, S * 32 + brow[b] * KG * 2, 0);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rS, ok ? sl : kOob, S * 512 + brow[b] * KG * 2, 0);
       sc[b][0] = v[0];
       sc[b][1] = v[1];
-    }
-  };
-  // the scales of super-steps S and S + 1 (one 16-byte load per row, half
-  // the load instructions and, since the row's 128-byte line is then read
-  // in two visits instead of four, fewer re-reads of lines the weight stream
-  // has pushed out of L2): lane kq takes groups 8kq..8kq+7 of the 32.  Only
-  // the lane offset is range-checked, so a lane whose super-step is not a
-  // whole one of this row (kq >= 2 when S + 1 is past them) reads nothing.
-  auto load_sc2 = [&](int S, uint32_t (&sc)[NBB][4], bool ok) __attribute__((always_inline)) {
-    const bool in_row = ok && S + (kq >> 1) < S_end_full;
-#pragma unroll
-    for (int b = 0; b < NBB; ++b) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rS, in_row ? sl2 : kOob, S * 32 + brow[b] * KG * 2, 0);
-      sc[b][0] = v[0];
-      sc[b][1] = v[1];
-      sc[b][2] = v[2];
-      sc[b][3] = v[3];
     }
   };
   // token of tile row m (m < nr), from its sorted slot; -1 if the slot is
@@ -728,15 +695,10 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   __shared__ __attribute__((aligned(16))) _Float16 lds_a1[MB * 4 * kBlkHalves];
 #define QMOE_LDS_A(BUF) ((BUF) ? lds_a1 : lds_a0)
   // Scales: this super-step's by sub-step (sc_cur), the next one's in load
-  // layout (sc_nxt).  Gate+up loads each row's scales two super-steps at a
-  // time (sc_pair, see load_sc2) and keeps sc_cur two to a dword, which pays
-  // for the pair's registers; on MI355X this took gate+up at 90-1024 tokens
-  // 3-5% faster and its L2 misses at 256 tokens from 8.2 to 7.1 GB per call.
-  // Down, whose super-steps move half the bytes through L2 and whose scale
-  // lines stay there, keeps one load per super-step (the pair measured
-  // slower there).
-  constexpr bool kPairSc = GATEUP;
-  uint32_t sc_cur[NBB][kPairSc ? 2 : 4], sc_nxt[NBB][2], sc_pair[NBB][4];
+  // layout (sc_nxt).  Gate+up, whose 8-block loop holds 128 accumulators,
+  // keeps sc_cur two to a dword.
+  constexpr bool kCompactSc = GATEUP;
+  uint32_t sc_cur[NBB][kCompactSc ? 2 : 4], sc_nxt[NBB][2];
   Frag<NBB> fb0, fb1, fb2, fb3;  // the weights of sub-steps 0..3
   // Down: the first weights go out before the item's rows are looked up,
   // so the round trips of the lookups (sorted slot, routing weight) overlap
@@ -801,16 +763,6 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   auto promote_scales = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int b = 0; b < NBB; ++b) transpose_scales_to(sc_nxt[b][0], sc_nxt[b][1], sc_cur[b]);
-  };
-  // the first of a pair of super-steps from sc_pair; the second one's scales
-  // wait in sc_nxt
-  auto promote_pair = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int b = 0; b < NBB; ++b) {
-      uint32_t lo0, hi0;
-      split_scale_pair(sc_pair[b], lo0, hi0, sc_nxt[b][0], sc_nxt[b][1]);
-      transpose_scales_to(lo0, hi0, sc_cur[b]);
-    }
   };
   // this wave's blocks of sub-step U of super-step S into buffer BUF, for
   // the NMBC row blocks in use (row block amb0 + MBS*t; a wave-uniform
@@ -955,15 +907,10 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
   // zero rows, which are never stored).
   auto kloop = [&](auto nmbc_tag) __attribute__((always_inline)) {
     constexpr int NMBC = decltype(nmbc_tag)::value;
-    // scale pairs in every gate+up loop but the 8-block one, whose 128
-    // accumulators leave no room for them: there the pair was spilled, and
-    // its reload waited for every load in flight
-    constexpr bool kPair = kPairSc && NMBC < 8;
     const int n = S_end_full - S_begin;
     if (n > 0) {
       if (!kEarlyB) {
-        if (kPair) load_sc2(S_begin, sc_pair, true);
-        else load_sc(S_begin, sc_nxt, true);
+        load_sc(S_begin, sc_nxt, true);
         load_b(S_begin, 0, fb0, true);
         QMOE_LOAD_A_TILE(S_begin, 0, true, 0);
         load_b(S_begin, 1, fb1, true);
@@ -973,36 +920,29 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(GATEUP 
         wait_vmcnt<0>();
       }
       __syncthreads();
-      if (kPair) promote_pair();
-      else promote_scales();
+      promote_scales();
       for (int S = S_begin; S < S_end_full; ++S) {
         // the next super-step, clamped: the last one reloads itself
         const int Sn = min(S + 1, S_end_full - 1);
-        // scales: the second super-step of each pair loads the next pair
-        const bool second = ((S - S_begin) & 1) != 0;
-        if (!kPair) load_sc(Sn, sc_nxt, true);
         if constexpr (GATEUP && NMBC <= kGuPairRowBlocks) {
           // weights two sub-steps at a time: sub-steps 2 and 3 go out with
           // sub-step 0, the next super-step's 0 and 1 with sub-step 2.  The
-          // next scale pair goes out with sub-step 3's tile, whose deadline
-          // it shares: held from there to its use it takes no registers
-          // through the other sub-steps (issued with sub-step 0, it was
-          // spilled in the 8-block loop, and reloading it waited for every
-          // load in flight)
+          // next scales go out with sub-step 3's tile, whose deadline they
+          // share: held from there to their use they take no registers
+          // through the other sub-steps
           QMOE_SUBSTEP_PAIR(0, fb0, S, 1, S, 2, fb2, fb3, 0);
           QMOE_SUBSTEP_NOB(1, fb1, S, 2, 1);
           QMOE_SUBSTEP_PAIR(2, fb2, S, 3, Sn, 0, fb0, fb1, 0);
-          if (second) load_sc2(S + 1, sc_pair, S + 1 < S_end_full);
+          load_sc(Sn, sc_nxt, true);
           QMOE_SUBSTEP_NOB(3, fb3, Sn, 0, 1);
         } else {
-          if (kPair && second) load_sc2(S + 1, sc_pair, S + 1 < S_end_full);
+          load_sc(Sn, sc_nxt, true);
           QMOE_SUBSTEP(0, fb0, S, 1, S, 2, fb2, 0);
           QMOE_SUBSTEP(1, fb1, S, 2, S, 3, fb3, 1);
           QMOE_SUBSTEP(2, fb2, S, 3, Sn, 0, fb0, 0);
           QMOE_SUBSTEP(3, fb3, Sn, 0, Sn, 1, fb1, 1);
         }
-        if (kPair && second) promote_pair();
-        else promote_scales();
+        promote_scales();
       }
     }
     if (has_tail) QMOE_TAIL();
@@ -1778,16 +1718,29 @@ __global__ __launch_bounds__(kThreads) void tile_codes_kernel(const uint4* __res
   dst[c] = src[(n * K2 + sub * 64 + (l >> 4) * 16) / 16];
 }
 
+// The same for a scale array (tiled_scale_offset): one thread per 8-byte
+// chunk of the destination (four groups of one row); KG = K/32 is a
+// multiple of 4.
+__global__ __launch_bounds__(kThreads) void tile_scales_kernel(const uint2* __restrict__ src, uint2* __restrict__ dst,
+                                                                long long chunks, int KG) {
+  const long long c = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (c >= chunks) return;
+  const long long blk = c / (4 * KG);  // 16-row block: 16 * KG * 2 bytes = 4 KG chunks
+  const int w = (int)(c % (4 * KG)), S = w / 64, l = w % 64;
+  const long long n = blk * 16 + (l & 15);  // row r = l % 16, group quad kq = l / 16
+  dst[c] = src[(n * KG + S * 16 + (l >> 4) * 4) / 4];
+}
+
 // ------------------------------------------------------------- inspection
 
-// w: one expert's codes in tile order (K2 = K/2 bytes per row)
+// w, s: one expert's codes and scales in tile order (K2 = K/2 bytes per row)
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t* w, const uint16_t* s, int N,
                                                             int K, uint16_t* out) {
   const long long idx = (long long)blockIdx.x * kThreads + threadIdx.x;
   const int per_row = K / 8;
   if (idx >= (long long)N * per_row) return;
   const int n = (int)(idx / per_row), d = (int)(idx % per_row);
-  half8_t v = dq8(w[tiled_code_offset(n, 4 * (size_t)d, K / 2) / 4], s[(size_t)n * (K / 32) + d / 4]);
+  half8_t v = dq8(w[tiled_code_offset(n, 4 * (size_t)d, K / 2) / 4], s[tiled_scale_offset(n, d / 4, K / 32) / 2]);
 #pragma unroll
   for (int p = 0; p < 8; ++p)
     if (x16_pos(p)) v[p] = v[p] * (_Float16)0.0625f;  // exact: undo the operand's x16
@@ -1892,10 +1845,12 @@ struct qmoe_layer {
   std::atomic<uint64_t> receipt_seq{0};  // forward calls since creation (not reset by qmoe_reset_stats)
   std::atomic<uint64_t> forward_calls{0}, route_calls{0}, gemm_launches{0}, launches{0}, inits{0},
       ws_last{0}, ws_peak{0}, prefill_tiles{0}, gemv_tiles{0}, gemv_nt{0}, splitk_launches{0};
-  // the codes in tile order: one device allocation made at creation and
-  // freed at destruction (the descriptor's code pointers are read once)
+  // the codes and scales in tile order: one device allocation made at
+  // creation and freed at destruction (the descriptor's pointers to them are
+  // read once)
   void* tiled = nullptr;
   const uint8_t *w13 = nullptr, *w2 = nullptr, *sh_w13 = nullptr, *sh_w2 = nullptr;
+  const uint16_t *s13 = nullptr, *s2 = nullptr, *sh_s13 = nullptr, *sh_s2 = nullptr;
 };
 
 namespace {
@@ -2135,9 +2090,9 @@ void fill_gemm_args(const qmoe_layer* L, int64_t M, void* ws, const Layout& lay,
   g.tickets = at<int>(ws, lay.tickets);
   if (GATEUP) {
     g.w = L->w13;
-    g.s = L->d.s13;
+    g.s = L->s13;
     g.w_sh = L->sh_w13;
-    g.s_sh = L->d.shared_s13;
+    g.s_sh = L->sh_s13;
     g.K = H;
     g.N = I;
     g.Nw = 2 * I;
@@ -2147,9 +2102,9 @@ void fill_gemm_args(const qmoe_layer* L, int64_t M, void* ws, const Layout& lay,
     g.y_out = nullptr;
   } else {
     g.w = L->w2;
-    g.s = L->d.s2;
+    g.s = L->s2;
     g.w_sh = L->sh_w2;
-    g.s_sh = L->d.shared_s2;
+    g.s_sh = L->sh_s2;
     g.K = I;
     g.N = H;
     g.Nw = H;
@@ -2186,6 +2141,8 @@ int launch_gemv(qmoe_layer* L, int64_t M, void* ws, const Layout& lay, hipStream
   // the dot-product GEMV reads the codes as given (row order)
   g.w = GATEUP ? L->d.w13 : L->d.w2;
   g.w_sh = GATEUP ? L->d.shared_w13 : L->d.shared_w2;
+  g.s = GATEUP ? L->d.s13 : L->d.s2;
+  g.s_sh = GATEUP ? L->d.shared_s13 : L->d.shared_s2;
   if (mixed) {  // the light experts' list of a mixed call: at most one item per local expert
     g.items = at<int4>(ws, lay.items_gv);
     g.count_at = 2;
@@ -2287,44 +2244,63 @@ int qmoe_version(void) { return QMOE_VERSION; }
 const char* qmoe_last_error(void) { return g_err.c_str(); }
 
 namespace {
-// The layer's codes in tile order: w13 [L, 2I, H/2] and w2 [L, H, I/2] of
-// the L local experts (and the shared expert's), copied once into one
-// allocation, which the MFMA tiles read (the dot-product GEMV reads the
-// caller's codes as given).  The device is synchronised before (the
-// caller's writes of the codes, on any stream, are complete) and after (the
-// copy is complete before any stream can use it).
+// The layer's codes and scales in tile order: w13 [L, 2I, H/2], w2
+// [L, H, I/2] and their scales s13 [L, 2I, H/32], s2 [L, H, I/32] of the L
+// local experts (and the shared expert's), copied once into one allocation,
+// which the MFMA tiles read (the dot-product GEMV reads the caller's arrays
+// as given).  The device is synchronised before (the caller's writes of the
+// weights, on any stream, are complete) and after (the copy is complete
+// before any stream can use it).
 int make_tiled_codes(qmoe_layer* L) {
   const int64_t H = L->d.H, I = L->d.I, nl = L->nloc;
   if (hipDeviceSynchronize() != hipSuccess) return fail(QMOE_ERR_DEVICE, "hipDeviceSynchronize failed");
-  const int64_t b13 = 2 * I * (H / 2), b2 = H * (I / 2);  // code bytes of one expert
-  const int64_t total = nl * (b13 + b2) + (L->shared ? b13 + b2 : 0);
+  const int64_t b13 = 2 * I * (H / 2), b2 = H * (I / 2);        // code bytes of one expert
+  const int64_t c13 = 2 * I * (H / 32) * 2, c2 = H * (I / 32) * 2;  // scale bytes of one expert
+  const int64_t nexp = nl + (L->shared ? 1 : 0);
+  const int64_t total = nexp * (b13 + b2 + c13 + c2);
   if (hipMalloc(&L->tiled, (size_t)total) != hipSuccess) {
     L->tiled = nullptr;
     (void)hipGetLastError();
-    return fail(QMOE_ERR_DEVICE, "cannot allocate " + std::to_string(total) + " bytes for the tile-ordered codes");
+    return fail(QMOE_ERR_DEVICE, "cannot allocate " + std::to_string(total) + " bytes for the tile-ordered weights");
   }
   uint8_t* base = static_cast<uint8_t*>(L->tiled);
+  uint8_t* sbase = base + nexp * (b13 + b2);  // the scales after all codes (16-byte aligned: b13, b2 are)
   struct Part {
     const void* src;
     uint8_t* dst;
-    int64_t rows, K2;
+    int64_t rows, K;
+    bool scales;
   };
-  const Part parts[4] = {{L->d.w13, base, nl * 2 * I, H / 2},
-                         {L->d.w2, base + nl * b13, nl * H, I / 2},
-                         {L->d.shared_w13, base + nl * (b13 + b2), 2 * I, H / 2},
-                         {L->d.shared_w2, base + nl * (b13 + b2) + b13, H, I / 2}};
-  for (int i = 0; i < (L->shared ? 4 : 2); ++i) {
+  const Part parts[8] = {{L->d.w13, base, nl * 2 * I, H, false},
+                         {L->d.w2, base + nl * b13, nl * H, I, false},
+                         {L->d.s13, sbase, nl * 2 * I, H, true},
+                         {L->d.s2, sbase + nl * c13, nl * H, I, true},
+                         {L->d.shared_w13, base + nl * (b13 + b2), 2 * I, H, false},
+                         {L->d.shared_w2, base + nl * (b13 + b2) + b13, H, I, false},
+                         {L->d.shared_s13, sbase + nl * (c13 + c2), 2 * I, H, true},
+                         {L->d.shared_s2, sbase + nl * (c13 + c2) + c13, H, I, true}};
+  for (int i = 0; i < (L->shared ? 8 : 4); ++i) {
     const Part& p = parts[i];
-    const long long chunks = p.rows * p.K2 / 16;
-    tile_codes_kernel<<<dim3((unsigned)ceil_div(chunks, kThreads)), kThreads, 0, nullptr>>>(
-        static_cast<const uint4*>(p.src), reinterpret_cast<uint4*>(p.dst), chunks, (int)p.K2);
-    if (hipGetLastError() != hipSuccess) return fail(QMOE_ERR_LAUNCH, "tile_codes_kernel launch failed");
+    if (p.scales) {
+      const long long chunks = p.rows * (p.K / 32) / 4;
+      tile_scales_kernel<<<dim3((unsigned)ceil_div(chunks, kThreads)), kThreads, 0, nullptr>>>(
+          static_cast<const uint2*>(p.src), reinterpret_cast<uint2*>(p.dst), chunks, (int)(p.K / 32));
+    } else {
+      const long long chunks = p.rows * (p.K / 2) / 16;
+      tile_codes_kernel<<<dim3((unsigned)ceil_div(chunks, kThreads)), kThreads, 0, nullptr>>>(
+          static_cast<const uint4*>(p.src), reinterpret_cast<uint4*>(p.dst), chunks, (int)(p.K / 2));
+    }
+    if (hipGetLastError() != hipSuccess) return fail(QMOE_ERR_LAUNCH, "tiling the weights: launch failed");
   }
-  if (hipDeviceSynchronize() != hipSuccess) return fail(QMOE_ERR_DEVICE, "tiling the codes failed");
+  if (hipDeviceSynchronize() != hipSuccess) return fail(QMOE_ERR_DEVICE, "tiling the weights failed");
   L->w13 = parts[0].dst;
   L->w2 = parts[1].dst;
-  L->sh_w13 = L->shared ? parts[2].dst : nullptr;
-  L->sh_w2 = L->shared ? parts[3].dst : nullptr;
+  L->s13 = reinterpret_cast<const uint16_t*>(parts[2].dst);
+  L->s2 = reinterpret_cast<const uint16_t*>(parts[3].dst);
+  L->sh_w13 = L->shared ? parts[4].dst : nullptr;
+  L->sh_w2 = L->shared ? parts[5].dst : nullptr;
+  L->sh_s13 = L->shared ? reinterpret_cast<const uint16_t*>(parts[6].dst) : nullptr;
+  L->sh_s2 = L->shared ? reinterpret_cast<const uint16_t*>(parts[7].dst) : nullptr;
   return QMOE_OK;
 }
 }  // namespace
@@ -2597,10 +2573,10 @@ int qmoe_dequant_debug(qmoe_layer* L, int32_t expert, int32_t which, uint16_t* o
   const uint16_t* s;
   if (expert < L->nloc) {
     w = (which == 0 ? L->w13 : L->w2) + (size_t)expert * N * (K / 2);
-    s = (which == 0 ? L->d.s13 : L->d.s2) + (size_t)expert * N * (K / 32);
+    s = (which == 0 ? L->s13 : L->s2) + (size_t)expert * N * (K / 32);
   } else {
     w = which == 0 ? L->sh_w13 : L->sh_w2;
-    s = which == 0 ? L->d.shared_s13 : L->d.shared_s2;
+    s = which == 0 ? L->sh_s13 : L->sh_s2;
   }
   const int64_t n = (int64_t)N * (K / 8);
   dequant_kernel<<<dim3((unsigned)ceil_div(n, kThreads)), kThreads, 0, static_cast<hipStream_t>(stream)>>>(

@@ -100,6 +100,17 @@ __host__ __device__ constexpr size_t tiled_code_offset(size_t n, size_t b, size_
   return (n / 16) * 16 * K2 + (b / 64) * 1024 + (((b % 64) / 16) * 16 + n % 16) * 16 + b % 16;
 }
 
+// Tile order of the group scales (the layer's copy; KG = K/32 groups per
+// row, a multiple of 4): each 16-row block's scales stored super-step by
+// super-step (16 groups: 32 bytes of each of its rows, 512 bytes), and
+// within a super-step lane l = 16 kq + r's 8 bytes (row r, groups
+// 4 kq .. 4 kq + 3 of the super-step) at 8 l, so one 8-byte load per lane
+// reads a block's super-step of scales as 512 contiguous bytes.  Byte
+// offset of the scale of group g of row n:
+__host__ __device__ constexpr size_t tiled_scale_offset(size_t n, size_t g, size_t KG) {
+  return (n / 16) * 16 * KG * 2 + (g / 16) * 512 + (((g % 16) / 4) * 16 + n % 16) * 8 + (g % 4) * 2;
+}
+
 // h = SiLU(g) * u as stored: the product rounded to fp32, then to fp16.  The
 // empty asm pins the fp32 value, so the compiler cannot fuse the product into
 // the conversion (one rounding instead of two) in some kernels or

@@ -45,6 +45,18 @@ class Layer:
                  local_count=0, scoring="softmax", expert_bias=None, routed_scale=0.0):
         self.lib = load_library()
         self.E, self.H, self.I, self.top_k, self.max_rows = E, H, I, top_k, max_rows
+        # creation copies all four arrays into the tile order, so each must
+        # hold its full size (a short one would be read past its end)
+        n_loc = local_count or E
+        need = {"w13": n_loc * 2 * I * (H // 2), "s13": n_loc * 2 * I * (H // 32) * 2,
+                "w2": n_loc * H * (I // 2), "s2": n_loc * H * (I // 32) * 2}
+        arrays = {"w13": w13, "s13": s13, "w2": w2, "s2": s2}
+        for key, nbytes in need.items():
+            t = arrays[key]
+            if t is not None and t.numel() * t.element_size() < nbytes:
+                raise ValueError(f"{key} holds {t.numel() * t.element_size()} bytes, {nbytes} needed")
+            if shared and shared[key].numel() * shared[key].element_size() < nbytes // n_loc:
+                raise ValueError(f"shared {key} holds fewer than {nbytes // n_loc} bytes")
         self._keep = [w13, s13, w2, s2]
         sh = shared or {}
         if shared:

@@ -123,3 +123,23 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(B, "_HERE", str(tmp_path))
     with pytest.raises(RuntimeError, match="missing"):
         B.load_library()
+
+
+def test_layer_rejects_short_weight_arrays(lib):
+    """Creation copies the codes and scales into the tile order, so the
+    torch wrapper refuses an array shorter than its full size before the
+    library reads it (CPU tensors: the size check comes first)."""
+    import torch
+    from quantized_mixture_experts_top_amd import Layer
+    E, H, I = 4, 256, 128
+    full = dict(w13=torch.zeros((E, 2 * I, H // 2), dtype=torch.uint8),
+                s13=torch.zeros((E, 2 * I, H // 32), dtype=torch.int16),
+                w2=torch.zeros((E, H, I // 2), dtype=torch.uint8),
+                s2=torch.zeros((E, H, I // 32), dtype=torch.int16))
+    for key in full:
+        kw = dict(full)
+        kw[key] = torch.zeros(128, dtype=torch.int16)
+        with pytest.raises(ValueError, match=key):
+            Layer(E=E, H=H, I=I, top_k=2, max_rows=16, **kw)
+    with pytest.raises(ValueError, match="on the GPU"):
+        Layer(E=E, H=H, I=I, top_k=2, max_rows=16, **full)

@@ -544,17 +544,17 @@ def test_receipt_exact_counts(E, H, I, k, M, shared):
 
 def _router_only_layer(E, H, max_rows):
     """A layer handle for router calls only.  Creation copies the weight
-    codes into the layer's tile order, so the code arrays have their full
-    shapes (zeros, I = 128); the router kernels read no expert weights and
-    nothing reads the scales here, so a tiny placeholder stands in for
-    them."""
+    codes and scales into the layer's tile order, so all four arrays have
+    their full shapes (zeros, I = 128), although the router kernels read
+    none of them."""
     import torch
     from quantized_mixture_experts_top_amd import Layer
     I = 128
     w13 = torch.zeros((E, 2 * I, H // 2), dtype=torch.uint8, device="cuda")
     w2 = torch.zeros((E, H, I // 2), dtype=torch.uint8, device="cuda")
-    ps = torch.zeros(128, dtype=torch.int16, device="cuda")
-    return Layer(E=E, H=H, I=I, top_k=min(8, E), max_rows=max_rows, w13=w13, s13=ps, w2=w2, s2=ps)
+    s13 = torch.zeros((E, 2 * I, H // 32), dtype=torch.int16, device="cuda")
+    s2 = torch.zeros((E, H, I // 32), dtype=torch.int16, device="cuda")
+    return Layer(E=E, H=H, I=I, top_k=min(8, E), max_rows=max_rows, w13=w13, s13=s13, w2=w2, s2=s2)
 
 
 @pytest.mark.parametrize("E,H,M", [
