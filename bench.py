@@ -36,6 +36,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import statistics
 import sys
 import time
@@ -147,7 +148,13 @@ def summarize_counters(key: str, fetch_csv: str, write_csv: str, path: str = COU
     its tile launch and its dot-product launch together), mean over the calls
     of one FETCH_SIZE and one WRITE_SIZE counter pass (rocprofv3 csv), scaled
     by the copy calibration, stored under `key` with the current source hash
-    (entries taken on other sources are dropped)."""
+    (entries taken on other sources are dropped).  `key` is the workload and M
+    as the benchmark names them (`plateau:M=4096`); `plateau:4096`, the form
+    `--only` takes, is accepted and stored in that form."""
+    m = re.fullmatch(r"([a-z0-9]+):(?:M=)?(\d+)", key)
+    if not m:
+        raise SystemExit(f"counter key {key!r} is not <workload>:M=<tokens>")
+    key = key_of(m.group(1), int(m.group(2)))
     def per_dispatch(p, counter):
         vals, tiles = {}, set()
         for r in csv.DictReader(open(p)):

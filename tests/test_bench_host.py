@@ -50,6 +50,12 @@ def test_counter_summary(tmp_path):
     b = bench.summarize_counters("plateau:M=4096", str(f), str(w), str(out))
     assert b == round(130 * 1024 * bench.FETCH_FACTOR + 3 * 1024 * bench.WRITE_FACTOR)
     assert bench.stored_traffic("plateau", 4096, str(out)) == b
+    # the `--only` form of the key is stored under the benchmark's name
+    assert bench.summarize_counters("skew:512", str(f), str(w), str(out)) == b
+    assert bench.stored_traffic("skew", 512, str(out)) == b
+    assert set(json.load(open(out))["gate_up_bytes_per_launch"]) == {"plateau:M=4096", "skew:M=512"}
+    with pytest.raises(SystemExit):
+        bench.summarize_counters("plateau 4096", str(f), str(w), str(out))
 
 
 @pytest.mark.parametrize("shape", [synth.TINY, synth.FULL])
