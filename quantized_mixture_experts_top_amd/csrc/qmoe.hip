@@ -59,9 +59,10 @@ constexpr int kDnWN = 8, kDnNBW = 1, kDnWPE = 4;
 // Gate+up K loops of up to this many 16-row blocks issue their weights two
 // sub-steps at a time: 2-4% faster at 90-1024 tokens on the 384-expert layer
 // (measured with the codes in row order, where the two sub-steps were the
-// halves of each row's 128-byte line).
-// Larger gate+up loops have no registers left for the extra live fragment
-// (it spills); in the down tiles pairing measured neutral to 3-5% slower.
+// halves of each row's 128-byte line).  Loops of 5-7 blocks fit the extra
+// live fragment too (the 8-block loop spills it), but there pairing measured
+// no faster at 90-1024 tokens and 1-2% slower at 4096 than the interleaved
+// issue; in the down tiles pairing measured neutral to 3-5% slower.
 constexpr int kGuPairRowBlocks = 4;
 constexpr int kPrefillRows = kTileMB * 16;
 
@@ -2251,7 +2252,7 @@ namespace {
 // as given).  The device is synchronised before (the caller's writes of the
 // weights, on any stream, are complete) and after (the copy is complete
 // before any stream can use it).
-int make_tiled_codes(qmoe_layer* L) {
+int make_tiled_weights(qmoe_layer* L) {
   const int64_t H = L->d.H, I = L->d.I, nl = L->nloc;
   if (hipDeviceSynchronize() != hipSuccess) return fail(QMOE_ERR_DEVICE, "hipDeviceSynchronize failed");
   const int64_t b13 = 2 * I * (H / 2), b2 = H * (I / 2);        // code bytes of one expert
@@ -2358,7 +2359,7 @@ int qmoe_layer_create(const qmoe_layer_desc* d, qmoe_layer** out) {
   L->lo = d->local_count ? d->local_first : 0;
   L->nloc = d->local_count ? d->local_count : d->E;
   L->rscale = d->routed_scale == 0.0f ? 1.0f : d->routed_scale;
-  const int rc = make_tiled_codes(L);
+  const int rc = make_tiled_weights(L);
   if (rc != QMOE_OK) {
     qmoe_layer_destroy(L);
     return rc;
