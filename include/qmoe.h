@@ -59,11 +59,15 @@
  *
  * Ownership: the caller owns every buffer.  The layer handle borrows the
  * weight pointers (and the expert bias) for its lifetime: the dot-product
- * GEMV reads the codes as given.  It also copies the codes once, at
- * creation, into one device allocation it owns (the same size as the
- * codes, freed by qmoe_layer_destroy) in the order the MFMA tiles' loads
- * read them.  Forward calls allocate nothing: per-call scratch lives in a
- * caller-provided workspace whose size comes from qmoe_workspace_size().
+ * GEMV reads the codes and scales as given.  It also copies the codes and
+ * scales once, at creation, into one device allocation it owns (the same
+ * size as the weights, freed by qmoe_layer_destroy) in the order the MFMA
+ * tiles' loads read them.  So the weights must not change while the handle
+ * lives: after new weights are written, destroy the handle and create a new
+ * one (a handle that saw the change would compute decode-sized calls with
+ * the new weights and tile calls with the old).  Forward calls allocate
+ * nothing: per-call scratch lives in a caller-provided workspace whose size
+ * comes from qmoe_workspace_size().
  *
  * Streams: every enqueueing call takes a hipStream_t (as void*, NULL = the
  * default stream), only enqueues work on it and never synchronises.  Faults

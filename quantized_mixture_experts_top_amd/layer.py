@@ -39,7 +39,9 @@ class Layer:
     shard routes over E experts but holds and computes only experts
     local_first .. local_first + local_count - 1 (the weight tensors then
     have local_count experts) and returns its partial sum.  The layer keeps
-    references to the tensors (the library borrows their memory)."""
+    references to the tensors (the library borrows their memory) and a copy
+    of them in the MFMA tiles' order made at construction, so the weights
+    must not change while the layer lives: build a new Layer instead."""
 
     def __init__(self, *, E, H, I, top_k, max_rows, w13, s13, w2, s2, shared=None, local_first=0,
                  local_count=0, scoring="softmax", expert_bias=None, routed_scale=0.0):
